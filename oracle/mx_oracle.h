@@ -1,0 +1,75 @@
+/*
+ * mx_oracle.h -- CPU oracle for the MXFP4 weight-quantized mixture-of-experts MLP.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library. The product path (the HIP library under
+ * mxfp4_weight_quantized_amd/) shares no code, header, table or constant with it.
+ *
+ * Plain, slow, obviously correct: loops in the order the definitions give, fp64 arithmetic,
+ * rounding only at the precision points listed per function. OpenMP splits independent rows or
+ * tokens across threads; nothing is blocked, fused or reordered inside a row.
+ *
+ * Sources (cited by page title and section):
+ *   [EN] "Transformers 4.40 performance upgrades for OpenAI GPT-OSS: zero-build kernels, MXFP4
+ *        quantization, parallelism, and faster loading" (agentlenshq.com, English page),
+ *        section "MXFP4 4-Bit Quantization", subsections "What MXFP4 Is" and "Memory Savings".
+ *   [ZH] the Chinese version of the same page, section "MXFP4 是什么".
+ *   [FR] "GPT-OSS ... améliorations OpenAI" (otomatix.tech), section "Quantification MXFP4 :
+ *        un format atypique".
+ * The pages fix the element format (E2M1: 1 sign, 2 exponent, 1 mantissa bit) and that every
+ * 32 consecutive elements share one scale. Every other rule here (the E8M0 scale choice, rounding,
+ * packing, routing, SwiGLU) is a reading of an open point; each is stated where it is used.
+ */
+#ifndef MX_ORACLE_H
+#define MX_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Value of a 4-bit E2M1 code (0..15) built from its bit fields. */
+double mxo_e2m1_value(unsigned code);
+/* Value of an E8M0 scale byte: 2^(b-127); 255 is NaN. */
+double mxo_e8m0_value(unsigned b);
+/* fp64 -> bf16 bit pattern, round to nearest even, one rounding step, subnormals kept. */
+uint16_t mxo_bf16_from_double(double d);
+double mxo_double_from_bf16(uint16_t b);
+
+/* Quantize rows of K values (K % 32 == 0) in 32-element blocks along K.
+ * packed: rows*K/2 bytes, element 2j in the low nibble of byte j; scales: rows*K/32 bytes. */
+void mxo_quantize_f32(const float* src, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales);
+void mxo_quantize_bf16(const uint16_t* src, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales);
+/* Exact dequantization to fp64. */
+void mxo_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K, double* dst);
+
+/* Router: logits[t][e] = fp32(sum_h x[t][h]*wr[e][h] + br[e]) with the sum in fp64 (br nullable). */
+void mxo_router_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H, int E,
+                       float* logits);
+/* Top-k by (logit descending, expert index ascending); softmax over the k selected, fp64 -> fp32. */
+void mxo_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w);
+/* Stable counting sort of the T*k (token, slot) pairs by expert.
+ * Returns 0, or -1 if an index lies outside [0, E). */
+int mxo_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm, int32_t* inv);
+
+/* Dense weight-only linear y[m][n] = sum_k x[m][k] * W^[n][k] in fp64.
+ * mx_act != 0: the rows of x are first quantized and dequantized along K (activation variant). */
+void mxo_linear(const uint16_t* x, int M, int K, const uint8_t* packed, const uint8_t* scales, int N,
+                int mx_act, double* y);
+
+/* MoE MLP for a list of tokens (tokens == NULL: all T tokens, in order), given the routing.
+ * out: [n_tokens][H] fp64.  h_out (nullable): [n_tokens][k][F] bf16 bits of the SwiGLU output.
+ * Returns 0, or -1 on an expert index outside [0, E). */
+int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
+                const int32_t* topk_idx, const float* topk_w,
+                const uint8_t* gu_packed, const uint8_t* gu_scales,
+                const uint8_t* dn_packed, const uint8_t* dn_scales,
+                const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out);
+
+/* Number of OpenMP threads the oracle uses. */
+int mxo_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

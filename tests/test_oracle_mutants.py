@@ -1,0 +1,77 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks that the pin tests
+catch every one of them. The real oracle source is never modified."""
+import os
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mx_oracle.c")
+PIN_TESTS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
+             os.path.join(ROOT, "tests", "test_oracle_path.py")]
+
+# (name, exact text in mx_oracle.c, replacement)
+MUTANTS = [
+    ("tie-to-odd", "(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    ("scale-minus-1", "s = (q - 1) - 2;", "s = (q - 1) - 1;"),
+    ("scale-ceil", "s = (q - 1) - 2;", "s = q - 2;"),
+    ("no-lower-clamp", "if (s < -127) s = -127;", ";"),
+    ("nibble-order-pack", "codes[2 * j] | (codes[2 * j + 1] << 4)",
+     "codes[2 * j + 1] | (codes[2 * j] << 4)"),
+    ("nibble-order-decode", "(k & 1) ? (byte >> 4) : (byte & 0xfu)",
+     "(k & 1) ? (byte & 0xfu) : (byte >> 4)"),
+    ("negative-zero-sign", "(signbit(x[i]) ? 8 : 0)", "(x[i] < 0 ? 8 : 0)"),
+    ("e2m1-bias", "ldexp(1.0 + 0.5 * (double)m, (int)e - 1)", "ldexp(1.0 + 0.5 * (double)m, (int)e - 2)"),
+    ("e8m0-bias", "ldexp(1.0, (int)b - 127)", "ldexp(1.0, (int)b - 128)"),
+    ("nonfinite-not-flagged", "*scale = 255;", "*scale = 254;"),
+    ("topk-tie-high-index", "if (best < 0 || l[e] > l[best]) best = e;",
+     "if (best < 0 || l[e] >= l[best]) best = e;"),
+    ("softmax-denominator", "(float)(exp(sel[j] - mx) / sum)", "(float)(exp(sel[j] - mx) / (sum + 1e-3))"),
+    ("router-no-bias", "if (br) acc += (double)br[e];", ";"),
+    ("permute-unstable", "int32_t row = offsets[e] + fill[e]++;",
+     "int32_t row = offsets[e + 1] - 1 - fill[e]++;"),
+    ("swiglu-gate-up-swapped", "double g = a[f], u = a[F + f];", "double g = a[F + f], u = a[f];"),
+    ("silu-sign", "hb[f] = mxo_bf16_from_double(g / (1.0 + exp(-g)) * u);",
+     "hb[f] = mxo_bf16_from_double(g / (1.0 + exp(g)) * u);"),
+    ("routing-weight-dropped", "o[m] += wt * acc;", "o[m] += acc;"),
+    ("down-expert-stride", "dn_packed + ((int64_t)e * H + m) * dn_row",
+     "dn_packed + ((int64_t)e * F + m) * dn_row"),
+    ("mx-act-h-skipped", "activation_row(hb, F, mx_act, h);", "activation_row(hb, F, 0, h);"),
+    ("bf16-truncates", "nearbyint(a / quantum)", "floor(a / quantum)"),
+]
+
+
+def _run_mutant(args):
+    name, old, new, tmp = args
+    with open(SRC) as f:
+        src = f.read()
+    assert old is None or src.count(old) == 1, "mutation site for %s not found once" % name
+    if old is None:  # the unmodified source, built the same way: must pass
+        old = new = ""
+    msrc = os.path.join(tmp, "mut_%s.c" % name)
+    with open(msrc, "w") as f:
+        f.write(src.replace(old, new) if old else src)
+    mlib = os.path.join(tmp, "libmut_%s.so" % name)
+    oracle.build(src=msrc, out=mlib)
+    env = dict(os.environ, MXO_ORACLE_LIB=mlib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PIN_TESTS], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    return name, r.returncode
+
+
+@pytest.mark.timeout(900)
+def test_every_planted_mistake_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        with ThreadPoolExecutor(4) as ex:
+            results = list(ex.map(_run_mutant, [("unmodified", None, None, tmp)] +
+                                  [(n, o, w, tmp) for n, o, w in MUTANTS]))
+    assert results[0] == ("unmodified", 0), "the harness fails even without a planted mistake"
+    results = results[1:]
+    survivors = [n for n, rc in results if rc == 0]
+    assert not survivors, "planted mistakes not caught by the pins: %s" % survivors
