@@ -1,0 +1,184 @@
+/*
+ * mxfp4moe.h -- C ABI of the MI355X (gfx950) MXFP4 weight-quantized mixture-of-experts MLP.
+ *
+ * Sources, cited by page title and section:
+ *   [EN] "Transformers 4.40 performance upgrades for OpenAI GPT-OSS: zero-build kernels, MXFP4
+ *        quantization, parallelism, and faster loading" (agentlenshq.com, English page),
+ *        section "MXFP4 4-Bit Quantization" (subsections "What MXFP4 Is", "Native Support in
+ *        transformers", "Memory Savings"); section "Zero-Build Kernels from the Hub" (the MoE MLP
+ *        kernel is the MegaBlocks MoE layer there).
+ *   [GGUF] "Hugging Face Transformers GGUF 지원" (agentlenshq.com, Korean page), section
+ *        "ggml Metal 커널 통합": the quantized matmul reads packed weights without expanding
+ *        them first, and MoE expert selection is a top-k.
+ * The pages fix: E2M1 elements (1 sign, 2 exponent, 1 mantissa bit) and one shared scale per
+ * 32-element block. The library fixes what they leave open, the same way everywhere:
+ *   - scale: E8M0 byte b, value 2^(b-127); b = clamp(floor(log2 amax) - 2, -127, 127) + 127,
+ *     amax = 0 gives b = 0; a block with NaN/Inf gets b = 255 (decodes to NaN) and codes 0;
+ *   - elements: nearest E2M1 value to x / 2^(b-127), ties to the even code, magnitudes above 6
+ *     saturate to 6; sign bit = sign bit of x;
+ *   - layout ("packed MXFP4 tensor" [rows][K]): row-major, K contiguous; packed bytes
+ *     uint8[rows][K/2] with element 2j in the low nibble of byte j; scales uint8[rows][K/32];
+ *   - MoE expert: gate_up rows [0, F) = gate, [F, 2F) = up; h = silu(gate) * up, rounded to bf16;
+ *     expert output = h W_down^T; token output = sum over its k experts of weight * output;
+ *   - router: logits = x W_r^T + b; top-k by (logit desc, expert index asc); softmax over the k.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked host. bf16 tensors are passed as uint16_t bit
+ *     patterns. The caller owns every buffer; the library never allocates or frees memory and
+ *     never synchronizes (mx_workspace_status is the one exception). Work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and outputs are valid once it completes.
+ *   - Inputs and outputs must not alias.
+ *   - Argument errors are found on the host before anything is launched and return a status
+ *     (never a C++ exception); mx_last_error() then describes it. A failed launch returns
+ *     MX_ERR_HIP. Faults inside kernels surface at the caller's next synchronization.
+ *   - The library runs on gfx950 only: other devices get MX_ERR_UNSUPPORTED.
+ *   - Zero-sized work (rows = 0, T = 0, M = 0) returns MX_OK and launches nothing.
+ */
+#ifndef MXFP4MOE_H
+#define MXFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = 1,        /* a required pointer is NULL */
+  MX_ERR_SHAPE = 2,       /* a size is negative, not a multiple of 32 where required, or too big */
+  MX_ERR_ALIGN = 3,       /* a pointer lacks the alignment the entry point states */
+  MX_ERR_DTYPE = 4,       /* unknown dtype enum */
+  MX_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the matching *_workspace() query */
+  MX_ERR_UNSUPPORTED = 6, /* not a gfx950 device, or an unknown flag / descriptor version */
+  MX_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+} mx_status;
+
+typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
+
+/* Activation variant: the GEMM A-operands (x along H, and the bf16 SwiGLU output h along F) are
+ * themselves MXFP4-quantized with the rule above and multiplied on the scaled FP4 matrix cores. */
+#define MX_ACT_MXFP4 0x1u
+
+/* Upper limits checked on the host. */
+#define MX_MAX_EXPERTS 256
+#define MX_MAX_TOPK 8
+#define MX_MAX_K 8192            /* reduction length of mxfp4_linear and of H, F in the MoE MLP */
+
+/* ------------------------------------------------------------------------------------------------
+ * mxfp4_quantize -- pack `rows` rows of K values into MXFP4 ([EN] "What MXFP4 Is").
+ *   src     [rows][K] fp32 (src_dtype MX_F32) or bf16 bits (MX_BF16), row-major.
+ *   packed  [rows][K/2] bytes out; scales [rows][K/32] bytes out (layout above).
+ *   K % 32 == 0 (else MX_ERR_SHAPE); src 16-byte aligned (fp32) or 8-byte aligned (bf16),
+ *   packed 16-byte aligned (else MX_ERR_ALIGN). Bit-exact: the result depends only on the values.
+ * ---------------------------------------------------------------------------------------------- */
+mx_status mxfp4_quantize(const void* src, mx_dtype src_dtype, int64_t rows, int64_t K,
+                         uint8_t* packed, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * mxfp4_dequantize -- exact values code * 2^(b-127) ([EN] "Memory Savings": the de-quantized
+ * model is the bf16 one).
+ *   packed [rows][K/2], scales [rows][K/32]; dst [rows][K] fp32 or bf16 bits (dst_dtype).
+ *   Every value is exact in both types except overflow past the type's max (-> +-Inf, as IEEE
+ *   rounding gives) and scale byte 255 (-> NaN). K % 32 == 0; packed 16-byte aligned; dst
+ *   16-byte aligned.
+ * ---------------------------------------------------------------------------------------------- */
+mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K,
+                           void* dst, mx_dtype dst_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * moe_route_topk -- router logits, top-k expert selection and softmax over the k selected
+ * ([GGUF] "ggml Metal 커널 통합": top-k expert selection for MoE; the router itself is a reading).
+ *   x [T][H] bf16, wr [E][H] bf16, br [E] fp32 or NULL (no bias).
+ *   logits [T][E] fp32 out (may be NULL: not stored); topk_idx [T][k] int32 out, in rank order
+ *   (logit descending, lower expert index first on equal logits); topk_w [T][k] fp32 out.
+ *   Limits: 1 <= k <= min(E, MX_MAX_TOPK), 1 <= E <= MX_MAX_EXPERTS, H % 32 == 0 (MX_ERR_SHAPE);
+ *   x and wr 16-byte aligned (MX_ERR_ALIGN). Logits are fp32 sums of bf16 products; the top-k
+ *   is exact given those logits.
+ * ---------------------------------------------------------------------------------------------- */
+mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int32_t T,
+                         int32_t H, int32_t E, int32_t k, float* logits, int32_t* topk_idx,
+                         float* topk_w, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * moe_permute -- group the T*k (token, slot) pairs by expert: histogram over experts, exclusive
+ * prefix sum, stable scatter in (token, slot) order (the row grouping an MoE MLP kernel such as
+ * [EN] "Zero-Build Kernels from the Hub"'s MegaBlocks MoE layer runs its grouped GEMMs on).
+ *   topk_idx [T][k] int32 in.
+ *   offsets [E+1] int32 out: expert e owns permuted rows [offsets[e], offsets[e+1]).
+ *   perm [T*k] int32 out: perm[row] = t*k + j of the pair at permuted row `row`.
+ *   inv [T*k] int32 out: inv[t*k + j] = its permuted row.
+ *   status: one int32 out (may be NULL): 0, or 1 if some index lay outside [0, E); such pairs
+ *   are left out of perm and their inv entry is -1.
+ *   Deterministic (no ordering by atomics). Limits as for moe_route_topk; T*k < 2^31.
+ * ---------------------------------------------------------------------------------------------- */
+mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* offsets,
+                      int32_t* perm, int32_t* inv, int32_t* status, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * mxfp4_moe_mlp -- the whole MoE MLP: route -> permute -> gate_up grouped GEMM with fused SwiGLU
+ * -> down grouped GEMM scaled by the routing weight -> combine over the k experts. The grouped
+ * GEMMs read the packed weights and decode them in registers, never materializing bf16 weights
+ * ([GGUF] "ggml Metal 커널 통합"; [EN] "MXFP4 4-Bit Quantization": MXFP4 weights served by
+ * dedicated kernels instead of a bf16 fallback).
+ * ---------------------------------------------------------------------------------------------- */
+typedef struct mx_moe_desc {
+  size_t struct_size;          /* sizeof(mx_moe_desc); other values -> MX_ERR_UNSUPPORTED */
+  int32_t T, H, F, E, k;       /* tokens, hidden, expert FFN width, experts, experts per token */
+  uint32_t flags;              /* 0 or MX_ACT_MXFP4 */
+  mx_dtype out_dtype;          /* dtype of `out` */
+  const uint16_t* x;           /* [T][H] bf16 */
+  const uint16_t* wr;          /* [E][H] bf16 router weight; unused if topk_idx_in is given */
+  const float* br;             /* [E] fp32 router bias, NULL = none */
+  const int32_t* topk_idx_in;  /* [T][k] caller routing, NULL = route internally */
+  const float* topk_w_in;      /* [T][k] caller routing weights (required with topk_idx_in) */
+  const uint8_t* gu_packed;    /* [E][2F][H/2] */
+  const uint8_t* gu_scales;    /* [E][2F][H/32] */
+  const uint8_t* dn_packed;    /* [E][H][F/2] */
+  const uint8_t* dn_scales;    /* [E][H][F/32] */
+  void* out;                   /* [T][H] out_dtype */
+  int32_t* topk_idx_out;       /* [T][k], NULL = not stored (internal routing only) */
+  float* topk_w_out;           /* [T][k], NULL = not stored */
+  float* logits_out;           /* [T][E], NULL = not stored */
+} mx_moe_desc;
+
+/* Bytes of workspace mxfp4_moe_mlp needs for this descriptor (0 if the shapes are invalid). */
+size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc);
+
+/*   desc (host pointer) as above; ws: device workspace of at least mxfp4_moe_mlp_workspace(desc)
+ *   bytes, 256-byte aligned, owned by the caller, contents need not be initialized.
+ *   Limits: H, F multiples of 32 and <= MX_MAX_K; E, k as for moe_route_topk; all weight, x and
+ *   out pointers 16-byte aligned. Routing indices outside [0, E) (caller routing) are skipped and
+ *   flagged in the workspace status word (read it with mx_workspace_status); their tokens'
+ *   outputs then lack those experts. Concurrent calls must use distinct workspaces. */
+mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * mxfp4_linear -- dense weight-only linear y = x W^T with W packed MXFP4 [N][K] (the single
+ * matrix product the MoE MLP's grouped GEMMs are made of; [EN] "MXFP4 4-Bit Quantization").
+ *   x [M][K] bf16; packed [N][K/2], scales [N][K/32]; y [M][N] fp32 or bf16 (y_dtype).
+ *   flags: 0 or MX_ACT_MXFP4 (x is MXFP4-quantized along K first; needs the workspace).
+ *   ws: mxfp4_linear_workspace(M, K, N, flags) bytes (may be 0 and ws NULL when flags == 0).
+ *   K % 32 == 0, K <= MX_MAX_K; x, packed, y 16-byte aligned.
+ * ---------------------------------------------------------------------------------------------- */
+size_t mxfp4_linear_workspace(int32_t M, int32_t K, int32_t N, uint32_t flags);
+mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uint8_t* packed,
+                       const uint8_t* scales, int32_t N, void* y, mx_dtype y_dtype, uint32_t flags,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Diagnostics.
+ * ---------------------------------------------------------------------------------------------- */
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* mx_last_error(void);
+/* Synchronizes `stream`, then copies the status word of an mxfp4_moe_mlp workspace to *status
+ * (host pointer): 0 = fine, 1 = routing index outside [0, E) seen. */
+mx_status mx_workspace_status(const void* ws, void* stream, int32_t* status);
+/* Library version string. */
+const char* mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP4MOE_H */

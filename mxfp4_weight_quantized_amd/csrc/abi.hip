@@ -1,0 +1,284 @@
+// abi.hip -- the C ABI (include/mxfp4moe.h): host-side argument checks, workspace layout and the
+// launch sequence. No allocation, no synchronization (except mx_workspace_status), no C++
+// exception crosses the boundary.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/mxfp4moe.h"
+#include "mx_launch.h"
+
+#define MX_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+mx_status fail(mx_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mx_status ok() {
+  g_err[0] = 0;
+  return MX_OK;
+}
+
+mx_status hip_fail(hipError_t e, const char* what) {
+  return fail(MX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::once_flag g_init_once;
+hipError_t g_init_err = hipSuccess;
+
+// gfx950 check for the current device (cached per device).
+mx_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MX_ERR_UNSUPPORTED, "device index %d", dev);
+  int v = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    v = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_ok[dev].store(v, std::memory_order_release);
+  }
+  if (v != 1) return fail(MX_ERR_UNSUPPORTED, "this library runs on gfx950 (MI355X) devices only");
+  std::call_once(g_init_once, [] { g_init_err = mx::gemm_init(); });
+  if (g_init_err != hipSuccess) return hip_fail(g_init_err, "kernel setup");
+  return MX_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// ---- mxfp4_moe_mlp workspace layout ----
+struct MoeLayout {
+  size_t status, logits, idx, w, offsets, perm, inv, tiles, h, y, xq, xqs, hq, hqs, total;
+  int tile_rows, max_tiles;
+};
+
+MoeLayout moe_layout(const mx_moe_desc& d) {
+  MoeLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t T = (size_t)d.T, P = (size_t)d.T * d.k, E = (size_t)d.E;
+  L.tile_rows = mx::moe_tile_rows(d.T, d.k, d.E);
+  L.max_tiles = mx::moe_max_tiles(d.T, d.k, d.E, L.tile_rows);
+  L.status = take(256);  // int32 status, int32 tile count
+  L.logits = take(T * E * 4);
+  L.idx = take(P * 4);
+  L.w = take(P * 4);
+  L.offsets = take((E + 1) * 4);
+  L.perm = take(P * 4);
+  L.inv = take(P * 4);
+  L.tiles = take((size_t)L.max_tiles * 8);
+  L.h = take(P * (size_t)d.F * 2);
+  L.y = take(P * (size_t)d.H * 4);
+  if (d.flags & MX_ACT_MXFP4) {
+    L.xq = take(T * (size_t)d.H / 2);
+    L.xqs = take(T * (size_t)d.H / 32);
+    L.hq = take(P * (size_t)d.F / 2);
+    L.hqs = take(P * (size_t)d.F / 32);
+  }
+  L.total = off;
+  return L;
+}
+
+mx_status check_routing_shape(int64_t T, int64_t H, int64_t E, int64_t k) {
+  if (T < 0 || H <= 0 || E <= 0 || k <= 0) return fail(MX_ERR_SHAPE, "T=%lld H=%lld E=%lld k=%lld", (long long)T, (long long)H, (long long)E, (long long)k);
+  if (E > MX_MAX_EXPERTS) return fail(MX_ERR_SHAPE, "E=%lld exceeds %d", (long long)E, MX_MAX_EXPERTS);
+  if (k > E || k > MX_MAX_TOPK) return fail(MX_ERR_SHAPE, "k=%lld must be <= min(E, %d)", (long long)k, MX_MAX_TOPK);
+  if (T * k >= (1LL << 31)) return fail(MX_ERR_SHAPE, "T*k too large");
+  return MX_OK;
+}
+
+mx_status check_moe_desc(const mx_moe_desc* d) {
+  if (d == nullptr) return fail(MX_ERR_NULL, "desc is NULL");
+  if (d->struct_size != sizeof(mx_moe_desc)) return fail(MX_ERR_UNSUPPORTED, "desc.struct_size %zu != %zu", d->struct_size, sizeof(mx_moe_desc));
+  mx_status st = check_routing_shape(d->T, d->H, d->E, d->k);
+  if (st != MX_OK) return st;
+  if (d->F <= 0 || d->H % 32 || d->F % 32) return fail(MX_ERR_SHAPE, "H=%d and F=%d must be positive multiples of 32", d->H, d->F);
+  if (d->H > 3072 || d->F > 3072) return fail(MX_ERR_SHAPE, "H and F must be <= 3072 in the MoE MLP");
+  if (d->flags & ~MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "out_dtype %d", (int)d->out_dtype);
+  if (d->T == 0) return MX_OK;
+  if (!d->x || !d->gu_packed || !d->gu_scales || !d->dn_packed || !d->dn_scales || !d->out)
+    return fail(MX_ERR_NULL, "x, weights, scales and out are required");
+  if (d->topk_idx_in == nullptr && d->wr == nullptr) return fail(MX_ERR_NULL, "wr is required for internal routing");
+  if (d->topk_idx_in != nullptr && d->topk_w_in == nullptr) return fail(MX_ERR_NULL, "topk_w_in is required with topk_idx_in");
+  const void* a16[] = {d->x, d->wr, d->gu_packed, d->gu_scales, d->dn_packed, d->dn_scales, d->out};
+  for (const void* p : a16)
+    if (p && !aligned(p, 16)) return fail(MX_ERR_ALIGN, "x, wr, weights, scales and out must be 16-byte aligned");
+  return MX_OK;
+}
+
+}  // namespace
+
+// =============================================================================================
+MX_API mx_status mxfp4_quantize(const void* src, mx_dtype src_dtype, int64_t rows, int64_t K,
+                                uint8_t* packed, uint8_t* scales, void* stream) {
+  if (src_dtype != MX_F32 && src_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "src_dtype %d", (int)src_dtype);
+  if (rows < 0 || K < 0 || K % 32) return fail(MX_ERR_SHAPE, "rows=%lld K=%lld (K must be a multiple of 32)", (long long)rows, (long long)K);
+  if (rows == 0 || K == 0) return ok();
+  if (!src || !packed || !scales) return fail(MX_ERR_NULL, "src, packed and scales are required");
+  if (!aligned(src, src_dtype == MX_F32 ? 16 : 8) || !aligned(packed, 16)) return fail(MX_ERR_ALIGN, "src or packed misaligned");
+  mx_status st = check_device();
+  if (st != MX_OK) return st;
+  hipError_t e = mx::launch_quantize(src, src_dtype == MX_BF16, rows * (K / 32), packed, scales, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "quantize launch");
+}
+
+MX_API mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows,
+                                  int64_t K, void* dst, mx_dtype dst_dtype, void* stream) {
+  if (dst_dtype != MX_F32 && dst_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "dst_dtype %d", (int)dst_dtype);
+  if (rows < 0 || K < 0 || K % 32) return fail(MX_ERR_SHAPE, "rows=%lld K=%lld (K must be a multiple of 32)", (long long)rows, (long long)K);
+  if (rows == 0 || K == 0) return ok();
+  if (!packed || !scales || !dst) return fail(MX_ERR_NULL, "packed, scales and dst are required");
+  if (!aligned(packed, 16) || !aligned(dst, 16)) return fail(MX_ERR_ALIGN, "packed or dst misaligned");
+  mx_status st = check_device();
+  if (st != MX_OK) return st;
+  hipError_t e = mx::launch_dequantize(packed, scales, rows * (K / 32), dst, dst_dtype == MX_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "dequantize launch");
+}
+
+MX_API mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int32_t T,
+                                int32_t H, int32_t E, int32_t k, float* logits, int32_t* topk_idx,
+                                float* topk_w, void* stream) {
+  mx_status st = check_routing_shape(T, H, E, k);
+  if (st != MX_OK) return st;
+  if (H % 32) return fail(MX_ERR_SHAPE, "H=%d must be a multiple of 32", H);
+  if (T == 0) return ok();
+  if (!x || !wr || !topk_idx || !topk_w) return fail(MX_ERR_NULL, "x, wr, topk_idx and topk_w are required");
+  if (!aligned(x, 16) || !aligned(wr, 16)) return fail(MX_ERR_ALIGN, "x and wr must be 16-byte aligned");
+  st = check_device();
+  if (st != MX_OK) return st;
+  hipError_t e = mx::launch_route_topk(x, wr, br, T, H, E, k, logits, topk_idx, topk_w, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "route launch");
+}
+
+MX_API mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                             int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
+                             void* stream) {
+  mx_status st = check_routing_shape(T, 32, E, k);
+  if (st != MX_OK) return st;
+  if (!offsets) return fail(MX_ERR_NULL, "offsets is required");
+  if (T > 0 && (!topk_idx || !perm || !inv)) return fail(MX_ERR_NULL, "topk_idx, perm and inv are required");
+  st = check_device();
+  if (st != MX_OK) return st;
+  hipError_t e = mx::launch_permute(topk_idx, T, k, E, offsets, perm, inv, status, 0, nullptr, nullptr, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
+}
+
+MX_API size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc) {
+  if (desc == nullptr || desc->struct_size != sizeof(mx_moe_desc)) return 0;
+  if (check_routing_shape(desc->T, desc->H, desc->E, desc->k) != MX_OK || desc->F <= 0) return 0;
+  return moe_layout(*desc).total;
+}
+
+MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void* stream) {
+  mx_status st = check_moe_desc(desc);
+  if (st != MX_OK) return st;
+  const mx_moe_desc& d = *desc;
+  if (d.T == 0) return ok();
+  const MoeLayout L = moe_layout(d);
+  if (ws == nullptr || ws_bytes < L.total) return fail(MX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, ws_bytes);
+  if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (d.flags & MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "MX_ACT_MXFP4 is not available in this build");
+  st = check_device();
+  if (st != MX_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = static_cast<char*>(ws);
+  int32_t* status = reinterpret_cast<int32_t*>(w + L.status);
+  const int32_t* idx;
+  const float* tw;
+  hipError_t e;
+  if (d.topk_idx_in == nullptr) {
+    float* logits = d.logits_out ? d.logits_out : reinterpret_cast<float*>(w + L.logits);
+    int32_t* oi = d.topk_idx_out ? d.topk_idx_out : reinterpret_cast<int32_t*>(w + L.idx);
+    float* ow = d.topk_w_out ? d.topk_w_out : reinterpret_cast<float*>(w + L.w);
+    e = mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, s);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+    idx = oi;
+    tw = ow;
+  } else {
+    idx = d.topk_idx_in;
+    tw = d.topk_w_in;
+  }
+  int32_t* offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
+  int32_t* inv = reinterpret_cast<int32_t*>(w + L.inv);
+  int2* tiles = reinterpret_cast<int2*>(w + L.tiles);
+  e = mx::launch_permute(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows, tiles, status + 1, s);
+  if (e != hipSuccess) return hip_fail(e, "permute launch");
+  mx::MoeGemmArgs g{};
+  g.T = d.T; g.H = d.H; g.F = d.F; g.E = d.E; g.k = d.k;
+  g.x = d.x;
+  g.perm = perm;
+  g.inv = inv;
+  g.offsets = offsets;
+  g.tiles = tiles;
+  g.num_tiles = status + 1;
+  g.max_tiles = L.max_tiles;
+  g.topk_w = tw;
+  g.gu_packed = d.gu_packed; g.gu_scales = d.gu_scales;
+  g.dn_packed = d.dn_packed; g.dn_scales = d.dn_scales;
+  g.h = reinterpret_cast<uint16_t*>(w + L.h);
+  g.y = reinterpret_cast<float*>(w + L.y);
+  g.out = d.out;
+  g.out_bf16 = d.out_dtype == MX_BF16;
+  e = mx::launch_moe_gemms(g, s);
+  if (e != hipSuccess) return hip_fail(e, "grouped GEMM launch");
+  return ok();
+}
+
+MX_API size_t mxfp4_linear_workspace(int32_t M, int32_t K, int32_t N, uint32_t flags) {
+  if (M < 0 || K < 0 || N < 0) return 0;
+  if (flags & MX_ACT_MXFP4) return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
+  return 0;
+}
+
+MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uint8_t* packed,
+                              const uint8_t* scales, int32_t N, void* y, mx_dtype y_dtype,
+                              uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  if (y_dtype != MX_F32 && y_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "y_dtype %d", (int)y_dtype);
+  if (M < 0 || N < 0 || K <= 0 || K % 32 || K > MX_MAX_K) return fail(MX_ERR_SHAPE, "M=%d K=%d N=%d (K a multiple of 32, <= %d)", M, K, N, MX_MAX_K);
+  if (flags & ~MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if (M == 0 || N == 0) return ok();
+  if (!x || !packed || !scales || !y) return fail(MX_ERR_NULL, "x, packed, scales and y are required");
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 16) || !aligned(y, 16)) return fail(MX_ERR_ALIGN, "x, packed, scales and y must be 16-byte aligned");
+  if (flags & MX_ACT_MXFP4) {
+    if (ws == nullptr || ws_bytes < mxfp4_linear_workspace(M, K, N, flags)) return fail(MX_ERR_WORKSPACE, "workspace too small");
+    return fail(MX_ERR_UNSUPPORTED, "MX_ACT_MXFP4 is not available in this build");
+  }
+  mx_status st = check_device();
+  if (st != MX_OK) return st;
+  hipError_t e = mx::launch_linear(x, M, K, packed, scales, N, y, y_dtype == MX_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "linear launch");
+}
+
+MX_API const char* mx_last_error(void) { return g_err; }
+
+MX_API mx_status mx_workspace_status(const void* ws, void* stream, int32_t* status) {
+  if (!ws || !status) return fail(MX_ERR_NULL, "ws and status are required");
+  hipError_t e = hipMemcpyAsync(status, ws, sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "status read");
+}
+
+MX_API const char* mx_version(void) { return "mxfp4moe 0.1 (gfx950)"; }

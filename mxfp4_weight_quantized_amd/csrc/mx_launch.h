@@ -1,0 +1,54 @@
+// mx_launch.h -- host-side launchers of the gfx950 kernels (called by the C ABI layer only).
+// Every launcher enqueues on `stream`, performs no allocation or synchronization, and returns the
+// launch status. Shapes have been validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// codec.hip
+hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8_t* packed,
+                           uint8_t* scales, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t nblocks,
+                             void* dst, bool bf16_out, hipStream_t stream);
+
+// route.hip
+hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
+                             int E, int k, float* logits, int32_t* idx, float* w,
+                             hipStream_t stream);
+
+// permute.hip: tiles/num_tiles may be NULL (tile_rows ignored then).
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm,
+                          int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
+                          int32_t* num_tiles, hipStream_t stream);
+
+// gemm.hip
+struct MoeGemmArgs {
+  int T, H, F, E, k;
+  const uint16_t* x;         // [T][H] bf16
+  const int32_t* perm;       // [P]
+  const int32_t* inv;        // [P]
+  const int32_t* offsets;    // [E+1]
+  const int2* tiles;         // [max_tiles]
+  const int32_t* num_tiles;  // device
+  int max_tiles;
+  const float* topk_w;       // [P]
+  const uint8_t *gu_packed, *gu_scales, *dn_packed, *dn_scales;
+  uint16_t* h;               // [P][F] bf16 workspace
+  float* y;                  // [P][H] fp32 workspace
+  void* out;                 // [T][H]
+  bool out_bf16;
+};
+// Tile rows (BM) the grouped GEMMs use for this problem; the permutation's tile list must match.
+int moe_tile_rows(int T, int k, int E);
+int moe_max_tiles(int T, int k, int E, int tile_rows);
+hipError_t launch_moe_gemms(const MoeGemmArgs& a, hipStream_t stream);
+
+hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
+                         const uint8_t* scales, int N, void* y, bool y_bf16, hipStream_t stream);
+
+// Kernel attributes that must be set once per process before the first launch.
+hipError_t gemm_init();
+
+}  // namespace mx

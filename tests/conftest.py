@@ -15,3 +15,9 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # Name each test on the real stdout before it runs, so a run that dies mid-test says where.
+    sys.__stdout__.write("\n[start] %s\n" % nodeid)
+    sys.__stdout__.flush()

@@ -1,0 +1,136 @@
+"""C-ABI library: it loads, exports every entry point the header declares, and rejects bad
+arguments on the host (before touching a device). CPU only: no kernel runs here."""
+import ctypes
+import re
+
+import pytest
+import torch
+
+import mxfp4_weight_quantized_amd as mx
+
+
+def _declared_functions():
+    text = open(mx.HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    keep = {n for n in names if n.startswith(("mx", "moe_"))}
+    keep -= {"mx_status", "mx_dtype"}
+    return sorted(keep)
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return mx.lib()
+    except RuntimeError as e:
+        pytest.fail("HIP library not built: %s" % e)
+
+
+def test_exports_every_declared_entry_point(L):
+    names = _declared_functions()
+    for required in ("mxfp4_quantize", "mxfp4_dequantize", "moe_route_topk", "moe_permute",
+                     "mxfp4_moe_mlp", "mxfp4_moe_mlp_workspace", "mxfp4_linear",
+                     "mxfp4_linear_workspace", "mx_last_error", "mx_workspace_status",
+                     "mx_version"):
+        assert required in names
+    for n in names:
+        assert hasattr(L, n), "library does not export %s" % n
+    assert set(names) == set(mx.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_error_string(L):
+    assert "gfx950" in mx.version()
+    assert isinstance(mx.last_error(), str)
+
+
+def _fake(n=1 << 20):
+    # A host address that is never dereferenced: argument checks fail before any launch.
+    return ctypes.c_void_p(0x10000000)
+
+
+def test_quantize_argument_errors(L):
+    p = _fake()
+    assert L.mxfp4_quantize(p, 7, 4, 64, p, p, None) == mx.MX_ERR_DTYPE
+    assert L.mxfp4_quantize(p, mx.MX_F32, 4, 33, p, p, None) == mx.MX_ERR_SHAPE
+    assert "multiple of 32" in mx.last_error()
+    assert L.mxfp4_quantize(p, mx.MX_F32, -1, 64, p, p, None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_quantize(None, mx.MX_F32, 4, 64, p, p, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_quantize(ctypes.c_void_p(0x10000004), mx.MX_F32, 4, 64, p, p, None) == mx.MX_ERR_ALIGN
+    assert L.mxfp4_quantize(p, mx.MX_F32, 0, 64, p, p, None) == mx.MX_OK  # empty: no-op
+    assert L.mxfp4_dequantize(p, p, 4, 48, p, mx.MX_F32, None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_dequantize(p, p, 4, 64, p, 9, None) == mx.MX_ERR_DTYPE
+    assert L.mxfp4_dequantize(p, p, 0, 64, p, mx.MX_BF16, None) == mx.MX_OK
+
+
+def test_route_and_permute_argument_errors(L):
+    p = _fake()
+    assert L.moe_route_topk(p, p, None, 4, 64, 8, 9, p, p, p, None) == mx.MX_ERR_SHAPE  # k > E
+    assert L.moe_route_topk(p, p, None, 4, 64, 300, 4, p, p, p, None) == mx.MX_ERR_SHAPE  # E > 256
+    assert L.moe_route_topk(p, p, None, 4, 64, 32, 9, p, p, p, None) == mx.MX_ERR_SHAPE  # k > 8
+    assert L.moe_route_topk(p, p, None, 4, 48, 32, 4, p, p, p, None) == mx.MX_ERR_SHAPE  # H % 32
+    assert L.moe_route_topk(p, None, None, 4, 64, 32, 4, p, p, p, None) == mx.MX_ERR_NULL
+    assert L.moe_route_topk(p, p, None, 0, 64, 32, 4, p, p, p, None) == mx.MX_OK  # T = 0
+    assert L.moe_permute(p, 4, 2, 8, None, p, p, None, None) == mx.MX_ERR_NULL
+    assert L.moe_permute(p, 4, 0, 8, p, p, p, None, None) == mx.MX_ERR_SHAPE
+
+
+def _desc(T=4, H=64, F=64, E=8, k=2, **kw):
+    d = mx.MoeDesc()
+    d.struct_size = ctypes.sizeof(mx.MoeDesc)
+    d.T, d.H, d.F, d.E, d.k = T, H, F, E, k
+    d.out_dtype = mx.MX_F32
+    p = 0x10000000
+    for f in ("x", "wr", "gu_packed", "gu_scales", "dn_packed", "dn_scales", "out"):
+        setattr(d, f, p)
+    for f, v in kw.items():
+        setattr(d, f, v)
+    return d
+
+
+def test_moe_workspace_query_and_errors(L):
+    d = _desc(T=64, H=2880, F=2880, E=32, k=4)
+    n = mx.mxfp4_moe_mlp_workspace(d)
+    P = 64 * 4
+    # at least the bf16 SwiGLU output and the fp32 per-pair expert outputs
+    assert n >= P * 2880 * 2 + P * 2880 * 4 and n % 256 == 0
+    d_mx = _desc(T=64, H=2880, F=2880, E=32, k=4, flags=mx.MX_ACT_MXFP4)
+    assert mx.mxfp4_moe_mlp_workspace(d_mx) > n
+    bad = _desc()
+    bad.struct_size = 8
+    assert mx.mxfp4_moe_mlp_workspace(bad) == 0
+    assert L.mxfp4_moe_mlp(ctypes.byref(bad), _fake(), 1 << 30, None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mxfp4_moe_mlp(None, _fake(), 1 << 30, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(H=48)), _fake(), 1 << 30, None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(k=9)), _fake(), 1 << 30, None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(flags=4)), _fake(), 1 << 30, None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(out_dtype=5)), _fake(), 1 << 30, None) == mx.MX_ERR_DTYPE
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(x=0)), _fake(), 1 << 30, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(x=0x10000002)), _fake(), 1 << 30, None) == mx.MX_ERR_ALIGN
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(wr=0)), _fake(), 1 << 30, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(topk_idx_in=0x10000000)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_NULL  # weights missing
+    small = _desc()
+    need = mx.mxfp4_moe_mlp_workspace(small)
+    assert L.mxfp4_moe_mlp(ctypes.byref(small), _fake(), need - 1, None) == mx.MX_ERR_WORKSPACE
+    assert L.mxfp4_moe_mlp(ctypes.byref(small), None, need, None) == mx.MX_ERR_WORKSPACE
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(T=0)), None, 0, None) == mx.MX_OK
+
+
+def test_linear_argument_errors(L):
+    p = _fake()
+    assert L.mxfp4_linear(p, 4, 40, p, p, 8, p, mx.MX_F32, 0, None, 0, None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_linear(p, 4, 64, p, p, 8, p, 3, 0, None, 0, None) == mx.MX_ERR_DTYPE
+    assert L.mxfp4_linear(p, 4, 16384, p, p, 8, p, mx.MX_F32, 0, None, 0, None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_linear(p, 4, 64, p, p, 8, p, mx.MX_F32, 2, None, 0, None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mxfp4_linear(None, 4, 64, p, p, 8, p, mx.MX_F32, 0, None, 0, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_linear(p, 0, 64, p, p, 8, p, mx.MX_F32, 0, None, 0, None) == mx.MX_OK
+    assert mx.mxfp4_linear_workspace(4, 64, 8, 0) == 0
+    assert mx.mxfp4_linear_workspace(4, 64, 8, mx.MX_ACT_MXFP4) > 0
+    assert L.mxfp4_linear(p, 4, 64, p, p, 8, p, mx.MX_F32, mx.MX_ACT_MXFP4, None, 0,
+                          None) == mx.MX_ERR_WORKSPACE
+
+
+def test_binding_rejects_cpu_tensors():
+    x = torch.zeros(4, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        mx.mxfp4_quantize(x)

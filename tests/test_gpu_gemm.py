@@ -1,0 +1,167 @@
+"""GPU parity of mxfp4_linear and mxfp4_moe_mlp against the oracle (tolerance bound).
+
+Shapes span several tiles with ragged tails (rows per expert, N not a multiple of the tile, K not
+a multiple of the K tile), the decode- and prefill-shaped tile configurations, and the full-size
+layers (sampled tokens where the oracle would take too long)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_weight_quantized_amd import inputs
+import mxfp4_weight_quantized_amd as mx
+from parity_util import (DEV, bf16_host_bits, check_bf16_output, check_tolerance, moe_weights,
+                         moe_weights_dev, note, to_dev, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------------------------ linear
+def _linear_case(M, K, N, seed, out_dtype):
+    x = inputs.activations(seed, M, K)
+    w = inputs.linear_weight_f32(seed, N, K)
+    p, s = oracle.quantize(w)
+    note("linear M=%d K=%d N=%d %s" % (M, K, N, out_dtype))
+    y = mx.mxfp4_linear(to_dev(x), to_dev(p), to_dev(s), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y, oracle.linear(x, p, s)
+
+
+def test_linear_single_layer_4x256x512():
+    """4 x 256 bf16 activations, 512 x 256 weights, fp32 out, seed 0."""
+    y, ref = _linear_case(4, 256, 512, 0, torch.float32)
+    check_tolerance(to_f64(y), ref, "linear 4x256x512")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_linear_decode_sweep_bf16(M):
+    """K = 2880, N = 5760, bf16 out, seed 1."""
+    y, ref = _linear_case(M, 2880, 5760, 1, torch.bfloat16)
+    check_bf16_output(bf16_host_bits(y), ref, "linear M=%d" % M)
+    y32, _ = _linear_case(M, 2880, 5760, 1, torch.float32)
+    check_tolerance(to_f64(y32), ref, "linear M=%d fp32" % M)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 32, 16), (17, 96, 200), (5, 64, 48), (100, 2880, 300),
+                                   (130, 320, 130), (3, 8192, 64), (257, 2880, 96)])
+def test_linear_ragged(M, K, N):
+    y, ref = _linear_case(M, K, N, 7 + M, torch.float32)
+    check_tolerance(to_f64(y), ref, "linear %dx%dx%d" % (M, K, N))
+
+
+# ------------------------------------------------------------------------------------ MoE MLP
+def _routing(T, E, k, seed):
+    r = np.random.default_rng(seed)
+    idx = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = r.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+def _run_moe(x, weights_dev, k, out_dtype, wr=None, br=None, idx=None, w=None):
+    gp, gs, dp, ds = weights_dev
+    out, routing = mx.mxfp4_moe_mlp(
+        to_dev(x), gp, gs, dp, ds, k, wr=None if wr is None else to_dev(wr),
+        br=None if br is None else to_dev(br), topk_idx=None if idx is None else to_dev(idx),
+        topk_w=None if w is None else to_dev(w), out_dtype=out_dtype, return_routing=True)
+    torch.cuda.synchronize()
+    return out, routing
+
+
+@pytest.mark.parametrize("T,H,F,E,k", [(1, 64, 64, 1, 1), (37, 256, 192, 8, 2), (7, 96, 320, 4, 4),
+                                       (200, 128, 96, 16, 4), (513, 64, 128, 4, 2)])
+def test_moe_small_pinned_routing(T, H, F, E, k):
+    seed = 60 + T
+    x = inputs.activations(seed, T, H)
+    wts = moe_weights(seed, E, H, F)
+    idx, w = _routing(T, E, k, seed)
+    note("moe pinned T=%d H=%d F=%d E=%d k=%d" % (T, H, F, E, k))
+    out, _ = _run_moe(x, moe_weights_dev(seed, E, H, F), k, torch.float32, idx=idx, w=w)
+    ref = oracle.moe_mlp(x, idx, w, *wts, E=E)
+    check_tolerance(to_f64(out), ref, "moe T=%d" % T)
+
+
+def test_moe_small_internal_routing_bf16():
+    T, H, F, E, k, seed = 50, 256, 128, 8, 2, 70
+    x = inputs.activations(seed, T, H)
+    wr, br = inputs.router(seed, E, H, bias_std=0.5)
+    wts = moe_weights(seed, E, H, F)
+    note("moe internal routing T=%d" % T)
+    out, (lg, idx, w) = _run_moe(x, moe_weights_dev(seed, E, H, F), k, torch.bfloat16, wr=wr, br=br)
+    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    oidx, ow = oracle.topk_softmax(lg, k)
+    np.testing.assert_array_equal(idx, oidx)
+    ref = oracle.moe_mlp(x, idx, w, *wts, E=E)
+    check_bf16_output(bf16_host_bits(out), ref, "moe internal bf16")
+
+
+def test_moe_is_deterministic():
+    T, H, F, E, k, seed = 300, 128, 128, 8, 4, 71
+    x = inputs.activations(seed, T, H)
+    idx, w = _routing(T, E, k, seed)
+    wd = moe_weights_dev(seed, E, H, F)
+    a, _ = _run_moe(x, wd, k, torch.float32, idx=idx, w=w)
+    b, _ = _run_moe(x, wd, k, torch.float32, idx=idx, w=w)
+    assert torch.equal(a, b)
+
+
+def test_moe_bad_routing_index_is_flagged():
+    T, H, F, E, k, seed = 4, 64, 64, 4, 2, 72
+    x = inputs.activations(seed, T, H)
+    idx, w = _routing(T, E, k, seed)
+    idx[2, 1] = 7
+    gp, gs, dp, ds = moe_weights_dev(seed, E, H, F)
+    out = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    d = mx.make_moe_desc(to_dev(x), gp, gs, dp, ds, k, out, topk_idx=to_dev(idx), topk_w=to_dev(w))
+    ws = torch.empty(mx.mxfp4_moe_mlp_workspace(d), dtype=torch.uint8, device=DEV)
+    mx._check(mx.lib().mxfp4_moe_mlp(mx.ctypes.byref(d), ws.data_ptr(), ws.numel(),
+                                     mx._stream(None)))
+    assert mx.workspace_status(ws) == 1
+    good = [0, 1, 3]
+    ref = oracle.moe_mlp(x[good], idx[good], w[good], *moe_weights(seed, E, H, F), E=E)
+    check_tolerance(to_f64(out)[good], ref, "moe rows without the bad index")
+
+
+# ----------------------------------------------------------------------------- full-size layers
+def _full_moe(shape, n_sample, out_dtype=torch.float32):
+    s = shape
+    x = inputs.activations(s.seed, s.T, s.H)
+    wr, br = inputs.router(s.seed, s.E, s.H, s.bias_std)
+    wts = moe_weights(s.seed, s.E, s.H, s.F)
+    note("moe full %s" % s.name)
+    out, (lg, idx, w) = _run_moe(x, moe_weights_dev(s.seed, s.E, s.H, s.F), s.k, out_dtype,
+                                 wr=wr, br=br if s.bias_std else None)
+    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    oidx, ow = oracle.topk_softmax(lg, s.k)
+    np.testing.assert_array_equal(idx, oidx)
+    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
+    # sampled tokens: spread over the batch plus tokens routed to the busiest expert
+    r = np.random.default_rng(s.seed)
+    busiest = np.bincount(idx.reshape(-1), minlength=s.E).argmax()
+    on_busiest = np.nonzero((idx == busiest).any(axis=1))[0]
+    toks = np.unique(np.concatenate([r.choice(s.T, size=min(s.T, n_sample), replace=False),
+                                     on_busiest[:4], [0, s.T - 1]])).astype(np.int32)
+    ref = oracle.moe_mlp(x, idx, w, *wts, E=s.E, tokens=toks)
+    got = to_f64(out)[toks] if out_dtype == torch.float32 else bf16_host_bits(out)[toks]
+    return got, ref
+
+
+def test_moe_20b_decode_T64_full():
+    got, ref = _full_moe(inputs.MOE_20B_DECODE, 64)
+    check_tolerance(got, ref, "20b decode")
+
+
+def test_moe_20b_decode_T64_bf16():
+    got, ref = _full_moe(inputs.MOE_20B_DECODE, 16, torch.bfloat16)
+    check_bf16_output(got, ref, "20b decode bf16")
+
+
+def test_moe_20b_prefill_T8192_sampled():
+    got, ref = _full_moe(inputs.MOE_20B_PREFILL, 24)
+    check_tolerance(got, ref, "20b prefill")
+
+
+@pytest.mark.parametrize("T", [1, 256, 4096])
+def test_moe_120b_sampled(T):
+    got, ref = _full_moe(inputs.MOE_120B[T], 12)
+    check_tolerance(got, ref, "120b T=%d" % T)

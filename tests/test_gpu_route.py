@@ -1,0 +1,105 @@
+"""GPU parity of moe_route_topk and moe_permute.
+
+Logits are compared with the oracle's by tolerance (fp32 sums in a different order); the top-k
+indices must equal the oracle's top-k taken on the GPU's own logits, bit for bit, and the
+permutation must equal the oracle's bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_weight_quantized_amd import inputs
+import mxfp4_weight_quantized_amd as mx
+from parity_util import DEV, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _route(T, H, E, k, seed, bias_std=0.0, wr=None):
+    x = inputs.activations(seed, T, H)
+    wr_, br = inputs.router(seed, E, H, bias_std)
+    if wr is not None:
+        wr_ = wr
+    note("route T=%d H=%d E=%d k=%d" % (T, H, E, k))
+    lg, idx, w = mx.moe_route_topk(to_dev(x), to_dev(wr_), to_dev(br) if bias_std else None, k)
+    torch.cuda.synchronize()
+    return x, wr_, (br if bias_std else None), lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,H,E,k,bias", [(1, 2880, 128, 4, 0.0), (5, 64, 8, 1, 0.0),
+                                          (37, 256, 40, 8, 0.5), (64, 2880, 32, 4, 0.0),
+                                          (300, 96, 256, 8, 1.0), (8192, 2880, 32, 4, 0.5)])
+def test_route_topk_parity(T, H, E, k, bias):
+    x, wr, br, lg, idx, w = _route(T, H, E, k, seed=31 + T, bias_std=bias)
+    ref = oracle.router_logits(x, wr, br)
+    assert np.all(np.abs(lg - ref) <= 1e-5 * (np.abs(ref) + 1) + 2e-6 * np.abs(ref).max()), \
+        float(np.abs(lg - ref).max())
+    oidx, ow = oracle.topk_softmax(lg, k)  # top-k on identical (GPU) logits
+    np.testing.assert_array_equal(idx, oidx)
+    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
+    # the oracle's own end-to-end routing agrees except where two logits are within noise
+    ridx, _ = oracle.topk_softmax(ref, k)
+    diff = np.any(ridx != idx, axis=1)
+    for t in np.nonzero(diff)[0]:
+        s = np.sort(ref[t])[::-1]
+        assert np.min(np.abs(np.diff(s[:k + 1]))) < 1e-4, "routing differs beyond a near-tie"
+
+
+def test_route_ties_go_to_lower_index():
+    T, H, E, k = 20, 64, 16, 4
+    wr = inputs.router(40, E, H)[0].copy()
+    wr[5] = wr[2]       # experts 2 and 5 always tie
+    wr[9] = wr[2]
+    wr[11] = wr[7]
+    x, wr, br, lg, idx, w = _route(T, H, E, k, seed=40, wr=wr)
+    assert np.all(lg[:, 5] == lg[:, 2]) and np.all(lg[:, 9] == lg[:, 2])
+    oidx, ow = oracle.topk_softmax(lg, k)
+    np.testing.assert_array_equal(idx, oidx)
+    x0 = np.zeros((3, H), np.uint16)   # zero tokens: all logits 0 -> experts 0..k-1, weights 1/k
+    lg0, idx0, w0 = mx.moe_route_topk(to_dev(x0), to_dev(wr), None, k)
+    torch.cuda.synchronize()
+    assert np.all(idx0.cpu().numpy() == np.arange(k)) and np.all(w0.cpu().numpy() == 0.25)
+
+
+def _permute(idx, E):
+    note("permute P=%d E=%d" % (idx.size, E))
+    offs, perm, inv, status = mx.moe_permute(to_dev(idx), E)
+    torch.cuda.synchronize()
+    return offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), int(status.cpu()[0])
+
+
+@pytest.mark.parametrize("T,k,E,skew", [(1, 1, 1, 0), (1, 4, 128, 0), (3, 2, 8, 0),
+                                        (64, 4, 32, 0), (1000, 3, 7, 1), (8192, 4, 32, 1),
+                                        (4096, 4, 128, 0), (257, 8, 256, 0)])
+def test_permute_bit_exact(T, k, E, skew):
+    r = np.random.default_rng(50 + T)
+    if skew:
+        p = np.exp(r.normal(0, 1.5, E)); p /= p.sum()
+        idx = np.stack([r.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    else:
+        idx = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    offs, perm, inv, st = _permute(idx, E)
+    o_offs, o_perm, o_inv = oracle.permute(idx, E)
+    assert st == 0
+    np.testing.assert_array_equal(offs, o_offs)
+    np.testing.assert_array_equal(perm, o_perm)
+    np.testing.assert_array_equal(inv, o_inv)
+
+
+def test_permute_all_to_one_expert_and_empty_experts():
+    idx = np.full((500, 1), 3, np.int32)
+    offs, perm, inv, st = _permute(idx, 9)
+    o = oracle.permute(idx, 9)
+    np.testing.assert_array_equal(offs, o[0])
+    np.testing.assert_array_equal(perm, o[1])
+    np.testing.assert_array_equal(inv, o[2])
+
+
+def test_permute_flags_out_of_range_indices():
+    idx = np.array([[0, 1], [5, 2], [-1, 0]], np.int32)
+    offs, perm, inv, st = _permute(idx, 4)
+    assert st == 1
+    assert inv[2] == -1 and inv[4] == -1
+    valid = np.array([0, 1, 3, 5])  # pairs with an index inside [0, 4)
+    assert offs[-1] == 4 and sorted(perm[:4].tolist()) == valid.tolist()
+    np.testing.assert_array_equal(perm[:4], [0, 5, 1, 3])  # experts 0,0,1,2 in pair order
