@@ -1,0 +1,451 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 weight-quantized MoE-MLP hot path on one MI355X.
+
+One step = one ``mxfp4_moe_mlp`` call (router -> permutation -> gate_up grouped GEMM with SwiGLU
+-> down grouped GEMM -> combine) over one batch of synthetic tokens, inputs resident in HBM.
+Prints ONE JSON line: tokens/s for the whole step, plus the roofline of the dominant kernel
+(timed with HIP events recorded by the library on the stream it launches on) and the CPU oracle
+timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --summarize-counters DIR_FETCH DIR_WRITE   (rocprofv3 --pmc output -> profiles/)
+
+Decode-shaped workloads rotate through several copies of the weights (and several token
+batches) so the working set exceeds the 256 MB Infinity Cache and every step reads HBM.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "mxfp4_weight_quantized_amd", "csrc", "gemm.hip")
+
+METRIC = "MXFP4 MoE-MLP tokens/s; decode HBM GB/s; prefill TFLOP/s vs peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0      # dense fp4 MFMA
+CACHE_BYTES = 256 << 20        # Infinity Cache (MALL)
+DEFAULT_WORKLOAD = "moe-20b-prefill-T8192-skewed"
+
+
+def workloads():
+    from mxfp4_weight_quantized_amd import inputs
+    w = {}
+    for s in (inputs.MOE_20B_DECODE, inputs.MOE_20B_PREFILL, *inputs.MOE_120B.values()):
+        w[s.name] = ("moe", s, 0)
+    for T in (1, 256, 4096):
+        s = inputs.MOE_120B[T]
+        w["moe-120b-mxact-T%d" % T] = ("moe", s, 1)
+    for M in (1, 8, 32):
+        w["linear-decode-M%d" % M] = ("linear", dict(M=M, K=2880, N=5760, seed=1), 0)
+    return w
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "mxfp4_weight_quantized_amd", "csrc", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------------------------
+def _upload_bf16(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def setup_moe(shape, flags, want_host_weights):
+    """Device inputs for a MoE layer; weights drawn in fp32 and packed by the HIP quantizer.
+    With want_host_weights the same draws are also packed by the oracle for the CPU leg."""
+    import numpy as np
+    import torch
+    import mxfp4_weight_quantized_amd as mx
+    from mxfp4_weight_quantized_amd import inputs
+    s = shape
+    E, H, F = s.E, s.H, s.F
+    gp = torch.empty((E, 2 * F, H // 2), dtype=torch.uint8, device="cuda")
+    gs = torch.empty((E, 2 * F, H // 32), dtype=torch.uint8, device="cuda")
+    dp = torch.empty((E, H, F // 2), dtype=torch.uint8, device="cuda")
+    ds = torch.empty((E, H, F // 32), dtype=torch.uint8, device="cuda")
+    host = None
+    if want_host_weights:
+        host = [np.empty(t.shape, np.uint8) for t in (gp, gs, dp, ds)]
+        import oracle
+
+    def draw(e):
+        return e, inputs.gate_up_f32(s.seed, e, F, H), inputs.down_f32(s.seed, e, H, F)
+
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(8) as ex:
+        for e, wgu, wdn in ex.map(draw, range(E)):
+            mx.mxfp4_quantize(torch.from_numpy(wgu).cuda(), gp[e], gs[e])
+            mx.mxfp4_quantize(torch.from_numpy(wdn).cuda(), dp[e], ds[e])
+            if host is not None:
+                host[0][e], host[1][e] = oracle.quantize(wgu)
+                host[2][e], host[3][e] = oracle.quantize(wdn)
+    torch.cuda.synchronize()
+    wr, br = inputs.router(s.seed, E, H, s.bias_std)
+    return (gp, gs, dp, ds), wr, (br if s.bias_std else None), host
+
+
+def touched_stats(idx_np, E):
+    import numpy as np
+    cnt = np.bincount(idx_np.reshape(-1), minlength=E)
+    return int((cnt > 0).sum()), int(cnt.sum())
+
+
+def kernel_work(name, T, H, F, E, k, touched, P, out_bytes, mxact):
+    """Algorithmic (flops, bytes) of one launch of a kernel kind."""
+    wb = 17.0 / 32.0                 # packed bytes per weight (nibble + 1/32 scale byte)
+    abytes = 17.0 / 32.0 if mxact else 2.0   # activation bytes per element read by a GEMM
+    if name == "moe_gate_up_swiglu":
+        return 2.0 * P * H * 2 * F, touched * 2 * F * H * wb + T * H * abytes + P * F * 2
+    if name == "moe_down_weighted":
+        return 2.0 * P * F * H, touched * H * F * wb + P * F * abytes + P * H * 4
+    if name == "moe_combine":
+        return P * H, P * H * 4 + T * H * out_bytes
+    if name == "route_topk":
+        return 2.0 * T * E * H, T * H * 2 + E * H * 2 + T * E * 4 + T * k * 8
+    if name == "permute":
+        return 0.0, T * k * 4 * 4 + (E + 1) * 4
+    if name == "quantize":
+        return 0.0, (T + P) * H * (2 + wb)
+    return 0.0, 0.0
+
+
+def roofline_entry(flops, nbytes, avg_ms, peak_mfma):
+    ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if nbytes > 0 and flops / nbytes > ridge:
+        ach = flops / (avg_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak_mfma,
+                "unit": "TFLOP/s", "frac": round(ach / peak_mfma, 4)}
+    ach = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4)}
+
+
+def read_traffic(workload, kernel):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken on the
+    current kernel sources; else None."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(workload, {}).get(kernel)
+    if not ent or ent.get("source_sha") != source_sha():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------------------------
+def bench_moe(args, name, shape, flags):
+    import numpy as np
+    import torch
+    import mxfp4_weight_quantized_amd as mx
+    from mxfp4_weight_quantized_amd import inputs
+    s = shape
+    want_cpu = not args.no_cpu_baseline
+    weights, wr_np, br_np, host_w = setup_moe(s, flags, want_cpu)
+    wr = _upload_bf16(wr_np)
+    br = torch.from_numpy(br_np).cuda() if br_np is not None else None
+    layer_bytes = s.E * (2 * s.F * s.H + s.H * s.F) * 17 // 32
+    # token batches: decode-shaped runs rotate through several batches (different experts)
+    n_x = 1 if s.T * s.k >= 48 * s.E else 16
+    x_all = inputs.activations(s.seed, s.T * n_x, s.H)
+    xs = [_upload_bf16(x_all[i * s.T:(i + 1) * s.T]) for i in range(n_x)]
+    # routing of every batch (outside the timed region) -> touched experts per step
+    stats = []
+    for x in xs:
+        _, idx, _ = mx.moe_route_topk(x, wr, br, s.k, want_logits=False)
+        stats.append(touched_stats(idx.cpu().numpy(), s.E))
+    touched = float(np.mean([t for t, _ in stats]))
+    step_bytes = touched * layer_bytes / s.E
+    n_w = 1
+    if step_bytes * n_x < 2 * CACHE_BYTES or layer_bytes < 2 * CACHE_BYTES:
+        n_w = int(min(8, max(1, math.ceil(2 * CACHE_BYTES / max(1.0, min(layer_bytes, step_bytes * n_x))))))
+    wsets = [weights] + [tuple(t.clone() for t in weights) for _ in range(n_w - 1)]
+    out_dtype = torch.bfloat16
+    out = torch.empty((s.T, s.H), dtype=out_dtype, device="cuda")
+    descs = []
+    for i in range(max(n_x, n_w)):
+        gp, gs, dp, ds = wsets[i % n_w]
+        descs.append(mx.make_moe_desc(xs[i % n_x], gp, gs, dp, ds, s.k, out, wr=wr, br=br,
+                                      flags=flags))
+    ws_bytes = max(mx.mxfp4_moe_mlp_workspace(d) for d in descs)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    L = mx.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    import ctypes
+    refs = [ctypes.byref(d) for d in descs]
+
+    def step(i):
+        st = L.mxfp4_moe_mlp(refs[i % len(refs)], ws.data_ptr(), ws_bytes, sh)
+        if st != 0:
+            raise mx.MXError(st, mx.last_error())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # per-kernel times over a second pass of the same steps (events recorded by the library)
+    mx.mx_profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = mx.mx_profile_read()
+    mx.mx_profile_enable(False)
+
+    P = s.T * s.k
+    peak = PEAK_FP4_TFLOPS if flags else PEAK_BF16_TFLOPS
+    kern = {}
+    for kname, (n, tot) in prof.items():
+        fl, by = kernel_work(kname, s.T, s.H, s.F, s.E, s.k, touched, P, 2, bool(flags))
+        kern[kname] = {"avg_ms": round(tot / n, 5), "launches": n, "flops": fl, "bytes": by}
+    dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
+    d = kern[dom]
+    roof = roofline_entry(d["flops"], d["bytes"], d["avg_ms"], peak)
+    roof["traffic"] = read_traffic(name, dom)
+    roof["kernel"] = dom
+    roof["avg_ms"] = d["avg_ms"]
+    roof["algorithmic_bytes"] = int(d["bytes"])
+    roof["algorithmic_flops"] = d["flops"]
+
+    layer_flops = 2.0 * P * (s.H * 2 * s.F + s.F * s.H)
+    layer_traffic = touched * layer_bytes / s.E + s.T * s.H * 2 * 2
+    result = {
+        "metric": METRIC, "value": round(s.T / (ms * 1e-3), 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4" if flags else "bf16", "data": "synthetic",
+        "config": {"workload": name, "T": s.T, "H": s.H, "F": s.F, "E": s.E, "k": s.k,
+                   "weights": "mxfp4 (e2m1 + e8m0 per 32)", "activations": "mxfp4" if flags else "bf16",
+                   "out_dtype": "bf16", "router_bias_std": s.bias_std, "seed": s.seed,
+                   "parallelism": "single-gpu", "weight_copies": n_w, "token_batches": n_x},
+        "step": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
+                 "hbm_gbs_algorithmic": round(layer_traffic / (ms * 1e-3) / 1e9, 1),
+                 "touched_experts": touched},
+        "kernels": kern,
+        "roofline": roof,
+    }
+    if want_cpu:
+        result["cpu_baseline"] = cpu_baseline_moe(args, s, x_all[:s.T], wr_np, br_np, host_w)
+    return result
+
+
+def cpu_baseline_moe(args, s, x_np, wr_np, br_np, host_w):
+    """The oracle (router + top-k + MoE MLP) on the first tokens of the same batch, in chunks,
+    until about args.cpu_seconds of wall time have passed."""
+    import numpy as np
+    import oracle
+    chunk = max(1, min(s.T, oracle.num_threads()))
+    done = 0
+    t0 = time.perf_counter()
+    while done < s.T and time.perf_counter() - t0 < args.cpu_seconds:
+        n = min(chunk, s.T - done)
+        xc = np.ascontiguousarray(x_np[done:done + n])
+        lg = oracle.router_logits(xc, wr_np, br_np)
+        idx, w = oracle.topk_softmax(lg, s.k)
+        oracle.moe_mlp(xc, idx, w, *host_w, E=s.E)
+        done += n
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "first %d of the %d tokens: router, top-%d softmax and MoE MLP in the fp64 "
+                      "C oracle, %.1f s wall" % (done, s.T, s.k, el)}
+
+
+def bench_linear(args, name, cfg):
+    import numpy as np
+    import torch
+    import mxfp4_weight_quantized_amd as mx
+    from mxfp4_weight_quantized_amd import inputs
+    M, K, N, seed = cfg["M"], cfg["K"], cfg["N"], cfg["seed"]
+    x = _upload_bf16(inputs.activations(seed, M, K))
+    w = inputs.linear_weight_f32(seed, N, K)
+    p, sc = mx.mxfp4_quantize(torch.from_numpy(w).cuda())
+    wbytes = N * K * 17 // 32
+    n_w = max(1, math.ceil(2 * CACHE_BYTES / wbytes))
+    wsets = [(p, sc)] + [(p.clone(), sc.clone()) for _ in range(n_w - 1)]
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    L = mx.lib()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i):
+        pp, ss = wsets[i % n_w]
+        st = L.mxfp4_linear(x.data_ptr(), M, K, pp.data_ptr(), ss.data_ptr(), N, out.data_ptr(),
+                            mx.MX_BF16, 0, None, 0, sh)
+        if st != 0:
+            raise mx.MXError(st, mx.last_error())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    mx.mx_profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = mx.mx_profile_read()
+    mx.mx_profile_enable(False)
+    n, tot = prof["linear"]
+    avg = tot / n
+    flops = 2.0 * M * K * N
+    nbytes = wbytes + M * K * 2 + M * N * 2
+    roof = roofline_entry(flops, nbytes, avg, PEAK_BF16_TFLOPS)
+    roof.update({"traffic": read_traffic(name, "linear"), "kernel": "linear",
+                 "avg_ms": round(avg, 5), "algorithmic_bytes": nbytes, "algorithmic_flops": flops})
+    result = {
+        "metric": METRIC, "value": round(M / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "M": M, "K": K, "N": N, "seed": seed, "weight_copies": n_w,
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        xh = inputs.activations(seed, M, K)
+        ph, sh_ = oracle.quantize(w)
+        reps, t0c = 0, time.perf_counter()
+        while time.perf_counter() - t0c < min(args.cpu_seconds, 5.0) or reps == 0:
+            oracle.linear(xh, ph, sh_)
+            reps += 1
+        el = time.perf_counter() - t0c
+        result["cpu_baseline"] = {"value": round(reps * M / el, 3), "unit": "tokens/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": "%d full calls (%d tokens each), %.1f s wall" % (reps, M, el)}
+    return result
+
+
+def calibrate_copy(nbytes=1 << 30):
+    """A plain device copy of known size, so counter runs can scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(a, 1.0, out=b)   # reads nbytes, writes nbytes
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------------------------
+def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from two rocprofv3 --pmc
+    runs of `bench.py --calibrate-copy`, scaled by what the copy kernel's counters read for its
+    known traffic; writes profiles/traffic.json and prints a text summary."""
+    def load(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        acc = {}
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                if row.get("Counter_Name") != counter:
+                    continue
+                k = row.get("Kernel_Name", "")
+                acc.setdefault(k, []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    copy_k = [k for k in fetch if "elementwise" in k or "copy" in k.lower()]
+    if not copy_k:
+        raise SystemExit("no copy kernel in the counter output")
+    ck = max(copy_k, key=lambda k: fetch[k])
+    f_fetch = copy_bytes / (fetch[ck] * 1024.0)
+    f_write = copy_bytes / (write[ck] * 1024.0)
+    kinds = {"moe_gate_up_swiglu": "moe_gate_up_swiglu_kernel", "moe_down_weighted":
+             "moe_down_weighted_kernel", "moe_combine": "combine_kernel", "route_topk":
+             "route_topk_kernel", "permute": "permute_kernel", "linear": "linear_kernel"}
+    out = {}
+    for kind, sym in kinds.items():
+        ks = [k for k in fetch if sym in k]
+        if not ks:
+            continue
+        fk = sum(fetch[k] for k in ks) / len(ks)
+        wk = sum(write.get(k, 0.0) for k in ks) / len(ks)
+        out[kind] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                     "hbm_bytes_per_launch": int(fk * 1024 * f_fetch + wk * 1024 * f_write),
+                     "copy_scale_fetch": round(f_fetch, 4), "copy_scale_write": round(f_write, 4),
+                     "source_sha": source_sha()}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--traffic-workload", default=None,
+                    help="with --summarize-counters: workload name to file the numbers under")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        wl = args.traffic_workload or args.workload
+        res = summarize_counters(*args.summarize_counters)
+        data = {}
+        if os.path.exists(TRAFFIC_FILE):
+            data = json.load(open(TRAFFIC_FILE))
+        data[wl] = res
+        os.makedirs(PROFILES, exist_ok=True)
+        json.dump(data, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+        print(json.dumps({wl: res}, indent=1))
+        return 0
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        return 2
+    wl = workloads()
+    if args.workload not in wl:
+        print("unknown workload %s; choose from %s" % (args.workload, sorted(wl)), file=sys.stderr)
+        return 2
+    kind, cfg, flags = wl[args.workload]
+    if kind == "moe":
+        res = bench_moe(args, args.workload, cfg, flags)
+    else:
+        res = bench_linear(args, args.workload, cfg)
+    if args.calibrate_copy:
+        calibrate_copy()
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -64,7 +64,8 @@ typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
 /* Upper limits checked on the host. */
 #define MX_MAX_EXPERTS 256
 #define MX_MAX_TOPK 8
-#define MX_MAX_K 8192            /* reduction length of mxfp4_linear and of H, F in the MoE MLP */
+#define MX_MAX_K 8192            /* reduction length K of mxfp4_linear */
+#define MX_MAX_MOE_DIM 3072      /* H and F of the MoE MLP */
 
 /* ------------------------------------------------------------------------------------------------
  * mxfp4_quantize -- pack `rows` rows of K values into MXFP4 ([EN] "What MXFP4 Is").
@@ -148,7 +149,7 @@ size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc);
 
 /*   desc (host pointer) as above; ws: device workspace of at least mxfp4_moe_mlp_workspace(desc)
  *   bytes, 256-byte aligned, owned by the caller, contents need not be initialized.
- *   Limits: H, F multiples of 32 and <= MX_MAX_K; E, k as for moe_route_topk; all weight, x and
+ *   Limits: H, F multiples of 32 and <= MX_MAX_MOE_DIM; E, k as for moe_route_topk; all weight, x and
  *   out pointers 16-byte aligned. Routing indices outside [0, E) (caller routing) are skipped and
  *   flagged in the workspace status word (read it with mx_workspace_status); their tokens'
  *   outputs then lack those experts. Concurrent calls must use distinct workspaces. */
@@ -177,6 +178,22 @@ const char* mx_last_error(void);
 mx_status mx_workspace_status(const void* ws, void* stream, int32_t* status);
 /* Library version string. */
 const char* mx_version(void);
+
+/* ------------------------------------------------------------------------------------------------
+ * Kernel timing, for benchmarks. While enabled, every kernel the entry points above launch is
+ * bracketed by two HIP events recorded on the caller's stream (small per-launch overhead).
+ * mx_profile_enable(0|1) clears what was recorded and switches recording off or on.
+ * mx_profile_read synchronizes the recorded events, writes up to `max` entries (one per kernel
+ * kind that ran: name, launch count, summed milliseconds) to `out` (host array), clears the
+ * record and returns the number of kinds.
+ * ---------------------------------------------------------------------------------------------- */
+typedef struct {
+  const char* name;
+  int32_t launches;
+  double total_ms;
+} mx_kernel_time;
+mx_status mx_profile_enable(int enable);
+int32_t mx_profile_read(mx_kernel_time* out, int32_t max);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,12 @@ class MXError(RuntimeError):
         self.status = status
 
 
+class KernelTime(ctypes.Structure):
+    """Mirror of ``mx_kernel_time``."""
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
 class MoeDesc(ctypes.Structure):
     """Mirror of ``mx_moe_desc``."""
     _fields_ = [
@@ -66,6 +72,8 @@ SIGNATURES = {
     "mx_last_error": (ctypes.c_char_p, []),
     "mx_workspace_status": (_INT, [_VP, _VP, ctypes.POINTER(ctypes.c_int32)]),
     "mx_version": (ctypes.c_char_p, []),
+    "mx_profile_enable": (_INT, [_INT]),
+    "mx_profile_read": (_I32, [ctypes.POINTER(KernelTime), _I32]),
 }
 
 
@@ -253,3 +261,16 @@ def workspace_status(workspace: torch.Tensor, stream=None) -> int:
 
 def version() -> str:
     return lib().mx_version().decode()
+
+
+def mx_profile_enable(enable: bool = True):
+    """Switch per-kernel event timing on or off (clears what was recorded)."""
+    _check(lib().mx_profile_enable(1 if enable else 0))
+
+
+def mx_profile_read() -> dict:
+    """{kernel kind: (launches, total milliseconds)} recorded since the last enable/read."""
+    buf = (KernelTime * 16)()
+    n = lib().mx_profile_read(buf, 16)
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms))
+            for i in range(min(n, 16))}

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "../../include/mxfp4moe.h"
 #include "mx_launch.h"
@@ -59,6 +60,54 @@ mx_status check_device() {
   if (g_init_err != hipSuccess) return hip_fail(g_init_err, "kernel setup");
   return MX_OK;
 }
+
+// ---- opt-in per-kernel timing (benchmarks): HIP events on the caller's stream ----
+enum ProfKind { PK_QUANTIZE, PK_DEQUANTIZE, PK_ROUTE, PK_PERMUTE, PK_GATE_UP, PK_DOWN, PK_COMBINE,
+                PK_LINEAR, PK_COUNT };
+const char* const kProfNames[PK_COUNT] = {"quantize", "dequantize", "route_topk", "permute",
+                                          "moe_gate_up_swiglu", "moe_down_weighted", "moe_combine",
+                                          "linear"};
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t prof_event() {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with two events when profiling is on; no-op otherwise.
+struct ProfScope {
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  ProfScope(int k, hipStream_t st) : kind(k), s(st) {
+    if (g_prof_on.load(std::memory_order_relaxed)) {
+      a = prof_event();
+      if (a) hipEventRecord(a, s);
+    }
+  }
+  ~ProfScope() {
+    if (!a) return;
+    hipEvent_t b = prof_event();
+    if (!b) return;
+    hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_recs.push_back({kind, a, b});
+  }
+};
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -114,7 +163,7 @@ mx_status check_moe_desc(const mx_moe_desc* d) {
   mx_status st = check_routing_shape(d->T, d->H, d->E, d->k);
   if (st != MX_OK) return st;
   if (d->F <= 0 || d->H % 32 || d->F % 32) return fail(MX_ERR_SHAPE, "H=%d and F=%d must be positive multiples of 32", d->H, d->F);
-  if (d->H > 3072 || d->F > 3072) return fail(MX_ERR_SHAPE, "H and F must be <= 3072 in the MoE MLP");
+  if (d->H > MX_MAX_MOE_DIM || d->F > MX_MAX_MOE_DIM) return fail(MX_ERR_SHAPE, "H and F must be <= %d in the MoE MLP", MX_MAX_MOE_DIM);
   if (d->flags & ~MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
   if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "out_dtype %d", (int)d->out_dtype);
   if (d->T == 0) return MX_OK;
@@ -140,6 +189,7 @@ MX_API mx_status mxfp4_quantize(const void* src, mx_dtype src_dtype, int64_t row
   if (!aligned(src, src_dtype == MX_F32 ? 16 : 8) || !aligned(packed, 16)) return fail(MX_ERR_ALIGN, "src or packed misaligned");
   mx_status st = check_device();
   if (st != MX_OK) return st;
+  ProfScope ps(PK_QUANTIZE, (hipStream_t)stream);
   hipError_t e = mx::launch_quantize(src, src_dtype == MX_BF16, rows * (K / 32), packed, scales, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "quantize launch");
 }
@@ -153,6 +203,7 @@ MX_API mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, 
   if (!aligned(packed, 16) || !aligned(dst, 16)) return fail(MX_ERR_ALIGN, "packed or dst misaligned");
   mx_status st = check_device();
   if (st != MX_OK) return st;
+  ProfScope ps(PK_DEQUANTIZE, (hipStream_t)stream);
   hipError_t e = mx::launch_dequantize(packed, scales, rows * (K / 32), dst, dst_dtype == MX_BF16, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "dequantize launch");
 }
@@ -168,6 +219,7 @@ MX_API mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const flo
   if (!aligned(x, 16) || !aligned(wr, 16)) return fail(MX_ERR_ALIGN, "x and wr must be 16-byte aligned");
   st = check_device();
   if (st != MX_OK) return st;
+  ProfScope ps(PK_ROUTE, (hipStream_t)stream);
   hipError_t e = mx::launch_route_topk(x, wr, br, T, H, E, k, logits, topk_idx, topk_w, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "route launch");
 }
@@ -181,6 +233,7 @@ MX_API mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int3
   if (T > 0 && (!topk_idx || !perm || !inv)) return fail(MX_ERR_NULL, "topk_idx, perm and inv are required");
   st = check_device();
   if (st != MX_OK) return st;
+  ProfScope ps(PK_PERMUTE, (hipStream_t)stream);
   hipError_t e = mx::launch_permute(topk_idx, T, k, E, offsets, perm, inv, status, 0, nullptr, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
 }
@@ -212,7 +265,10 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
     float* logits = d.logits_out ? d.logits_out : reinterpret_cast<float*>(w + L.logits);
     int32_t* oi = d.topk_idx_out ? d.topk_idx_out : reinterpret_cast<int32_t*>(w + L.idx);
     float* ow = d.topk_w_out ? d.topk_w_out : reinterpret_cast<float*>(w + L.w);
-    e = mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, s);
+    {
+      ProfScope ps(PK_ROUTE, s);
+      e = mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "route launch");
     idx = oi;
     tw = ow;
@@ -224,7 +280,10 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   int32_t* perm = reinterpret_cast<int32_t*>(w + L.perm);
   int32_t* inv = reinterpret_cast<int32_t*>(w + L.inv);
   int2* tiles = reinterpret_cast<int2*>(w + L.tiles);
-  e = mx::launch_permute(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows, tiles, status + 1, s);
+  {
+    ProfScope ps(PK_PERMUTE, s);
+    e = mx::launch_permute(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows, tiles, status + 1, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "permute launch");
   mx::MoeGemmArgs g{};
   g.T = d.T; g.H = d.H; g.F = d.F; g.E = d.E; g.k = d.k;
@@ -242,8 +301,21 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   g.y = reinterpret_cast<float*>(w + L.y);
   g.out = d.out;
   g.out_bf16 = d.out_dtype == MX_BF16;
-  e = mx::launch_moe_gemms(g, s);
-  if (e != hipSuccess) return hip_fail(e, "grouped GEMM launch");
+  {
+    ProfScope ps(PK_GATE_UP, s);
+    e = mx::launch_moe_gate_up(g, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "gate_up launch");
+  {
+    ProfScope ps(PK_DOWN, s);
+    e = mx::launch_moe_down(g, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "down launch");
+  {
+    ProfScope ps(PK_COMBINE, s);
+    e = mx::launch_moe_combine(g, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }
 
@@ -268,6 +340,7 @@ MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uin
   }
   mx_status st = check_device();
   if (st != MX_OK) return st;
+  ProfScope ps(PK_LINEAR, (hipStream_t)stream);
   hipError_t e = mx::launch_linear(x, M, K, packed, scales, N, y, y_dtype == MX_BF16, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "linear launch");
 }
@@ -279,6 +352,41 @@ MX_API mx_status mx_workspace_status(const void* ws, void* stream, int32_t* stat
   hipError_t e = hipMemcpyAsync(status, ws, sizeof(int32_t), hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "status read");
+}
+
+MX_API mx_status mx_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const ProfRec& r : g_prof_recs) {
+    hipEventSynchronize(r.b);
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  g_prof_on.store(enable != 0);
+  return ok();
+}
+
+MX_API int32_t mx_profile_read(mx_kernel_time* out, int32_t max) {
+  double total[PK_COUNT] = {0};
+  int32_t count[PK_COUNT] = {0};
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (const ProfRec& r : g_prof_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      total[r.kind] += ms;
+      count[r.kind] += 1;
+    }
+    g_event_pool.push_back(r.a);
+    g_event_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  int32_t n = 0;
+  for (int k = 0; k < PK_COUNT; ++k) {
+    if (count[k] == 0) continue;
+    if (out && n < max) out[n] = mx_kernel_time{kProfNames[k], count[k], total[k]};
+    ++n;
+  }
+  return n;
 }
 
 MX_API const char* mx_version(void) { return "mxfp4moe 0.1 (gfx950)"; }

@@ -69,7 +69,7 @@ __device__ __forceinline__ void wait_stage(int ahead) {
 }
 
 template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int NBMAX>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmKArgs p) {
+__device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
@@ -292,6 +292,20 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmKArgs p) {
   }
 }
 
+// One kernel name per role, so profiles show which product a launch is.
+template <int BM, int BN, int WM, int WN, int KT, int ST, int NBM>
+__global__ __launch_bounds__(WM * WN * 64) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, NBM>(p);
+}
+template <int BM, int BN, int WM, int WN, int KT, int ST, int NBM>
+__global__ __launch_bounds__(WM * WN * 64) void moe_down_weighted_kernel(GemmKArgs p) {
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, NBM>(p);
+}
+template <int BM, int BN, int WM, int WN, int KT, int ST, int NBM>
+__global__ __launch_bounds__(WM * WN * 64) void linear_kernel(GemmKArgs p) {
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, NBM>(p);
+}
+
 // out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
 // indices) contribute nothing.
 template <bool BF16_OUT>
@@ -327,8 +341,13 @@ constexpr int kNBMaxLarge = 256;    // K <= 8192 (decode tiles only)
 template <int BM, int BN, int WM, int WN, int KT, int ST, int MODE, int NBM>
 hipError_t launch_gemm(const GemmKArgs& a, int grid_x, int n_cols_tiles, hipStream_t stream) {
   if (grid_x <= 0 || n_cols_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, KT, ST, MODE, NBM>), dim3(grid_x, n_cols_tiles),
-                     dim3(WM * WN * 64), 0, stream, a);
+  const dim3 grid(grid_x, n_cols_tiles), block(WM * WN * 64);
+  if constexpr (MODE == MODE_GATE_UP)
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<BM, BN, WM, WN, KT, ST, NBM>), grid, block, 0, stream, a);
+  else if constexpr (MODE == MODE_DOWN)
+    hipLaunchKernelGGL((moe_down_weighted_kernel<BM, BN, WM, WN, KT, ST, NBM>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((linear_kernel<BM, BN, WM, WN, KT, ST, NBM>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -342,11 +361,9 @@ int moe_max_tiles(int T, int k, int E, int tile_rows) {
   return (int)(((int64_t)T * k + tile_rows - 1) / tile_rows) + E;
 }
 
-hipError_t launch_moe_gemms(const MoeGemmArgs& m, hipStream_t stream) {
-  const int P = m.T * m.k;
-  const bool pre = use_prefill_tiles(m.T, m.k, m.E);
+hipError_t launch_moe_gate_up(const MoeGemmArgs& m, hipStream_t stream) {
+  // A = x rows gathered through perm / k, B = W_gu[e] (2F rows), out = h [P][F]
   GemmKArgs g{};
-  // gate_up: A = x rows gathered through perm / k, B = W_gu[e] (2F rows), out = h [P][F]
   g.A = m.x;
   g.a_gather = m.perm;
   g.a_div = m.k;
@@ -361,14 +378,13 @@ hipError_t launch_moe_gemms(const MoeGemmArgs& m, hipStream_t stream) {
   g.offsets = m.offsets;
   g.F = m.F;
   g.out = m.h;
-  hipError_t err;
-  if (pre)
-    err = launch_gemm<128, 128, 2, 2, 4, 3, MODE_GATE_UP, kNBMax>(g, m.max_tiles, (m.F + 63) / 64, stream);
-  else
-    err = launch_gemm<16, 64, 1, 2, 8, 4, MODE_GATE_UP, kNBMax>(g, m.max_tiles, (m.F + 31) / 32, stream);
-  if (err != hipSuccess) return err;
+  if (use_prefill_tiles(m.T, m.k, m.E))
+    return launch_gemm<128, 128, 2, 2, 4, 3, MODE_GATE_UP, kNBMax>(g, m.max_tiles, (m.F + 63) / 64, stream);
+  return launch_gemm<16, 64, 1, 2, 8, 4, MODE_GATE_UP, kNBMax>(g, m.max_tiles, (m.F + 31) / 32, stream);
+}
 
-  // down: A = h rows (permuted order), B = W_dn[e] (H rows), out = Y[pair] * w
+hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
+  // A = h rows (permuted order), B = W_dn[e] (H rows), out = Y[pair] * routing weight
   GemmKArgs d{};
   d.A = m.h;
   d.a_gather = nullptr;
@@ -386,12 +402,12 @@ hipError_t launch_moe_gemms(const MoeGemmArgs& m, hipStream_t stream) {
   d.out = m.y;
   d.perm = m.perm;
   d.rw = m.topk_w;
-  if (pre)
-    err = launch_gemm<128, 128, 2, 2, 4, 3, MODE_DOWN, kNBMax>(d, m.max_tiles, (m.H + 127) / 128, stream);
-  else
-    err = launch_gemm<16, 64, 1, 4, 8, 4, MODE_DOWN, kNBMax>(d, m.max_tiles, (m.H + 63) / 64, stream);
-  if (err != hipSuccess) return err;
+  if (use_prefill_tiles(m.T, m.k, m.E))
+    return launch_gemm<128, 128, 2, 2, 4, 3, MODE_DOWN, kNBMax>(d, m.max_tiles, (m.H + 127) / 128, stream);
+  return launch_gemm<16, 64, 1, 4, 8, 4, MODE_DOWN, kNBMax>(d, m.max_tiles, (m.H + 63) / 64, stream);
+}
 
+hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {
   const int64_t n4 = (int64_t)m.T * (m.H / 4);
   const unsigned grid = (unsigned)((n4 + 255) / 256);
   if (m.out_bf16)
@@ -400,7 +416,6 @@ hipError_t launch_moe_gemms(const MoeGemmArgs& m, hipStream_t stream) {
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, stream, m.y, m.inv, m.T,
                        m.H, m.k, m.out);
-  (void)P;
   return hipGetLastError();
 }
 

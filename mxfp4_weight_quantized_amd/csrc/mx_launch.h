@@ -43,7 +43,9 @@ struct MoeGemmArgs {
 // Tile rows (BM) the grouped GEMMs use for this problem; the permutation's tile list must match.
 int moe_tile_rows(int T, int k, int E);
 int moe_max_tiles(int T, int k, int E, int tile_rows);
-hipError_t launch_moe_gemms(const MoeGemmArgs& a, hipStream_t stream);
+hipError_t launch_moe_gate_up(const MoeGemmArgs& a, hipStream_t stream);
+hipError_t launch_moe_down(const MoeGemmArgs& a, hipStream_t stream);
+hipError_t launch_moe_combine(const MoeGemmArgs& a, hipStream_t stream);
 
 hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
                          const uint8_t* scales, int N, void* y, bool y_bf16, hipStream_t stream);
