@@ -164,6 +164,8 @@ mx_status check_moe_desc(const mx_moe_desc* d) {
   if (st != MX_OK) return st;
   if (d->F <= 0 || d->H % 32 || d->F % 32) return fail(MX_ERR_SHAPE, "H=%d and F=%d must be positive multiples of 32", d->H, d->F);
   if (d->H > MX_MAX_MOE_DIM || d->F > MX_MAX_MOE_DIM) return fail(MX_ERR_SHAPE, "H and F must be <= %d in the MoE MLP", MX_MAX_MOE_DIM);
+  if ((int64_t)d->T * d->H * 2 >= (1LL << 31) || (int64_t)d->T * d->k * d->F * 2 >= (1LL << 31))
+    return fail(MX_ERR_SHAPE, "T*H and T*k*F bf16 activations must stay below 2 GiB");
   if (d->flags & ~MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
   if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "out_dtype %d", (int)d->out_dtype);
   if (d->T == 0) return MX_OK;
@@ -331,6 +333,8 @@ MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uin
   if (y_dtype != MX_F32 && y_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "y_dtype %d", (int)y_dtype);
   if (M < 0 || N < 0 || K <= 0 || K % 32 || K > MX_MAX_K) return fail(MX_ERR_SHAPE, "M=%d K=%d N=%d (K a multiple of 32, <= %d)", M, K, N, MX_MAX_K);
   if (flags & ~MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if ((int64_t)M * K * 2 >= (1LL << 31) || (int64_t)N * (K / 2) >= (1LL << 31))
+    return fail(MX_ERR_SHAPE, "x and the packed weight must each stay below 2 GiB");
   if (M == 0 || N == 0) return ok();
   if (!x || !packed || !scales || !y) return fail(MX_ERR_NULL, "x, packed, scales and y are required");
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 16) || !aligned(y, 16)) return fail(MX_ERR_ALIGN, "x, packed, scales and y must be 16-byte aligned");

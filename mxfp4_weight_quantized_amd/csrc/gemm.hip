@@ -30,12 +30,13 @@ enum { MODE_LINEAR = 0, MODE_GATE_UP = 1, MODE_DOWN = 2 };
 
 struct GemmKArgs {
   const uint16_t* A;          // bf16 activation rows of length K
+  int64_t a_rows;             // rows in A (bounds the buffer view of A)
   const int32_t* a_gather;    // A row of permuted row r = a_gather[r] / a_div (NULL: r)
   int a_div;
   const uint8_t* Bp;          // packed weights, expert-major
   const uint8_t* Bs;          // scales, expert-major
   int64_t b_rows_per_expert;  // weight rows per expert (2F gate_up, H down, N linear)
-  int64_t bs_total;           // bytes in the whole scale array (bounds the scale copy)
+  int n_tiles;                // column tiles
   int N;                      // output columns (F for gate_up)
   int K;
   const int2* tiles;          // grouped: (expert, first permuted row); NULL = dense
@@ -49,26 +50,61 @@ struct GemmKArgs {
   const float* rw;            // down: routing weight of each pair
 };
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+template <int B, int E, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+  if constexpr (B < E) {
+    fn(IntC<B>{});
+    static_for<B + 1, E>(fn);
+  }
+}
+
+// LDS swizzles. A 16-byte chunk c of LDS row r is stored at slot c ^ swz(r). The per-lane
+// 16-byte reads of one MFMA operand cover 16 consecutive rows at the same chunk; these XOR
+// patterns were measured conflict-free on gfx950 for exactly that access (SQ_LDS_BANK_CONFLICT
+// = 0 for ds_read_b128 over 16 rows x 4 lane groups; e.g. "r & 15" on 256-byte rows costs 2x):
+//   A rows (KT*64 bytes, >= 16 chunks): swz = ((r & 7) << 1) | ((r >> 3) & 1).
+//   B rows (KT*16 bytes): KT = 4 -> ((r >> 2) ^ (r >> 1)) & 3; KT = 8 -> (r ^ (r >> 3)) & 7.
+__device__ __forceinline__ int swz_a(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 template <int KT>
 __device__ __forceinline__ int swz_b(int row) {
-  static_assert(KT == 4 || KT == 8 || KT == 16, "K tile");
-  constexpr int SH = KT == 4 ? 2 : (KT == 8 ? 1 : 0);
-  return (row >> SH) & (KT - 1);
+  static_assert(KT == 4 || KT == 8, "K tile");
+  if constexpr (KT == 4) return ((row >> 2) ^ (row >> 1)) & 3;
+  else return (row ^ (row >> 3)) & 7;
 }
 
-template <int LPS, int STAGES>
-__device__ __forceinline__ void wait_stage(int ahead) {
-  // ahead = number of later stages already issued (0 .. STAGES-2)
-  if constexpr (STAGES >= 4) {
-    if (ahead >= 2) { wait_vmcnt<2 * LPS>(); return; }
-  }
-  if constexpr (STAGES >= 3) {
-    if (ahead >= 1) { wait_vmcnt<LPS>(); return; }
-  }
-  wait_vmcnt<0>();
+// Buffer views. Loads go through buffer resources (base address, byte size): each lane keeps a
+// fixed 32-bit offset and the stage's K offset is a scalar, so issuing a stage costs no vector
+// ALU work; an offset at or past the size reads zeros, which is how blocks past the end of K are
+// filled (zero codes and zero activations contribute nothing, so the MFMA loop needs no masks).
+constexpr uint32_t kBufWord3 = 0x00020000u;   // raw, untyped buffer (gfx9 family)
+constexpr uint32_t kOutOfRange = 0xfffffff0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, int64_t bytes) {
+  const int nrec = bytes > 0x7ffffff0LL ? 0x7ffffff0 : (int)bytes;  // host checks keep it below
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, (int)kBufWord3);
 }
 
-template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int NBMAX>
+// E8M0 byte -> fp32 scale operand, without branches (b = 0: 2^-127; b = 255: NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t b) {
+  uint32_t u = b << 23;
+  u = (b == 0u) ? 0x00400000u : u;
+  u = (b == 255u) ? 0x7fc00000u : u;
+  return __uint_as_float(u);
+}
+
+// Grouped / dense MXFP4 GEMM tile: out[BM rows x BN cols] of A (bf16) times the decoded weights.
+//   BM x BN workgroup tile, WM x WN waves, each wave a (BM/WM) x (BN/WN) tile of 16 x 16 MFMA
+//   fragments; KT 32-element blocks per pipeline stage; STAGES (3 or 4) stages in flight.
+// Per stage a workgroup moves: A chunks and B chunks straight into LDS (direct loads), and the
+// stage's BN x KT scale bytes into registers; the scale bytes go to LDS (as fp32 scales) one
+// iteration later, when they have arrived, so no wait is ever placed on the newest stage.
+// Tiles are numbered m-fastest and handed out in contiguous ranges per XCD (workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2), so consecutive workgroups of
+// one XCD share the weight tile of one expert's column block.
+template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE>
 __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
@@ -80,117 +116,79 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * B_ROW;
   constexpr int IA = A_STAGE / 1024 / NW;
   constexpr int IB = B_STAGE / 1024 / NW;
-  constexpr int LPS = IA + IB;
+  constexpr int SS = KT / 4;                       // super-steps per stage
+  constexpr int NSB = (BN * KT + NT - 1) / NT;     // scale-byte loads per thread per stage
+  constexpr int LPS = NSB + IA + IB;               // vector-memory ops per wave per stage
   static_assert(IA * NW * 1024 == A_STAGE && IB * NW * 1024 == B_STAGE, "stage split");
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "wave tile");
   static_assert(!SWIGLU || FN % 2 == 0, "gate/up fragment pairs");
-  static_assert(KT % 4 == 0 && STAGES >= 2 && STAGES <= 4, "pipeline");
-  static_assert((STAGES - 1) * LPS < 64, "vmcnt range");
-  constexpr int SC_ROWS = SWIGLU ? BNH : BN;
-  constexpr int SC_REGION = (SC_ROWS * NBMAX + 16 + 15) / 16 * 16;
-  constexpr int SC_BYTES = SWIGLU ? 2 * SC_REGION : SC_REGION;
+  static_assert(KT % 4 == 0 && A_ROW >= 256 && STAGES == 3, "pipeline");
+  static_assert(2 * LPS < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t sA[STAGES][A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB[STAGES][B_STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t sS[SC_BYTES];
+  __shared__ float sSc[STAGES][BN * KT];
   __shared__ int sArow[BM];
-  __shared__ int sMis[2];
 
-  // ---- which tile ----
+  // ---- which tile (XCD-contiguous, m-fastest) ----
+  const bool grouped = p.tiles != nullptr;
+  const int num_mt = grouped ? *p.num_tiles : (p.M + BM - 1) / BM;
+  const int total = num_mt * p.n_tiles;
+  const int per_xcd = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per_xcd) return;
+  const int t = (blockIdx.x & 7) * per_xcd + slot;
+  if (t >= total) return;
+  const int mt = t % num_mt, nt = t / num_mt;
   int e, r0, row_end;
-  if (p.tiles != nullptr) {
-    if ((int)blockIdx.x >= *p.num_tiles) return;
-    const int2 t = p.tiles[blockIdx.x];
-    e = t.x;
-    r0 = t.y;
-    row_end = p.offsets[e + 1];
+  if (grouped) {
+    const int2 tl = p.tiles[mt];
+    e = __builtin_amdgcn_readfirstlane(tl.x);
+    r0 = __builtin_amdgcn_readfirstlane(tl.y);
+    row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
   } else {
     e = 0;
-    r0 = blockIdx.x * BM;
+    r0 = mt * BM;
     row_end = p.M;
   }
-  const int nt = blockIdx.y;
   const int K = p.K;
   const int nb = K >> 5;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets go in M0
   const int wm = wave / WN, wn = wave % WN;
   const int ln = lane & 15, g = lane >> 4;
 
-  // ---- activation row table, scale copy ----
-  for (int i = tid; i < BM; i += NT) {
-    const int r = min(r0 + i, row_end - 1);
-    sArow[i] = p.a_gather ? p.a_gather[r] / p.a_div : r;
-  }
-#pragma unroll
-  for (int rg = 0; rg < (SWIGLU ? 2 : 1); ++rg) {
-    const int64_t first_row = (int64_t)e * p.b_rows_per_expert +
-                              (SWIGLU ? (rg ? (int64_t)p.F + nt * BNH : (int64_t)nt * BNH)
-                                      : (int64_t)nt * BN);
-    const int64_t gstart = first_row * nb;
-    const int64_t gend = min(gstart + (int64_t)SC_ROWS * nb, p.bs_total);
-    const int64_t abase = gstart & ~(int64_t)3;
-    if (tid == 0) sMis[rg] = (int)(gstart - abase);
-    const int ndw = (int)((gend - abase + 3) >> 2);
-    for (int i = tid; i < ndw; i += NT) {
-      const int64_t off = abase + 4 * (int64_t)i;
-      uint32_t v;
-      if (off + 4 <= p.bs_total) {
-        v = *reinterpret_cast<const uint32_t*>(p.Bs + off);
-      } else {
-        v = 0;
-        for (int b = 0; b < 4; ++b)
-          if (off + b < p.bs_total) v |= (uint32_t)p.Bs[off + b] << (8 * b);
-      }
-      *reinterpret_cast<uint32_t*>(sS + rg * SC_REGION + 4 * i) = v;
-    }
-  }
-  __syncthreads();
-
-  // ---- per-lane global sources of the direct-to-LDS loads ----
-  const uint16_t* aptr[IA];
-  int achunk[IA];
-#pragma unroll
-  for (int q = 0; q < IA; ++q) {
-    const int off = (wave * IA + q) * 1024 + lane * 16;
-    const int lrow = off / A_ROW;
-    const int chunk = ((off % A_ROW) >> 4) ^ (lrow & 7);
-    achunk[q] = chunk;
-    aptr[q] = p.A + (int64_t)sArow[lrow] * K + chunk * 8;
-  }
-  const uint8_t* bptr[IB];
-  int bchunk[IB];
+  // ---- weight rows (within the expert) ----
+  auto weight_row = [&](int lrow) -> int {
+    if (SWIGLU)
+      return lrow < BNH ? min(nt * BNH + lrow, p.F - 1) : p.F + min(nt * BNH + lrow - BNH, p.F - 1);
+    return min(nt * BN + lrow, p.N - 1);
+  };
+  const int64_t rpe = p.b_rows_per_expert;
+  const __amdgpu_buffer_rsrc_t rB = make_buf(p.Bp + (int64_t)e * rpe * (K >> 1), rpe * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rS = make_buf(p.Bs + (int64_t)e * rpe * nb, rpe * nb);
+  const __amdgpu_buffer_rsrc_t rA = make_buf(p.A, p.a_rows * K * 2);
+  uint32_t voffB[IB];
+  int bblk[IB];
 #pragma unroll
   for (int q = 0; q < IB; ++q) {
     const int off = (wave * IB + q) * 1024 + lane * 16;
     const int lrow = off / B_ROW;
     const int chunk = ((off % B_ROW) >> 4) ^ swz_b<KT>(lrow);
-    int grow;
-    if (SWIGLU)
-      grow = lrow < BNH ? min(nt * BNH + lrow, p.F - 1) : p.F + min(nt * BNH + lrow - BNH, p.F - 1);
-    else
-      grow = min(nt * BN + lrow, p.N - 1);
-    bchunk[q] = chunk;
-    bptr[q] = p.Bp + ((int64_t)e * p.b_rows_per_expert + grow) * (K >> 1) + chunk * 16;
+    bblk[q] = chunk;
+    voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
   }
-
-  auto issue = [&](int kt, int st) {
+  // scale bytes this thread fetches per stage: (row, block) = idx / KT, idx % KT
+  uint32_t voffS[NSB];
+  int sblk[NSB];
 #pragma unroll
-    for (int q = 0; q < IA; ++q) {
-      const int blk = kt * KT + (achunk[q] >> 2);
-      const uint16_t* src = blk < nb ? aptr[q] + kt * KT * 32 : aptr[q] - achunk[q] * 8;
-      load_lds_16(src, &sA[st][(wave * IA + q) * 1024]);
-    }
-#pragma unroll
-    for (int q = 0; q < IB; ++q) {
-      const int blk = kt * KT + bchunk[q];
-      const uint8_t* src = blk < nb ? bptr[q] + kt * KT * 16 : bptr[q] - bchunk[q] * 16;
-      load_lds_16(src, &sB[st][(wave * IB + q) * 1024]);
-    }
-  };
-
-  // ---- per-lane LDS read coordinates ----
-  int brow[FN], scoff[FN];
+  for (int q = 0; q < NSB; ++q) {
+    const int idx = min(tid + q * NT, BN * KT - 1);
+    sblk[q] = idx % KT;
+    voffS[q] = (uint32_t)weight_row(idx / KT) * (uint32_t)nb + sblk[q];
+  }
+  int brow[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
     int base;
@@ -199,9 +197,57 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     else
       base = wn * TN + f * 16;
     brow[f] = base + ln;
-    const int rg = SWIGLU ? (brow[f] >= BNH) : 0;
-    scoff[f] = rg * SC_REGION + sMis[rg] + (brow[f] - rg * BNH) * nb;
   }
+
+  // ---- activation rows ----
+  for (int i = tid; i < BM; i += NT) {
+    const int r = min(r0 + i, row_end - 1);
+    sArow[i] = p.a_gather ? p.a_gather[r] / p.a_div : r;
+  }
+  __syncthreads();
+  uint32_t voffA[IA];
+  int ablk[IA];
+#pragma unroll
+  for (int q = 0; q < IA; ++q) {
+    const int off = (wave * IA + q) * 1024 + lane * 16;
+    const int lrow = off / A_ROW;
+    const int chunk = ((off % A_ROW) >> 4) ^ swz_a(lrow);
+    ablk[q] = chunk >> 2;
+    voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
+  }
+
+  // Issue one stage: scale bytes into `sbytes`, then A and B chunks into LDS. Every wave issues
+  // exactly LPS vector-memory ops. Full stages add the K offset as a scalar; the stage that
+  // holds the end of K moves it into the lane offsets and sends blocks past K out of range.
+  uint32_t sbytes[NSB];
+  auto issue = [&](int kt, int st) {
+    const bool full = (kt + 1) * KT <= nb;
+    const int kb = kt * KT;
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      const uint32_t vo = full ? voffS[q] : (kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange);
+      sbytes[q] = __builtin_amdgcn_raw_buffer_load_b8(rS, vo, full ? kb : 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < IA; ++q) {
+      const uint32_t vo = full ? voffA[q] : (kb + ablk[q] < nb ? voffA[q] + kb * 64 : kOutOfRange);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)&sA[st][(wave * IA + q) * 1024], 16,
+                                               vo, full ? kb * 64 : 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < IB; ++q) {
+      const uint32_t vo = full ? voffB[q] : (kb + bblk[q] < nb ? voffB[q] + kb * 16 : kOutOfRange);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)&sB[st][(wave * IB + q) * 1024], 16,
+                                               vo, full ? kb * 16 : 0, 0, 0);
+    }
+  };
+  auto store_scales = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+      const int idx = tid + q * NT;
+      if (idx < BN * KT) sSc[st][idx] = e8m0_scale(sbytes[q] & 0xffu);
+    }
+  };
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -209,45 +255,57 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int ntk = (nb + KT - 1) / KT;
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntk) issue(s, s);
-
-  for (int kt = 0; kt < ntk; ++kt) {
-    wait_stage<LPS, STAGES>(min(ntk - 1 - kt, STAGES - 2));
-    barrier_lds();
-    if (kt + STAGES - 1 < ntk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-    const int st = kt % STAGES;
+  // One stage of MFMAs: per super-step, load the wave's A fragments, then per B fragment decode
+  // the lane's 16-byte block (two codes per cvt) and run its 4 x FM MFMAs.
+  auto compute = [&](int st) {
     const uint8_t* As = sA[st];
-    const uint8_t* Bs = sB[st];
-    const bool tail = (kt + 1) * KT > nb;
+    const uint8_t* Bsm = sB[st];
+    const float* Sc = sSc[st];
 #pragma unroll
-    for (int j = 0; j < KT / 4; ++j) {
-      const int blk = kt * KT + 4 * j + g;
-      const bool kval = !tail || blk < nb;
-      bf16x8 bf[FN][4];
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int r = brow[f];
-        const u32x4 w = lds_read_b128(Bs + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-        const float sc = e8m0_to_f32(sS[scoff[f] + (kval ? blk : 0)]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bf[f][s] = fp4x8_to_bf16x8(kval ? w[s] : 0u, sc);
-      }
+    for (int j = 0; j < SS; ++j) {
+      bf16x8 a[FM][4];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * TM + i * 16 + ln;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          u32x4 a = lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ (r & 7)) << 4));
-          if (!kval) a = u32x4{0u, 0u, 0u, 0u};
-          const bf16x8 av = u32x4_as_bf16x8(a);
+        for (int s = 0; s < 4; ++s)
+          a[i][s] = u32x4_as_bf16x8(
+              lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ swz_a(r)) << 4)));
+      }
 #pragma unroll
-          for (int f = 0; f < FN; ++f) acc[i][f] = mfma16x16x32(av, bf[f][s], acc[i][f]);
+      for (int f = 0; f < FN; ++f) {
+        const int r = brow[f];
+        const u32x4 w = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
+        const float sc = Sc[r * KT + 4 * j + g];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 b = fp4x8_to_bf16x8(w[s], sc);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b, acc[i][f]);
         }
       }
     }
+  };
+
+  // Pipeline (3 stages). Issue order: group g = [scale bytes of stage g][A, B chunks of stage g];
+  // group kt+2 is issued in iteration kt. At iteration kt stage kt must have landed, and the
+  // scale bytes of stage kt+1 too (they are stored to LDS now, from the one register set that
+  // always holds the newest group's bytes); the chunks of stage kt+1 may still be in flight.
+  const int ntk = (nb + KT - 1) / KT;
+  issue(0, 0);
+  wait_vmcnt<0>();
+  store_scales(0);
+  if (ntk > 1) issue(1, 1);
+  int st = 0;
+  for (int kt = 0; kt < ntk; ++kt) {
+    const bool next = kt + 1 < ntk;
+    if (next) wait_vmcnt<IA + IB>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    if (next) store_scales(st == 2 ? 0 : st + 1);
+    if (kt + 2 < ntk) issue(kt + 2, st == 0 ? 2 : st - 1);
+    compute(st);
+    st = (st == 2) ? 0 : st + 1;
   }
 
   // ---- epilogue ----
@@ -264,7 +322,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
           const int col = nt * BNH + wn * (BNH / WN) + f * 16 + ln;
           if (col >= p.F) continue;
           const float gt = acc[i][f][q], up = acc[i][FN / 2 + f][q];
-          const float hv = gt / (1.f + expf(-gt)) * up;
+          const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
           h[(int64_t)r * p.F + col] = (uint16_t)f32_to_bf16_bits(hv);
         }
       } else if constexpr (MODE == MODE_DOWN) {
@@ -293,17 +351,17 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 }
 
 // One kernel name per role, so profiles show which product a launch is.
-template <int BM, int BN, int WM, int WN, int KT, int ST, int NBM>
+template <int BM, int BN, int WM, int WN, int KT, int ST>
 __global__ __launch_bounds__(WM * WN * 64) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, NBM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int NBM>
+template <int BM, int BN, int WM, int WN, int KT, int ST>
 __global__ __launch_bounds__(WM * WN * 64) void moe_down_weighted_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, NBM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int NBM>
+template <int BM, int BN, int WM, int WN, int KT, int ST>
 __global__ __launch_bounds__(WM * WN * 64) void linear_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, NBM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR>(p);
 }
 
 // out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
@@ -333,25 +391,74 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // ---- tile configurations ----
-// Decode-shaped (few rows per expert): 16-row tiles, weight streaming dominates.
-// Prefill-shaped: 128 x 128 tiles, MFMA dominates.
-constexpr int kNBMax = 96;          // scale blocks per row held in LDS (K <= 3072)
-constexpr int kNBMaxLarge = 256;    // K <= 8192 (decode tiles only)
+// Prefill-shaped (many rows per expert): 128 x 256 workgroup tiles, eight waves of 64 x 64 (two
+// waves per SIMD, so one wave's LDS reads and dequantization overlap the other's MFMAs).
+// Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, weight
+// streaming dominates.
+struct CfgPre { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, KT = 4, ST = 3; };
+struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3; };
+struct CfgDecDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3; };
 
-template <int BM, int BN, int WM, int WN, int KT, int ST, int MODE, int NBM>
-hipError_t launch_gemm(const GemmKArgs& a, int grid_x, int n_cols_tiles, hipStream_t stream) {
-  if (grid_x <= 0 || n_cols_tiles <= 0) return hipSuccess;
-  const dim3 grid(grid_x, n_cols_tiles), block(WM * WN * 64);
+template <class C, int MODE>
+hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream) {
+  const int n_tiles = (MODE == MODE_GATE_UP) ? (n_cols + C::BN / 2 - 1) / (C::BN / 2)
+                                             : (n_cols + C::BN - 1) / C::BN;
+  if (m_tiles <= 0 || n_tiles <= 0) return hipSuccess;
+  a.n_tiles = n_tiles;
+  const int64_t total = (int64_t)m_tiles * n_tiles;
+  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(C::WM * C::WN * 64);
   if constexpr (MODE == MODE_GATE_UP)
-    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<BM, BN, WM, WN, KT, ST, NBM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST>), grid, block, 0, stream, a);
   else if constexpr (MODE == MODE_DOWN)
-    hipLaunchKernelGGL((moe_down_weighted_kernel<BM, BN, WM, WN, KT, ST, NBM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((linear_kernel<BM, BN, WM, WN, KT, ST, NBM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 bool use_prefill_tiles(int T, int k, int E) { return (int64_t)T * k >= 48LL * E; }
+
+GemmKArgs gate_up_args(const MoeGemmArgs& m) {
+  // A = x rows gathered through perm / k, B = W_gu[e] (2F rows), out = h [P][F]
+  GemmKArgs g{};
+  g.A = m.x;
+  g.a_rows = m.T;
+  g.a_gather = m.perm;
+  g.a_div = m.k;
+  g.Bp = m.gu_packed;
+  g.Bs = m.gu_scales;
+  g.b_rows_per_expert = 2LL * m.F;
+  g.N = m.F;
+  g.K = m.H;
+  g.tiles = m.tiles;
+  g.num_tiles = m.num_tiles;
+  g.offsets = m.offsets;
+  g.F = m.F;
+  g.out = m.h;
+  return g;
+}
+
+GemmKArgs down_args(const MoeGemmArgs& m) {
+  // A = h rows (permuted order), B = W_dn[e] (H rows), out = Y[pair] * routing weight
+  GemmKArgs d{};
+  d.A = m.h;
+  d.a_rows = (int64_t)m.T * m.k;
+  d.a_gather = nullptr;
+  d.a_div = 1;
+  d.Bp = m.dn_packed;
+  d.Bs = m.dn_scales;
+  d.b_rows_per_expert = m.H;
+  d.N = m.H;
+  d.K = m.F;
+  d.tiles = m.tiles;
+  d.num_tiles = m.num_tiles;
+  d.offsets = m.offsets;
+  d.F = m.F;
+  d.out = m.y;
+  d.perm = m.perm;
+  d.rw = m.topk_w;
+  return d;
+}
 
 }  // namespace
 
@@ -362,49 +469,15 @@ int moe_max_tiles(int T, int k, int E, int tile_rows) {
 }
 
 hipError_t launch_moe_gate_up(const MoeGemmArgs& m, hipStream_t stream) {
-  // A = x rows gathered through perm / k, B = W_gu[e] (2F rows), out = h [P][F]
-  GemmKArgs g{};
-  g.A = m.x;
-  g.a_gather = m.perm;
-  g.a_div = m.k;
-  g.Bp = m.gu_packed;
-  g.Bs = m.gu_scales;
-  g.b_rows_per_expert = 2LL * m.F;
-  g.bs_total = (int64_t)m.E * 2 * m.F * (m.H / 32);
-  g.N = m.F;
-  g.K = m.H;
-  g.tiles = m.tiles;
-  g.num_tiles = m.num_tiles;
-  g.offsets = m.offsets;
-  g.F = m.F;
-  g.out = m.h;
-  if (use_prefill_tiles(m.T, m.k, m.E))
-    return launch_gemm<128, 128, 2, 2, 4, 3, MODE_GATE_UP, kNBMax>(g, m.max_tiles, (m.F + 63) / 64, stream);
-  return launch_gemm<16, 64, 1, 2, 8, 4, MODE_GATE_UP, kNBMax>(g, m.max_tiles, (m.F + 31) / 32, stream);
+  const GemmKArgs g = gate_up_args(m);
+  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPre, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
+  return launch_gemm<CfgDecGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
 }
 
 hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
-  // A = h rows (permuted order), B = W_dn[e] (H rows), out = Y[pair] * routing weight
-  GemmKArgs d{};
-  d.A = m.h;
-  d.a_gather = nullptr;
-  d.a_div = 1;
-  d.Bp = m.dn_packed;
-  d.Bs = m.dn_scales;
-  d.b_rows_per_expert = m.H;
-  d.bs_total = (int64_t)m.E * m.H * (m.F / 32);
-  d.N = m.H;
-  d.K = m.F;
-  d.tiles = m.tiles;
-  d.num_tiles = m.num_tiles;
-  d.offsets = m.offsets;
-  d.F = m.F;
-  d.out = m.y;
-  d.perm = m.perm;
-  d.rw = m.topk_w;
-  if (use_prefill_tiles(m.T, m.k, m.E))
-    return launch_gemm<128, 128, 2, 2, 4, 3, MODE_DOWN, kNBMax>(d, m.max_tiles, (m.H + 127) / 128, stream);
-  return launch_gemm<16, 64, 1, 4, 8, 4, MODE_DOWN, kNBMax>(d, m.max_tiles, (m.H + 63) / 64, stream);
+  const GemmKArgs d = down_args(m);
+  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPre, MODE_DOWN>(d, m.max_tiles, m.H, stream);
+  return launch_gemm<CfgDecDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
 }
 
 hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {
@@ -423,23 +496,19 @@ hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
                          const uint8_t* scales, int N, void* y, bool y_bf16, hipStream_t stream) {
   GemmKArgs g{};
   g.A = x;
+  g.a_rows = M;
   g.a_div = 1;
   g.Bp = packed;
   g.Bs = scales;
   g.b_rows_per_expert = N;
-  g.bs_total = (int64_t)N * (K / 32);
   g.N = N;
   g.K = K;
   g.M = M;
   g.F = N;
   g.out = y;
   g.out_bf16 = y_bf16 ? 1 : 0;
-  const int nb = K / 32;
-  if (M > 64 && nb <= kNBMax)
-    return launch_gemm<128, 128, 2, 2, 4, 3, MODE_LINEAR, kNBMax>(g, (M + 127) / 128, (N + 127) / 128, stream);
-  if (nb <= kNBMax)
-    return launch_gemm<16, 64, 1, 4, 8, 4, MODE_LINEAR, kNBMax>(g, (M + 15) / 16, (N + 63) / 64, stream);
-  return launch_gemm<16, 64, 1, 4, 8, 3, MODE_LINEAR, kNBMaxLarge>(g, (M + 15) / 16, (N + 63) / 64, stream);
+  if (M > 64) return launch_gemm<CfgPre, MODE_LINEAR>(g, (M + CfgPre::BM - 1) / CfgPre::BM, N, stream);
+  return launch_gemm<CfgDecDn, MODE_LINEAR>(g, (M + CfgDecDn::BM - 1) / CfgDecDn::BM, N, stream);
 }
 
 hipError_t gemm_init() { return hipSuccess; }

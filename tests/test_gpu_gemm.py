@@ -112,7 +112,8 @@ def test_moe_bad_routing_index_is_flagged():
     idx[2, 1] = 7
     gp, gs, dp, ds = moe_weights_dev(seed, E, H, F)
     out = torch.empty((T, H), dtype=torch.float32, device=DEV)
-    d = mx.make_moe_desc(to_dev(x), gp, gs, dp, ds, k, out, topk_idx=to_dev(idx), topk_w=to_dev(w))
+    xd, idxd, wd = to_dev(x), to_dev(idx), to_dev(w)  # held until the call has completed
+    d = mx.make_moe_desc(xd, gp, gs, dp, ds, k, out, topk_idx=idxd, topk_w=wd)
     ws = torch.empty(mx.mxfp4_moe_mlp_workspace(d), dtype=torch.uint8, device=DEV)
     mx._check(mx.lib().mxfp4_moe_mlp(mx.ctypes.byref(d), ws.data_ptr(), ws.numel(),
                                      mx._stream(None)))
