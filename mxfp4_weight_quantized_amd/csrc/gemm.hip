@@ -101,10 +101,7 @@ __device__ __forceinline__ float e8m0_scale(uint32_t b) {
 // Per stage a workgroup moves: A chunks and B chunks straight into LDS (direct loads), and the
 // stage's BN x KT scale bytes into registers; the scale bytes go to LDS (as fp32 scales) one
 // iteration later, when they have arrived, so no wait is ever placed on the newest stage.
-// Tiles are numbered m-fastest and handed out in contiguous ranges per XCD (workgroups are
-// dispatched round-robin over the 8 XCDs, each with its own L2), so consecutive workgroups of
-// one XCD share the weight tile of one expert's column block.
-template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE>
+template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM>
 __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
@@ -117,29 +114,35 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int IA = A_STAGE / 1024 / NW;
   constexpr int IB = B_STAGE / 1024 / NW;
   constexpr int SS = KT / 4;                       // super-steps per stage
-  constexpr int NSB = (BN * KT + NT - 1) / NT;     // scale-byte loads per thread per stage
-  constexpr int LPS = NSB + IA + IB;               // vector-memory ops per wave per stage
+  constexpr int IS = BN * KT / 64 / NW;            // scale-byte DMA loads per wave per stage
+  constexpr int LPS = IS + IA + IB;                // vector-memory ops per wave per stage
   static_assert(IA * NW * 1024 == A_STAGE && IB * NW * 1024 == B_STAGE, "stage split");
+  static_assert(IS * NW * 64 == BN * KT, "scale split");
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "wave tile");
   static_assert(!SWIGLU || FN % 2 == 0, "gate/up fragment pairs");
-  static_assert(KT % 4 == 0 && A_ROW >= 256 && STAGES == 3, "pipeline");
+  static_assert(KT % 4 == 0 && A_ROW >= 256 && (STAGES == 2 || STAGES == 3), "pipeline");
   static_assert(2 * LPS < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t sA[STAGES][A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB[STAGES][B_STAGE];
-  __shared__ float sSc[STAGES][BN * KT];
+  __shared__ uint32_t sSc[STAGES][BN * KT];   // one E8M0 byte per dword (direct byte loads)
   __shared__ int sArow[BM];
 
-  // ---- which tile (XCD-contiguous, m-fastest) ----
+  // ---- which tile ----
+  // Workgroups go round-robin to the 8 XCDs (each with its own L2). XCD x takes super-tiles
+  // x, x+8, ...; a super-tile is GM x GN (m, n) tiles, and its GM*GN workgroups run together on
+  // the XCD, so at every K stage they share GM activation tiles and GN weight tiles in L2.
+  constexpr int GN = 32 / GM;
   const bool grouped = p.tiles != nullptr;
   const int num_mt = grouped ? *p.num_tiles : (p.M + BM - 1) / BM;
-  const int total = num_mt * p.n_tiles;
-  const int per_xcd = (total + 7) >> 3;
+  const int sm_count = (num_mt + GM - 1) / GM, sn_count = (p.n_tiles + GN - 1) / GN;
   const int slot = blockIdx.x >> 3;
-  if (slot >= per_xcd) return;
-  const int t = (blockIdx.x & 7) * per_xcd + slot;
-  if (t >= total) return;
-  const int mt = t % num_mt, nt = t / num_mt;
+  const int super_tile = (blockIdx.x & 7) + 8 * (slot / (GM * GN));
+  if (super_tile >= sm_count * sn_count) return;
+  const int pos = slot % (GM * GN);
+  const int mt = (super_tile % sm_count) * GM + pos / GN;
+  const int nt = (super_tile / sm_count) * GN + pos % GN;
+  if (mt >= num_mt || nt >= p.n_tiles) return;
   int e, r0, row_end;
   if (grouped) {
     const int2 tl = p.tiles[mt];
@@ -179,12 +182,13 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     bblk[q] = chunk;
     voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
   }
-  // scale bytes this thread fetches per stage: (row, block) = idx / KT, idx % KT
-  uint32_t voffS[NSB];
-  int sblk[NSB];
+  // scale bytes per stage: dword idx of the stage's scale area holds (row, block) =
+  // (idx / KT, idx % KT); wave w's load q covers idx = (w * IS + q) * 64 + lane
+  uint32_t voffS[IS];
+  int sblk[IS];
 #pragma unroll
-  for (int q = 0; q < NSB; ++q) {
-    const int idx = min(tid + q * NT, BN * KT - 1);
+  for (int q = 0; q < IS; ++q) {
+    const int idx = (wave * IS + q) * 64 + lane;
     sblk[q] = idx % KT;
     voffS[q] = (uint32_t)weight_row(idx / KT) * (uint32_t)nb + sblk[q];
   }
@@ -216,17 +220,18 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
   }
 
-  // Issue one stage: scale bytes into `sbytes`, then A and B chunks into LDS. Every wave issues
-  // exactly LPS vector-memory ops. Full stages add the K offset as a scalar; the stage that
-  // holds the end of K moves it into the lane offsets and sends blocks past K out of range.
-  uint32_t sbytes[NSB];
+  // Issue one stage: the stage's scale bytes, A chunks and B chunks, all straight into LDS.
+  // Every wave issues exactly LPS vector-memory ops. Full stages add the K offset as a scalar;
+  // the stage that holds the end of K moves it into the lane offsets and sends blocks past K out
+  // of range (they read as zeros).
   auto issue = [&](int kt, int st) {
     const bool full = (kt + 1) * KT <= nb;
     const int kb = kt * KT;
 #pragma unroll
-    for (int q = 0; q < NSB; ++q) {
+    for (int q = 0; q < IS; ++q) {
       const uint32_t vo = full ? voffS[q] : (kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange);
-      sbytes[q] = __builtin_amdgcn_raw_buffer_load_b8(rS, vo, full ? kb : 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)&sSc[st][(wave * IS + q) * 64], 1,
+                                               vo, full ? kb : 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < IA; ++q) {
@@ -241,13 +246,6 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
                                                vo, full ? kb * 16 : 0, 0, 0);
     }
   };
-  auto store_scales = [&](int st) {
-#pragma unroll
-    for (int q = 0; q < NSB; ++q) {
-      const int idx = tid + q * NT;
-      if (idx < BN * KT) sSc[st][idx] = e8m0_scale(sbytes[q] & 0xffu);
-    }
-  };
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -255,12 +253,13 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One stage of MFMAs: per super-step, load the wave's A fragments, then per B fragment decode
-  // the lane's 16-byte block (two codes per cvt) and run its 4 x FM MFMAs.
+  // One stage of MFMAs. Per super-step: read the wave's A fragments and its packed B blocks, then
+  // walk the B fragments, decoding fragment f+1 (two codes per cvt, into the other register set)
+  // while the 4 x FM MFMAs of fragment f run, so the MFMA pipe never waits on the conversions.
   auto compute = [&](int st) {
     const uint8_t* As = sA[st];
     const uint8_t* Bsm = sB[st];
-    const float* Sc = sSc[st];
+    const uint32_t* Sc = sSc[st];
 #pragma unroll
     for (int j = 0; j < SS; ++j) {
       bf16x8 a[FM][4];
@@ -272,40 +271,49 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
           a[i][s] = u32x4_as_bf16x8(
               lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ swz_a(r)) << 4)));
       }
+      u32x4 w[FN];
+      uint32_t scb[FN];
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
         const int r = brow[f];
-        const u32x4 w = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-        const float sc = Sc[r * KT + 4 * j + g];
+        w[f] = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
+        scb[f] = Sc[r * KT + 4 * j + g];
+      }
+      // all LDS reads of the super-step are in flight before any math starts
+      __builtin_amdgcn_sched_barrier(0);
+      float sc[FN];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 b = fp4x8_to_bf16x8(w[s], sc);
+      for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f] & 0xffu);
+      bf16x8 b[2][4];
 #pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b, acc[i][f]);
+      for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        if (f + 1 < FN) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s) b[(f + 1) & 1][s] = fp4x8_to_bf16x8(w[f + 1][s], sc[f + 1]);
         }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
       }
     }
   };
 
-  // Pipeline (3 stages). Issue order: group g = [scale bytes of stage g][A, B chunks of stage g];
-  // group kt+2 is issued in iteration kt. At iteration kt stage kt must have landed, and the
-  // scale bytes of stage kt+1 too (they are stored to LDS now, from the one register set that
-  // always holds the newest group's bytes); the chunks of stage kt+1 may still be in flight.
+  // Pipeline: stage kt+STAGES-1 is issued in iteration kt. At iteration kt the loads of stage kt
+  // must have landed; with 3 stages those of stage kt+1 may still be in flight.
   const int ntk = (nb + KT - 1) / KT;
   issue(0, 0);
-  wait_vmcnt<0>();
-  store_scales(0);
-  if (ntk > 1) issue(1, 1);
+  if (STAGES == 3 && ntk > 1) issue(1, 1);
   int st = 0;
   for (int kt = 0; kt < ntk; ++kt) {
-    const bool next = kt + 1 < ntk;
-    if (next) wait_vmcnt<IA + IB>();
+    if (STAGES == 3 && kt + 1 < ntk) wait_vmcnt<LPS>();
     else wait_vmcnt<0>();
     barrier_lds();
-    if (next) store_scales(st == 2 ? 0 : st + 1);
-    if (kt + 2 < ntk) issue(kt + 2, st == 0 ? 2 : st - 1);
+    if (kt + STAGES - 1 < ntk) issue(kt + STAGES - 1, st == 0 ? STAGES - 1 : st - 1);
     compute(st);
-    st = (st == 2) ? 0 : st + 1;
+    st = (st == STAGES - 1) ? 0 : st + 1;
   }
 
   // ---- epilogue ----
@@ -351,17 +359,17 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 }
 
 // One kernel name per role, so profiles show which product a launch is.
-template <int BM, int BN, int WM, int WN, int KT, int ST>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM>
 __global__ __launch_bounds__(WM * WN * 64) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM>
 __global__ __launch_bounds__(WM * WN * 64) void moe_down_weighted_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM>
 __global__ __launch_bounds__(WM * WN * 64) void linear_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM>(p);
 }
 
 // out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
@@ -391,13 +399,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // ---- tile configurations ----
-// Prefill-shaped (many rows per expert): 128 x 256 workgroup tiles, eight waves of 64 x 64 (two
-// waves per SIMD, so one wave's LDS reads and dequantization overlap the other's MFMAs).
+// Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles with a 2-stage pipeline, so
+// two workgroups fit in a CU's LDS and one's tile prologue / epilogue overlaps the other's MFMAs.
+// gate_up: four waves of 64 x 64; down: eight waves of 32 x 64 (measured best for each).
 // Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, weight
 // streaming dominates.
-struct CfgPre { static constexpr int BM = 128, BN = 256, WM = 2, WN = 4, KT = 4, ST = 3; };
-struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3; };
-struct CfgDecDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3; };
+struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4; };
+struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 2, WN = 4, KT = 4, ST = 2, GM = 4; };
+struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1; };
+struct CfgDecDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1; };
+constexpr int kPrefillRows = 64;
+static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
 
 template <class C, int MODE>
 hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream) {
@@ -405,14 +417,16 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
                                              : (n_cols + C::BN - 1) / C::BN;
   if (m_tiles <= 0 || n_tiles <= 0) return hipSuccess;
   a.n_tiles = n_tiles;
-  const int64_t total = (int64_t)m_tiles * n_tiles;
-  const dim3 grid((unsigned)((total + 7) / 8 * 8)), block(C::WM * C::WN * 64);
+  // grid: 8 XCDs x (super-tiles per XCD) x (tiles per super-tile), from the row-tile bound
+  constexpr int GN = 32 / C::GM;
+  const int64_t supers = (int64_t)((m_tiles + C::GM - 1) / C::GM) * ((n_tiles + GN - 1) / GN);
+  const dim3 grid((unsigned)(8 * 32 * ((supers + 7) / 8))), block(C::WM * C::WN * 64);
   if constexpr (MODE == MODE_GATE_UP)
-    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM>), grid, block, 0, stream, a);
   else if constexpr (MODE == MODE_DOWN)
-    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -462,7 +476,7 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
 
 }  // namespace
 
-int moe_tile_rows(int T, int k, int E) { return use_prefill_tiles(T, k, E) ? 128 : 16; }
+int moe_tile_rows(int T, int k, int E) { return use_prefill_tiles(T, k, E) ? kPrefillRows : 16; }
 
 int moe_max_tiles(int T, int k, int E, int tile_rows) {
   return (int)(((int64_t)T * k + tile_rows - 1) / tile_rows) + E;
@@ -470,13 +484,13 @@ int moe_max_tiles(int T, int k, int E, int tile_rows) {
 
 hipError_t launch_moe_gate_up(const MoeGemmArgs& m, hipStream_t stream) {
   const GemmKArgs g = gate_up_args(m);
-  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPre, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
+  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPreGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
   return launch_gemm<CfgDecGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
 }
 
 hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
   const GemmKArgs d = down_args(m);
-  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPre, MODE_DOWN>(d, m.max_tiles, m.H, stream);
+  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPreDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
   return launch_gemm<CfgDecDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
 }
 
@@ -507,7 +521,7 @@ hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
   g.F = N;
   g.out = y;
   g.out_bf16 = y_bf16 ? 1 : 0;
-  if (M > 64) return launch_gemm<CfgPre, MODE_LINEAR>(g, (M + CfgPre::BM - 1) / CfgPre::BM, N, stream);
+  if (M > 64) return launch_gemm<CfgPreGU, MODE_LINEAR>(g, (M + CfgPreGU::BM - 1) / CfgPreGU::BM, N, stream);
   return launch_gemm<CfgDecDn, MODE_LINEAR>(g, (M + CfgDecDn::BM - 1) / CfgDecDn::BM, N, stream);
 }
 
