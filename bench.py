@@ -46,6 +46,8 @@ def workloads():
     for T in (1, 256, 4096):
         s = inputs.MOE_120B[T]
         w["moe-120b-mxact-T%d" % T] = ("moe", s, 1)
+    w[inputs.MOE_20B_PREFILL.name + "-mxact"] = ("moe", inputs.MOE_20B_PREFILL, 1)
+    w[inputs.MOE_20B_DECODE.name + "-mxact"] = ("moe", inputs.MOE_20B_DECODE, 1)
     for M in (1, 8, 32):
         w["linear-decode-M%d" % M] = ("linear", dict(M=M, K=2880, N=5760, seed=1), 0)
     return w
@@ -119,8 +121,8 @@ def kernel_work(name, T, H, F, E, k, touched, P, out_bytes, mxact):
         return 2.0 * T * E * H, T * H * 2 + E * H * 2 + T * E * 4 + T * k * 8
     if name == "permute":
         return 0.0, T * k * 4 * 4 + (E + 1) * 4
-    if name == "quantize":
-        return 0.0, (T + P) * H * (2 + wb)
+    if name == "quantize":   # activation variant: x along H and h along F, two launches
+        return 0.0, (T * H + P * F) * (2 + wb) / 2
     return 0.0, 0.0
 
 
@@ -248,11 +250,12 @@ def bench_moe(args, name, shape, flags):
         "roofline": roof,
     }
     if want_cpu:
-        result["cpu_baseline"] = cpu_baseline_moe(args, s, x_all[:s.T], wr_np, br_np, host_w)
+        result["cpu_baseline"] = cpu_baseline_moe(args, s, x_all[:s.T], wr_np, br_np, host_w,
+                                                  bool(flags))
     return result
 
 
-def cpu_baseline_moe(args, s, x_np, wr_np, br_np, host_w):
+def cpu_baseline_moe(args, s, x_np, wr_np, br_np, host_w, mx_act=False):
     """The oracle (router + top-k + MoE MLP) on the first tokens of the same batch, in chunks,
     until about args.cpu_seconds of wall time have passed."""
     import numpy as np
@@ -265,13 +268,14 @@ def cpu_baseline_moe(args, s, x_np, wr_np, br_np, host_w):
         xc = np.ascontiguousarray(x_np[done:done + n])
         lg = oracle.router_logits(xc, wr_np, br_np)
         idx, w = oracle.topk_softmax(lg, s.k)
-        oracle.moe_mlp(xc, idx, w, *host_w, E=s.E)
+        oracle.moe_mlp(xc, idx, w, *host_w, E=s.E, mx_act=mx_act)
         done += n
     el = time.perf_counter() - t0
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "first %d of the %d tokens: router, top-%d softmax and MoE MLP in the fp64 "
-                      "C oracle, %.1f s wall" % (done, s.T, s.k, el)}
+            "sample": "first %d of the %d tokens: router, top-%d softmax and MoE MLP%s in the fp64 "
+                      "C oracle, %.1f s wall" % (done, s.T, s.k,
+                                                 " (activation variant)" if mx_act else "", el)}
 
 
 def bench_linear(args, name, cfg):

@@ -254,7 +254,6 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   const MoeLayout L = moe_layout(d);
   if (ws == nullptr || ws_bytes < L.total) return fail(MX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, ws_bytes);
   if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if (d.flags & MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "MX_ACT_MXFP4 is not available in this build");
   st = check_device();
   if (st != MX_OK) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -287,8 +286,21 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
     e = mx::launch_permute(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows, tiles, status + 1, s);
   }
   if (e != hipSuccess) return hip_fail(e, "permute launch");
+  const bool mx_act = (d.flags & MX_ACT_MXFP4) != 0;
+  if (mx_act) {
+    // activation variant: x quantized along H in 32-blocks (the same rule as the weights)
+    ProfScope ps(PK_QUANTIZE, s);
+    e = mx::launch_quantize(d.x, true, (int64_t)d.T * (d.H / 32), reinterpret_cast<uint8_t*>(w + L.xq),
+                            reinterpret_cast<uint8_t*>(w + L.xqs), s);
+    if (e != hipSuccess) return hip_fail(e, "x quantize launch");
+  }
   mx::MoeGemmArgs g{};
   g.T = d.T; g.H = d.H; g.F = d.F; g.E = d.E; g.k = d.k;
+  g.mx_act = mx_act;
+  g.xq = reinterpret_cast<uint8_t*>(w + L.xq);
+  g.xqs = reinterpret_cast<uint8_t*>(w + L.xqs);
+  g.hq = reinterpret_cast<uint8_t*>(w + L.hq);
+  g.hqs = reinterpret_cast<uint8_t*>(w + L.hqs);
   g.x = d.x;
   g.perm = perm;
   g.inv = inv;
@@ -308,6 +320,12 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
     e = mx::launch_moe_gate_up(g, s);
   }
   if (e != hipSuccess) return hip_fail(e, "gate_up launch");
+  if (mx_act) {
+    // the bf16 SwiGLU output h, quantized along F
+    ProfScope ps(PK_QUANTIZE, s);
+    e = mx::launch_quantize(g.h, true, (int64_t)d.T * d.k * (d.F / 32), g.hq, g.hqs, s);
+    if (e != hipSuccess) return hip_fail(e, "h quantize launch");
+  }
   {
     ProfScope ps(PK_DOWN, s);
     e = mx::launch_moe_down(g, s);
@@ -340,10 +358,23 @@ MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uin
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 16) || !aligned(y, 16)) return fail(MX_ERR_ALIGN, "x, packed, scales and y must be 16-byte aligned");
   if (flags & MX_ACT_MXFP4) {
     if (ws == nullptr || ws_bytes < mxfp4_linear_workspace(M, K, N, flags)) return fail(MX_ERR_WORKSPACE, "workspace too small");
-    return fail(MX_ERR_UNSUPPORTED, "MX_ACT_MXFP4 is not available in this build");
+    if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
   mx_status st = check_device();
   if (st != MX_OK) return st;
+  if (flags & MX_ACT_MXFP4) {
+    uint8_t* xq = static_cast<uint8_t*>(ws);
+    uint8_t* xqs = xq + align256((size_t)M * K / 2);
+    hipError_t e;
+    {
+      ProfScope ps(PK_QUANTIZE, (hipStream_t)stream);
+      e = mx::launch_quantize(x, true, (int64_t)M * (K / 32), xq, xqs, (hipStream_t)stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "x quantize launch");
+    ProfScope ps(PK_LINEAR, (hipStream_t)stream);
+    e = mx::launch_linear_mxact(xq, xqs, M, K, packed, scales, N, y, y_dtype == MX_BF16, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "linear launch");
+  }
   ProfScope ps(PK_LINEAR, (hipStream_t)stream);
   hipError_t e = mx::launch_linear(x, M, K, packed, scales, N, y, y_dtype == MX_BF16, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "linear launch");

@@ -31,6 +31,7 @@ enum { MODE_LINEAR = 0, MODE_GATE_UP = 1, MODE_DOWN = 2 };
 struct GemmKArgs {
   const uint16_t* A;          // bf16 activation rows of length K
   int64_t a_rows;             // rows in A (bounds the buffer view of A)
+  const uint8_t* Asc;         // A scales [a_rows][K/32] when A is MXFP4 (else unused)
   const int32_t* a_gather;    // A row of permuted row r = a_gather[r] / a_div (NULL: r)
   int a_div;
   const uint8_t* Bp;          // packed weights, expert-major
@@ -95,13 +96,26 @@ __device__ __forceinline__ float e8m0_scale(uint32_t b) {
   return __uint_as_float(u);
 }
 
-// Grouped / dense MXFP4 GEMM tile: out[BM rows x BN cols] of A (bf16) times the decoded weights.
+// 32-bit lane offsets of the direct loads of one LDS region. A region of `bytes` bytes is filled
+// by bytes/1024 wave-instructions of 64 x 16 bytes (or bytes/256 of 64 x 1 byte for scale
+// regions, one byte per dword); wave w issues instructions w*I .. w*I+I-1 (mod the count). When a
+// region is smaller than one instruction per wave, several waves load the same bytes to the same
+// place, which is harmless and keeps every wave's count of memory ops the same.
+template <int REGION_INSTRS, int NW>
+struct DmaPlan {
+  static constexpr int I = (REGION_INSTRS + NW - 1) / NW;  // instructions per wave
+  static __device__ __forceinline__ int instr(int wave, int q) { return (wave * I + q) % REGION_INSTRS; }
+};
+
+// Grouped / dense MXFP4 GEMM tile: out[BM rows x BN cols] = A times the weights (decoded).
 //   BM x BN workgroup tile, WM x WN waves, each wave a (BM/WM) x (BN/WN) tile of 16 x 16 MFMA
-//   fragments; KT 32-element blocks per pipeline stage; STAGES (3 or 4) stages in flight.
-// Per stage a workgroup moves: A chunks and B chunks straight into LDS (direct loads), and the
-// stage's BN x KT scale bytes into registers; the scale bytes go to LDS (as fp32 scales) one
-// iteration later, when they have arrived, so no wait is ever placed on the newest stage.
-template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM>
+//   fragments; KT 32-element blocks per pipeline stage; STAGES (2 or 3) stages in flight.
+//   AFP4 = false: A is bf16 and the weights are decoded to bf16 for v_mfma_f32_16x16x32_bf16.
+//   AFP4 = true:  A is MXFP4 too (packed codes + E8M0 scales, same layout as the weights) and
+//                 each 16 x 16 x 128 slice is one v_mfma_scale_f32_16x16x128_f8f6f4 with both
+//                 operands' block scales, so nothing is decoded.
+// Per stage a workgroup moves A chunks, B chunks and their scale bytes straight into LDS.
+template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4>
 __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
@@ -109,23 +123,26 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int FM = TM / 16, FN = TN / 16;
   constexpr bool SWIGLU = (MODE == MODE_GATE_UP);
   constexpr int BNH = BN / 2;
-  constexpr int A_ROW = KT * 64, B_ROW = KT * 16;
+  constexpr int A_ROW = AFP4 ? KT * 16 : KT * 64, B_ROW = KT * 16;
   constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * B_ROW;
-  constexpr int IA = A_STAGE / 1024 / NW;
-  constexpr int IB = B_STAGE / 1024 / NW;
-  constexpr int SS = KT / 4;                       // super-steps per stage
-  constexpr int IS = BN * KT / 64 / NW;            // scale-byte DMA loads per wave per stage
-  constexpr int LPS = IS + IA + IB;                // vector-memory ops per wave per stage
-  static_assert(IA * NW * 1024 == A_STAGE && IB * NW * 1024 == B_STAGE, "stage split");
-  static_assert(IS * NW * 64 == BN * KT, "scale split");
+  using PA = DmaPlan<A_STAGE / 1024, NW>;
+  using PB = DmaPlan<B_STAGE / 1024, NW>;
+  using PS = DmaPlan<BN * KT / 64, NW>;                    // weight scale bytes
+  using PSA = DmaPlan<AFP4 ? BM * KT / 64 : 1, NW>;         // activation scale bytes
+  constexpr int IA = PA::I, IB = PB::I, IS = PS::I, ISA = AFP4 ? PSA::I : 0;
+  constexpr int SS = KT / 4;                               // super-steps per stage
+  constexpr int LPS = IS + ISA + IA + IB;                  // vector-memory ops per wave per stage
+  static_assert(A_STAGE % 1024 == 0 && B_STAGE % 1024 == 0, "stage split");
+  static_assert((BN * KT) % 64 == 0 && (!AFP4 || (BM * KT) % 64 == 0), "scale split");
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "wave tile");
   static_assert(!SWIGLU || FN % 2 == 0, "gate/up fragment pairs");
-  static_assert(KT % 4 == 0 && A_ROW >= 256 && (STAGES == 2 || STAGES == 3), "pipeline");
+  static_assert(KT % 4 == 0 && (AFP4 || A_ROW >= 256) && (STAGES == 2 || STAGES == 3), "pipeline");
   static_assert(2 * LPS < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t sA[STAGES][A_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sB[STAGES][B_STAGE];
-  __shared__ uint32_t sSc[STAGES][BN * KT];   // one E8M0 byte per dword (direct byte loads)
+  __shared__ uint32_t sSc[STAGES][BN * KT];                 // one E8M0 byte per dword
+  __shared__ uint32_t sSa[AFP4 ? STAGES : 1][AFP4 ? BM * KT : 1];
   __shared__ int sArow[BM];
 
   // ---- which tile ----
@@ -171,24 +188,24 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   const int64_t rpe = p.b_rows_per_expert;
   const __amdgpu_buffer_rsrc_t rB = make_buf(p.Bp + (int64_t)e * rpe * (K >> 1), rpe * (K >> 1));
   const __amdgpu_buffer_rsrc_t rS = make_buf(p.Bs + (int64_t)e * rpe * nb, rpe * nb);
-  const __amdgpu_buffer_rsrc_t rA = make_buf(p.A, p.a_rows * K * 2);
+  const __amdgpu_buffer_rsrc_t rA = make_buf(p.A, p.a_rows * (AFP4 ? (K >> 1) : K * 2));
+  const __amdgpu_buffer_rsrc_t rSA = make_buf(p.Asc, AFP4 ? p.a_rows * nb : 0);
   uint32_t voffB[IB];
   int bblk[IB];
 #pragma unroll
   for (int q = 0; q < IB; ++q) {
-    const int off = (wave * IB + q) * 1024 + lane * 16;
+    const int off = PB::instr(wave, q) * 1024 + lane * 16;
     const int lrow = off / B_ROW;
     const int chunk = ((off % B_ROW) >> 4) ^ swz_b<KT>(lrow);
     bblk[q] = chunk;
     voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
   }
-  // scale bytes per stage: dword idx of the stage's scale area holds (row, block) =
-  // (idx / KT, idx % KT); wave w's load q covers idx = (w * IS + q) * 64 + lane
+  // scale dword idx of a stage's scale area holds (row, block) = (idx / KT, idx % KT)
   uint32_t voffS[IS];
   int sblk[IS];
 #pragma unroll
   for (int q = 0; q < IS; ++q) {
-    const int idx = (wave * IS + q) * 64 + lane;
+    const int idx = PS::instr(wave, q) * 64 + lane;
     sblk[q] = idx % KT;
     voffS[q] = (uint32_t)weight_row(idx / KT) * (uint32_t)nb + sblk[q];
   }
@@ -213,36 +230,56 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   int ablk[IA];
 #pragma unroll
   for (int q = 0; q < IA; ++q) {
-    const int off = (wave * IA + q) * 1024 + lane * 16;
+    const int off = PA::instr(wave, q) * 1024 + lane * 16;
     const int lrow = off / A_ROW;
-    const int chunk = ((off % A_ROW) >> 4) ^ swz_a(lrow);
-    ablk[q] = chunk >> 2;
-    voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
+    if constexpr (AFP4) {
+      const int chunk = ((off % A_ROW) >> 4) ^ swz_b<KT>(lrow);
+      ablk[q] = chunk;
+      voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K >> 1) + chunk * 16;
+    } else {
+      const int chunk = ((off % A_ROW) >> 4) ^ swz_a(lrow);
+      ablk[q] = chunk >> 2;
+      voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
+    }
+  }
+  uint32_t voffSA[ISA > 0 ? ISA : 1];
+  int sablk[ISA > 0 ? ISA : 1];
+#pragma unroll
+  for (int q = 0; q < ISA; ++q) {
+    const int idx = PSA::instr(wave, q) * 64 + lane;
+    sablk[q] = idx % KT;
+    voffSA[q] = (uint32_t)sArow[idx / KT] * (uint32_t)nb + sablk[q];
   }
 
-  // Issue one stage: the stage's scale bytes, A chunks and B chunks, all straight into LDS.
-  // Every wave issues exactly LPS vector-memory ops. Full stages add the K offset as a scalar;
-  // the stage that holds the end of K moves it into the lane offsets and sends blocks past K out
-  // of range (they read as zeros).
+  // Issue one stage: scale bytes, A chunks and B chunks, all straight into LDS. Every wave issues
+  // exactly LPS vector-memory ops. Full stages add the K offset as a scalar; the stage that holds
+  // the end of K moves it into the lane offsets and sends blocks past K out of range (zeros).
   auto issue = [&](int kt, int st) {
     const bool full = (kt + 1) * KT <= nb;
     const int kb = kt * KT;
 #pragma unroll
     for (int q = 0; q < IS; ++q) {
       const uint32_t vo = full ? voffS[q] : (kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)&sSc[st][(wave * IS + q) * 64], 1,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)&sSc[st][PS::instr(wave, q) * 64], 1,
                                                vo, full ? kb : 0, 0, 0);
     }
 #pragma unroll
+    for (int q = 0; q < ISA; ++q) {
+      const uint32_t vo = full ? voffSA[q] : (kb + sablk[q] < nb ? voffSA[q] + kb : kOutOfRange);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)&sSa[st][PSA::instr(wave, q) * 64], 1,
+                                               vo, full ? kb : 0, 0, 0);
+    }
+    constexpr int A_KB = AFP4 ? 16 : 64;  // bytes of A per 32-element block
+#pragma unroll
     for (int q = 0; q < IA; ++q) {
-      const uint32_t vo = full ? voffA[q] : (kb + ablk[q] < nb ? voffA[q] + kb * 64 : kOutOfRange);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)&sA[st][(wave * IA + q) * 1024], 16,
-                                               vo, full ? kb * 64 : 0, 0, 0);
+      const uint32_t vo = full ? voffA[q] : (kb + ablk[q] < nb ? voffA[q] + kb * A_KB : kOutOfRange);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)&sA[st][PA::instr(wave, q) * 1024], 16,
+                                               vo, full ? kb * A_KB : 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < IB; ++q) {
       const uint32_t vo = full ? voffB[q] : (kb + bblk[q] < nb ? voffB[q] + kb * 16 : kOutOfRange);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)&sB[st][(wave * IB + q) * 1024], 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)&sB[st][PB::instr(wave, q) * 1024], 16,
                                                vo, full ? kb * 16 : 0, 0, 0);
     }
   };
@@ -253,24 +290,16 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One stage of MFMAs. Per super-step: read the wave's A fragments and its packed B blocks, then
-  // walk the B fragments, decoding fragment f+1 (two codes per cvt, into the other register set)
-  // while the 4 x FM MFMAs of fragment f run, so the MFMA pipe never waits on the conversions.
+  // One stage of MFMAs.
+  //   bf16 A: per super-step, read the wave's A fragments and packed B blocks; decode B fragment
+  //   f+1 (two codes per cvt, other register set) while the 4 x FM MFMAs of fragment f run.
+  //   FP4 A: per super-step and fragment pair, one scaled MFMA on the raw blocks and scale bytes.
   auto compute = [&](int st) {
     const uint8_t* As = sA[st];
     const uint8_t* Bsm = sB[st];
     const uint32_t* Sc = sSc[st];
 #pragma unroll
     for (int j = 0; j < SS; ++j) {
-      bf16x8 a[FM][4];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * TM + i * 16 + ln;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          a[i][s] = u32x4_as_bf16x8(
-              lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ swz_a(r)) << 4)));
-      }
       u32x4 w[FN];
       uint32_t scb[FN];
 #pragma unroll
@@ -279,24 +308,47 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
         w[f] = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
         scb[f] = Sc[r * KT + 4 * j + g];
       }
-      // all LDS reads of the super-step are in flight before any math starts
-      __builtin_amdgcn_sched_barrier(0);
-      float sc[FN];
+      if constexpr (AFP4) {
+        u32x4 a[FM];
+        uint32_t sca[FM];
 #pragma unroll
-      for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f] & 0xffu);
-      bf16x8 b[2][4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        if (f + 1 < FN) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) b[(f + 1) & 1][s] = fp4x8_to_bf16x8(w[f + 1][s], sc[f + 1]);
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * TM + i * 16 + ln;
+          a[i] = lds_read_b128(As + r * A_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
+          sca[i] = sSa[st][r * KT + 4 * j + g];
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int f = 0; f < FN; ++f)
 #pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
+          for (int i = 0; i < FM; ++i)
+            acc[i][f] = mfma_fp4_16x16x128(a[i], w[f], sca[i], scb[f], acc[i][f]);
+      } else {
+        bf16x8 a[FM][4];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * TM + i * 16 + ln;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            a[i][s] = u32x4_as_bf16x8(
+                lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ swz_a(r)) << 4)));
+        }
+        float sc[FN];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f] & 0xffu);
+        bf16x8 b[2][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          if (f + 1 < FN) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) b[(f + 1) & 1][s] = fp4x8_to_bf16x8(w[f + 1][s], sc[f + 1]);
+          }
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
+        }
       }
     }
   };
@@ -359,17 +411,17 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 }
 
 // One kernel name per role, so profiles show which product a launch is.
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, bool AFP4>
 __global__ __launch_bounds__(WM * WN * 64) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, bool AFP4>
 __global__ __launch_bounds__(WM * WN * 64) void moe_down_weighted_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, bool AFP4>
 __global__ __launch_bounds__(WM * WN * 64) void linear_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4>(p);
 }
 
 // out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
@@ -411,7 +463,7 @@ struct CfgDecDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4,
 constexpr int kPrefillRows = 64;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
 
-template <class C, int MODE>
+template <class C, int MODE, bool AFP4 = false>
 hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream) {
   const int n_tiles = (MODE == MODE_GATE_UP) ? (n_cols + C::BN / 2 - 1) / (C::BN / 2)
                                              : (n_cols + C::BN - 1) / C::BN;
@@ -422,11 +474,11 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
   const int64_t supers = (int64_t)((m_tiles + C::GM - 1) / C::GM) * ((n_tiles + GN - 1) / GN);
   const dim3 grid((unsigned)(8 * 32 * ((supers + 7) / 8))), block(C::WM * C::WN * 64);
   if constexpr (MODE == MODE_GATE_UP)
-    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, AFP4>), grid, block, 0, stream, a);
   else if constexpr (MODE == MODE_DOWN)
-    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, AFP4>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, AFP4>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -483,14 +535,28 @@ int moe_max_tiles(int T, int k, int E, int tile_rows) {
 }
 
 hipError_t launch_moe_gate_up(const MoeGemmArgs& m, hipStream_t stream) {
-  const GemmKArgs g = gate_up_args(m);
-  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPreGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
+  GemmKArgs g = gate_up_args(m);
+  const bool pre = use_prefill_tiles(m.T, m.k, m.E);
+  if (m.mx_act) {
+    g.A = reinterpret_cast<const uint16_t*>(m.xq);  // packed codes, addressed in bytes
+    g.Asc = m.xqs;
+    if (pre) return launch_gemm<CfgPreGU, MODE_GATE_UP, true>(g, m.max_tiles, m.F, stream);
+    return launch_gemm<CfgDecGU, MODE_GATE_UP, true>(g, m.max_tiles, m.F, stream);
+  }
+  if (pre) return launch_gemm<CfgPreGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
   return launch_gemm<CfgDecGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
 }
 
 hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
-  const GemmKArgs d = down_args(m);
-  if (use_prefill_tiles(m.T, m.k, m.E)) return launch_gemm<CfgPreDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
+  GemmKArgs d = down_args(m);
+  const bool pre = use_prefill_tiles(m.T, m.k, m.E);
+  if (m.mx_act) {
+    d.A = reinterpret_cast<const uint16_t*>(m.hq);
+    d.Asc = m.hqs;
+    if (pre) return launch_gemm<CfgPreDn, MODE_DOWN, true>(d, m.max_tiles, m.H, stream);
+    return launch_gemm<CfgDecDn, MODE_DOWN, true>(d, m.max_tiles, m.H, stream);
+  }
+  if (pre) return launch_gemm<CfgPreDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
   return launch_gemm<CfgDecDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
 }
 
@@ -523,6 +589,27 @@ hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
   g.out_bf16 = y_bf16 ? 1 : 0;
   if (M > 64) return launch_gemm<CfgPreGU, MODE_LINEAR>(g, (M + CfgPreGU::BM - 1) / CfgPreGU::BM, N, stream);
   return launch_gemm<CfgDecDn, MODE_LINEAR>(g, (M + CfgDecDn::BM - 1) / CfgDecDn::BM, N, stream);
+}
+
+hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int K,
+                               const uint8_t* packed, const uint8_t* scales, int N, void* y,
+                               bool y_bf16, hipStream_t stream) {
+  GemmKArgs g{};
+  g.A = reinterpret_cast<const uint16_t*>(xq);
+  g.Asc = xqs;
+  g.a_rows = M;
+  g.a_div = 1;
+  g.Bp = packed;
+  g.Bs = scales;
+  g.b_rows_per_expert = N;
+  g.N = N;
+  g.K = K;
+  g.M = M;
+  g.F = N;
+  g.out = y;
+  g.out_bf16 = y_bf16 ? 1 : 0;
+  if (M > 64) return launch_gemm<CfgPreGU, MODE_LINEAR, true>(g, (M + CfgPreGU::BM - 1) / CfgPreGU::BM, N, stream);
+  return launch_gemm<CfgDecDn, MODE_LINEAR, true>(g, (M + CfgDecDn::BM - 1) / CfgDecDn::BM, N, stream);
 }
 
 hipError_t gemm_init() { return hipSuccess; }

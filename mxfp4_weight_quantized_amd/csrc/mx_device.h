@@ -59,6 +59,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x128 MXFP4 x MXFP4 MFMA with E8M0 block scales (v_mfma_scale_f32_16x16x128_f8f6f4, both
+// operands in format 4 = E2M1). Lane l supplies 32 codes (16 bytes) of A row l%16 and of B column
+// l%16 for K block l/16, and one scale byte for each (the low byte of the scale register).
+__device__ __forceinline__ f32x4 mfma_fp4_16x16x128(u32x4 a, u32x4 b, uint32_t sa, uint32_t sb,
+                                                    f32x4 c) {
+  const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Memory helpers
 // ---------------------------------------------------------------------------------------------

@@ -39,6 +39,9 @@ struct MoeGemmArgs {
   float* y;                  // [P][H] fp32 workspace
   void* out;                 // [T][H]
   bool out_bf16;
+  // activation variant: x and h MXFP4-quantized (packed [rows][K/2], scales [rows][K/32])
+  bool mx_act;
+  uint8_t *xq, *xqs, *hq, *hqs;
 };
 // Tile rows (BM) the grouped GEMMs use for this problem; the permutation's tile list must match.
 int moe_tile_rows(int T, int k, int E);
@@ -49,6 +52,10 @@ hipError_t launch_moe_combine(const MoeGemmArgs& a, hipStream_t stream);
 
 hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
                          const uint8_t* scales, int N, void* y, bool y_bf16, hipStream_t stream);
+// Activation variant: x already MXFP4 (xq [M][K/2], xqs [M][K/32]).
+hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int K,
+                               const uint8_t* packed, const uint8_t* scales, int N, void* y,
+                               bool y_bf16, hipStream_t stream);
 
 // Kernel attributes that must be set once per process before the first launch.
 hipError_t gemm_init();

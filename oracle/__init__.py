@@ -75,6 +75,9 @@ def lib():
             "mxo_moe_mlp": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, _P(u16), _P(i32),
                                     _P(f32), _P(u8), _P(u8), _P(u8), _P(u8), _P(i32), c_int,
                                     _P(f64), _P(u16)]),
+            "mxo_moe_mlp_ex": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, _P(u16), _P(i32),
+                                       _P(f32), _P(u8), _P(u8), _P(u8), _P(u8), _P(i32), c_int,
+                                       _P(f64), _P(u16), f64, _P(u16), _P(f64)]),
             "mxo_num_threads": (c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -201,11 +204,16 @@ def linear(x_bf16, packed, scales, mx_act: bool = False) -> np.ndarray:
 
 
 def moe_mlp(x_bf16, topk_idx, topk_w, gu_packed, gu_scales, dn_packed, dn_scales, E: int,
-            tokens=None, mx_act: bool = False, want_h: bool = False):
+            tokens=None, mx_act: bool = False, want_h: bool = False, fragile_c: float | None = None):
     """mxo_moe_mlp: fp64 output rows [n_tokens, H] (and optionally the bf16 h rows).
 
     Shapes: x [T, H] bf16 bits; topk_idx/topk_w [T, k]; gu_packed [E, 2F, H/2]; gu_scales
-    [E, 2F, H/32]; dn_packed [E, H, F/2]; dn_scales [E, H, F/32]."""
+    [E, 2F, H/32]; dn_packed [E, H, F/2]; dn_scales [E, H, F/32].
+
+    fragile_c (activation variant): also return (h_alt [n, k, F], slack [n, H]) from
+    mxo_moe_mlp_ex -- the h quantization decisions an fp32 implementation may take the other
+    way, with fp32 errors of g and u assumed below fragile_c * 2^-24 * sqrt(H * sum terms^2),
+    and the bound on the output change they can cause. Returned as (out, [h,] h_alt, slack)."""
     x = _as(x_bf16, np.uint16)
     T, H = x.shape
     idx = _as(topk_idx, np.int32)
@@ -219,15 +227,23 @@ def moe_mlp(x_bf16, topk_idx, topk_w, gu_packed, gu_scales, dn_packed, dn_scales
     n = T if tok is None else tok.shape[0]
     out = np.zeros((n, H), np.float64)
     h = np.zeros((n, k, F), np.uint16) if want_h else None
-    rc = lib().mxo_moe_mlp(T, H, F, E, k, int(bool(mx_act)), _ptr(x, ctypes.c_uint16),
-                           _ptr(idx, ctypes.c_int32), _ptr(w, ctypes.c_float),
-                           _ptr(gp, ctypes.c_uint8), _ptr(gs, ctypes.c_uint8),
-                           _ptr(dp, ctypes.c_uint8), _ptr(ds, ctypes.c_uint8),
-                           _ptr(tok, ctypes.c_int32), n, _ptr(out, ctypes.c_double),
-                           _ptr(h, ctypes.c_uint16))
+    args = (T, H, F, E, k, int(bool(mx_act)), _ptr(x, ctypes.c_uint16), _ptr(idx, ctypes.c_int32),
+            _ptr(w, ctypes.c_float), _ptr(gp, ctypes.c_uint8), _ptr(gs, ctypes.c_uint8),
+            _ptr(dp, ctypes.c_uint8), _ptr(ds, ctypes.c_uint8), _ptr(tok, ctypes.c_int32), n,
+            _ptr(out, ctypes.c_double), _ptr(h, ctypes.c_uint16))
+    if fragile_c is None:
+        rc = lib().mxo_moe_mlp(*args)
+    else:
+        h_alt = np.zeros((n, k, F), np.uint16)
+        slack = np.zeros((n, H), np.float64)
+        rc = lib().mxo_moe_mlp_ex(*args, float(fragile_c), _ptr(h_alt, ctypes.c_uint16),
+                                  _ptr(slack, ctypes.c_double))
     if rc != 0:
         raise ValueError("expert index out of range")
-    return (out, h) if want_h else out
+    res = [out] + ([h] if want_h else [])
+    if fragile_c is not None:
+        res += [h_alt, slack]
+    return tuple(res) if len(res) > 1 else out
 
 
 def num_threads() -> int:

@@ -308,11 +308,42 @@ void mxo_linear(const uint16_t* x, int M, int K, const uint8_t* packed, const ui
  * Precision: fp64 throughout except the bf16 rounding of h (and, in the activation variant, the
  * MXFP4 quantization of x along H and of the bf16 h along F).
  * ------------------------------------------------------------------------------------------- */
-int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
-                const int32_t* topk_idx, const float* topk_w,
-                const uint8_t* gu_packed, const uint8_t* gu_scales,
-                const uint8_t* dn_packed, const uint8_t* dn_scales,
-                const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out) {
+
+/* Adjacent bf16 patterns (one step towards +inf / -inf in value); NaN and Inf never get here. */
+static uint16_t bf16_step(uint16_t b, int up) {
+  const int neg = (b & 0x8000) != 0;
+  const uint16_t mag = b & 0x7fff;
+  if (mag == 0) return up ? 0x0001 : 0x8001;
+  if (up != neg) return (uint16_t)(b + 1); /* magnitude grows */
+  return (uint16_t)(b - 1);
+}
+
+/* The other bf16 a value v could have been rounded to when it is known only to within +-dv:
+ * the neighbour of hb whose midpoint with hb lies within dv of v. Returns 0 if there is none. */
+static int bf16_alternative(double v, uint16_t hb, double dv, uint16_t* alt) {
+  const double d = mxo_double_from_bf16(hb);
+  int found = 0;
+  double best = INFINITY;
+  for (int up = 0; up < 2; ++up) {
+    const uint16_t nb = bf16_step(hb, up);
+    const double dn = mxo_double_from_bf16(nb);
+    if (!isfinite(dn)) continue;
+    const double dist = fabs(v - 0.5 * (d + dn));
+    if (dist <= dv && dist < best) {
+      best = dist;
+      *alt = nb;
+      found = 1;
+    }
+  }
+  return found;
+}
+
+int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
+                   const int32_t* topk_idx, const float* topk_w,
+                   const uint8_t* gu_packed, const uint8_t* gu_scales,
+                   const uint8_t* dn_packed, const uint8_t* dn_scales,
+                   const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out,
+                   double acc_c, uint16_t* h_alt_out, double* slack_out) {
   ensure_tables();
   if (!tokens) n_tokens = T;
   for (int i = 0; i < n_tokens; ++i) {
@@ -322,17 +353,24 @@ int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x
       if (e < 0 || e >= E) return -1;
     }
   }
+  const int fragility = (h_alt_out != NULL || slack_out != NULL);
+  const double u32 = ldexp(1.0, -24);
   const int64_t gu_row = H / 2, gu_srow = H / 32, dn_row = F / 2, dn_srow = F / 32;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int i = 0; i < n_tokens; ++i) {
     int t = tokens ? tokens[i] : i;
     double* xr = (double*)malloc(sizeof(double) * (size_t)H);
     double* a = (double*)malloc(sizeof(double) * 2 * (size_t)F);
+    double* a2 = (double*)malloc(sizeof(double) * 2 * (size_t)F);
+    double* hv = (double*)malloc(sizeof(double) * (size_t)F);
     double* h = (double*)malloc(sizeof(double) * (size_t)F);
     uint16_t* hb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)F);
     double* o = out + (int64_t)i * H;
+    double* sl = slack_out ? slack_out + (int64_t)i * H : NULL;
     activation_row(x + (int64_t)t * H, H, mx_act, xr);
     for (int m = 0; m < H; ++m) o[m] = 0.0;
+    if (sl)
+      for (int m = 0; m < H; ++m) sl[m] = 0.0;
     for (int j = 0; j < k; ++j) {
       int e = topk_idx[(int64_t)t * k + j];
       double wt = (double)topk_w[(int64_t)t * k + j];
@@ -340,18 +378,67 @@ int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x
       for (int n = 0; n < 2 * F; ++n) {
         const uint8_t* prow = gu_packed + ((int64_t)e * 2 * F + n) * gu_row;
         const uint8_t* srow = gu_scales + ((int64_t)e * 2 * F + n) * gu_srow;
-        double acc = 0.0;
-        for (int kk = 0; kk < H; ++kk) acc += xr[kk] * decode_elem(prow, srow, kk);
+        double acc = 0.0, sq = 0.0;
+        for (int kk = 0; kk < H; ++kk) {
+          const double term = xr[kk] * decode_elem(prow, srow, kk);
+          acc += term;
+          if (fragility) sq += term * term;
+        }
         a[n] = acc;
+        a2[n] = sq;
       }
       /* SwiGLU, then bf16 rounding of h */
       for (int f = 0; f < F; ++f) {
         double g = a[f], u = a[F + f];
-        hb[f] = mxo_bf16_from_double(g / (1.0 + exp(-g)) * u);
+        hv[f] = g / (1.0 + exp(-g)) * u;
+        hb[f] = mxo_bf16_from_double(hv[f]);
       }
       if (h_out)
         memcpy(h_out + ((int64_t)i * k + j) * F, hb, sizeof(uint16_t) * (size_t)F);
       activation_row(hb, F, mx_act, h);
+      /* Fragile decisions of the activation variant (test aid, no effect on `out`): an
+       * implementation that forms g and u in fp32 knows h only to within
+       *   dv = |silu'(g) u| dg + |silu(g)| du + 16 u32 |h|,   dg = acc_c u32 sqrt(H sum terms^2),
+       * so its bf16 h may be the other neighbour of the exact value; where that alternative changes
+       * the block's MXFP4 quantization, the down product may legitimately differ by
+       *   wt * sum_i |dq'_i - dq_i| |W_dn[m][i]|  on output m, which is added to slack[m]. */
+      if (fragility) {
+        uint16_t* halt = h_alt_out ? h_alt_out + ((int64_t)i * k + j) * F : NULL;
+        if (halt) memcpy(halt, hb, sizeof(uint16_t) * (size_t)F);
+        if (mx_act) {
+          for (int f = 0; f < F; ++f) {
+            const double g = a[f], u = a[F + f];
+            const double sg = 1.0 / (1.0 + exp(-g));
+            const double dsilu = sg * (1.0 + g * (1.0 - sg));
+            const double dg = acc_c * u32 * sqrt((double)H * a2[f]);
+            const double du = acc_c * u32 * sqrt((double)H * a2[F + f]);
+            const double dv = fabs(dsilu * u) * dg + fabs(g * sg) * du + 16.0 * u32 * fabs(hv[f]);
+            uint16_t alt;
+            if (!bf16_alternative(hv[f], hb[f], dv, &alt)) continue;
+            const int b0 = f & ~31;
+            double blk[32], dq1[32];
+            uint8_t p1[16], s1;
+            for (int q = 0; q < 32; ++q) blk[q] = mxo_double_from_bf16(b0 + q == f ? alt : hb[b0 + q]);
+            quantize_block(blk, p1, &s1);
+            int differs = 0;
+            for (int q = 0; q < 32; ++q) {
+              dq1[q] = decode_elem(p1, &s1, q);
+              if (dq1[q] != h[b0 + q]) differs = 1;
+            }
+            if (!differs) continue;
+            if (halt) halt[f] = alt;
+            if (sl)
+              for (int m = 0; m < H; ++m) {
+                const uint8_t* wrow = dn_packed + ((int64_t)e * H + m) * dn_row;
+                const uint8_t* wsrow = dn_scales + ((int64_t)e * H + m) * dn_srow;
+                double d = 0.0;
+                for (int q = 0; q < 32; ++q)
+                  d += fabs(dq1[q] - h[b0 + q]) * fabs(decode_elem(wrow, wsrow, b0 + q));
+                sl[m] += wt * d;
+              }
+          }
+        }
+      }
       /* down, scaled by the routing weight, summed over the k selected experts */
       for (int m = 0; m < H; ++m) {
         const uint8_t* prow = dn_packed + ((int64_t)e * H + m) * dn_row;
@@ -363,10 +450,21 @@ int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x
     }
     free(hb);
     free(h);
+    free(hv);
+    free(a2);
     free(a);
     free(xr);
   }
   return 0;
+}
+
+int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
+                const int32_t* topk_idx, const float* topk_w,
+                const uint8_t* gu_packed, const uint8_t* gu_scales,
+                const uint8_t* dn_packed, const uint8_t* dn_scales,
+                const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out) {
+  return mxo_moe_mlp_ex(T, H, F, E, k, mx_act, x, topk_idx, topk_w, gu_packed, gu_scales,
+                        dn_packed, dn_scales, tokens, n_tokens, out, h_out, 0.0, NULL, NULL);
 }
 
 int mxo_num_threads(void) {

@@ -65,6 +65,17 @@ int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x
                 const uint8_t* gu_packed, const uint8_t* gu_scales,
                 const uint8_t* dn_packed, const uint8_t* dn_scales,
                 const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out);
+/* The same, plus (activation variant only) the h quantization decisions that an fp32
+ * implementation could legitimately take the other way. acc_c scales the assumed fp32 error of
+ * g and u: acc_c * 2^-24 * sqrt(H * sum of squared terms). h_alt_out (nullable, [n][k][F]): the
+ * other bf16 of each such element, else h itself. slack_out (nullable, [n][H]): bound on the
+ * output change those decisions can cause (0 everywhere when mx_act == 0). */
+int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
+                   const int32_t* topk_idx, const float* topk_w,
+                   const uint8_t* gu_packed, const uint8_t* gu_scales,
+                   const uint8_t* dn_packed, const uint8_t* dn_scales,
+                   const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out,
+                   double acc_c, uint16_t* h_alt_out, double* slack_out);
 
 /* Number of OpenMP threads the oracle uses. */
 int mxo_num_threads(void);

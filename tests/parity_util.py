@@ -48,14 +48,18 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def check_tolerance(got: np.ndarray, ref: np.ndarray, what: str = ""):
-    """Spec bound: ||got-ref||_F <= 5e-3 ||ref||_F and, per element,
-    |got-ref| <= 1e-2 * (||ref row||_2 / sqrt(N) + 1e-3)."""
+def check_tolerance(got: np.ndarray, ref: np.ndarray, what: str = "", slack=None):
+    """Output bound: ||got-ref||_F <= 5e-3 ||ref||_F and, per element,
+    |got-ref| <= 1e-2 * (||ref row||_2 / sqrt(N) + 1e-3).
+    slack (activation variant): per-element allowance for the h quantization decisions the oracle
+    flagged as fragile; the error is reduced by it (not below 0) before both checks."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), "%s: non-finite output" % what
     err = got - ref
+    if slack is not None:
+        err = np.sign(err) * np.maximum(np.abs(err) - np.asarray(slack, np.float64), 0.0)
     rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)
     assert rel <= REL_FROB, "%s: relative Frobenius error %.3e" % (what, rel)
     rms = np.linalg.norm(ref, axis=-1, keepdims=True) / np.sqrt(ref.shape[-1])
@@ -66,16 +70,20 @@ def check_tolerance(got: np.ndarray, ref: np.ndarray, what: str = ""):
     return rel
 
 
-def check_bf16_output(got_bits: np.ndarray, ref: np.ndarray, what: str = ""):
-    """bf16 output: within one bf16 ulp of the oracle value per element, and the Frobenius bound."""
+def check_bf16_output(got_bits: np.ndarray, ref: np.ndarray, what: str = "", slack=None):
+    """bf16 output: within one bf16 ulp of the oracle value per element, and the Frobenius bound
+    (after the fragile-decision slack, if given, as in check_tolerance)."""
     got = inputs.bf16_to_f32(got_bits).astype(np.float64)
     ref = np.asarray(ref, np.float64)
+    err = got - ref
+    if slack is not None:
+        err = np.sign(err) * np.maximum(np.abs(err) - np.asarray(slack, np.float64), 0.0)
     ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(ref), 1e-38))).astype(np.int64) - 7)
     rms = np.linalg.norm(ref, axis=-1, keepdims=True) / np.sqrt(ref.shape[-1])
     bound = np.maximum(ulp, PER_ELEM * (rms + PER_ELEM_FLOOR) * 0.1)
-    bad = np.abs(got - ref) > bound
+    bad = np.abs(err) > bound
     assert not bad.any(), "%s: %d bf16 elements off by more than one ulp" % (what, int(bad.sum()))
-    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300)
     assert rel <= REL_FROB, "%s: relative Frobenius error %.3e" % (what, rel)
 
 

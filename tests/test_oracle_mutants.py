@@ -13,7 +13,8 @@ import oracle
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "mx_oracle.c")
 PIN_TESTS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
-             os.path.join(ROOT, "tests", "test_oracle_path.py")]
+             os.path.join(ROOT, "tests", "test_oracle_path.py"),
+             os.path.join(ROOT, "tests", "test_oracle_fragile.py")]
 
 # (name, exact text in mx_oracle.c, replacement)
 MUTANTS = [
@@ -35,14 +36,21 @@ MUTANTS = [
     ("router-no-bias", "if (br) acc += (double)br[e];", ";"),
     ("permute-unstable", "int32_t row = offsets[e] + fill[e]++;",
      "int32_t row = offsets[e + 1] - 1 - fill[e]++;"),
-    ("swiglu-gate-up-swapped", "double g = a[f], u = a[F + f];", "double g = a[F + f], u = a[f];"),
-    ("silu-sign", "hb[f] = mxo_bf16_from_double(g / (1.0 + exp(-g)) * u);",
-     "hb[f] = mxo_bf16_from_double(g / (1.0 + exp(g)) * u);"),
+    ("swiglu-gate-up-swapped", "double g = a[f], u = a[F + f];\n        hv[f]",
+     "double g = a[F + f], u = a[f];\n        hv[f]"),
+    ("silu-sign", "hv[f] = g / (1.0 + exp(-g)) * u;", "hv[f] = g / (1.0 + exp(g)) * u;"),
     ("routing-weight-dropped", "o[m] += wt * acc;", "o[m] += acc;"),
-    ("down-expert-stride", "dn_packed + ((int64_t)e * H + m) * dn_row",
-     "dn_packed + ((int64_t)e * F + m) * dn_row"),
+    ("down-expert-stride", "prow = dn_packed + ((int64_t)e * H + m) * dn_row",
+     "prow = dn_packed + ((int64_t)e * F + m) * dn_row"),
     ("mx-act-h-skipped", "activation_row(hb, F, mx_act, h);", "activation_row(hb, F, 0, h);"),
     ("bf16-truncates", "nearbyint(a / quantum)", "floor(a / quantum)"),
+    # the fragile-decision aid of the activation variant
+    ("fragile-slack-unweighted", "sl[m] += wt * d;", "sl[m] += d;"),
+    ("fragile-alt-two-steps", "if (up != neg) return (uint16_t)(b + 1);",
+     "if (up != neg) return (uint16_t)(b + 2);"),
+    ("fragile-no-block-check", "if (!differs) continue;", ";"),
+    ("fragile-slack-wrong-weight-row", "wrow = dn_packed + ((int64_t)e * H + m) * dn_row",
+     "wrow = dn_packed + ((int64_t)e * H + (m + 1) % H) * dn_row"),
 ]
 
 
