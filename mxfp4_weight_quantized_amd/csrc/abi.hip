@@ -134,7 +134,7 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
   L.idx = take(P * 4);
   L.w = take(P * 4);
   L.offsets = take((E + 1) * 4);
-  L.perm = take(P * 4);
+  L.perm = take((P + mx::kMaxTileRows) * 4);  // tile-row padding (see launch_permute)
   L.inv = take(P * 4);
   L.tiles = take((size_t)L.max_tiles * 8);
   L.h = take(P * (size_t)d.F * 2);

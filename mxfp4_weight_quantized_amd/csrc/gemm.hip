@@ -44,6 +44,7 @@ struct GemmKArgs {
   const int32_t* num_tiles;
   const int32_t* offsets;     // grouped: expert row offsets [E+1]
   int M;                      // dense rows
+  int rows_total;             // rows of the (permuted) row space: P grouped, M dense
   int F;                      // gate_up: up rows start at F
   void* out;
   int out_bf16;
@@ -83,9 +84,35 @@ __device__ __forceinline__ int swz_b(int row) {
 // filled (zero codes and zero activations contribute nothing, so the MFMA loop needs no masks).
 constexpr uint32_t kBufWord3 = 0x00020000u;   // raw, untyped buffer (gfx9 family)
 constexpr uint32_t kOutOfRange = 0xfffffff0u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* base, int64_t bytes) {
+// A resource as the four scalar dwords: base[31:0]; base[47:32] with stride 0; size; word 3.
+__device__ __forceinline__ i32x4 make_res(const void* base, int64_t bytes) {
   const int nrec = bytes > 0x7ffffff0LL ? 0x7ffffff0 : (int)bytes;  // host checks keep it below
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, (int)kBufWord3);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu)),
+               __builtin_amdgcn_readfirstlane(nrec), (int)kBufWord3};
+}
+
+// Direct global -> LDS loads (buffer_load ... lds): lane i writes lds + 16*i (16-byte form) or
+// one byte into the dword at lds + 4*i (byte form); lds must be wave-uniform. They are written as
+// inline asm on purpose: the compiler orders each LDS read after every direct-to-LDS load it
+// cannot prove disjoint, and it does not tell the pipeline's stage buffers apart, so with the
+// builtin every LDS read of the current stage would also wait for the loads in flight into the
+// next ones. The callers wait for these loads themselves (s_waitcnt vmcnt, then a barrier)
+// before reading what they wrote. The s_nop covers the M0-write -> LDS-DMA hazard.
+__device__ __forceinline__ void dma_b128(const i32x4& res, uint32_t voff, uint32_t soff,
+                                         const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(res), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b8(const i32x4& res, uint32_t voff, uint32_t soff,
+                                       const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(res), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
+               : "memory", "m0");
 }
 
 // E8M0 byte -> fp32 scale operand, without branches (b = 0: 2^-127; b = 255: NaN).
@@ -107,60 +134,25 @@ struct DmaPlan {
   static __device__ __forceinline__ int instr(int wave, int q) { return (wave * I + q) % REGION_INSTRS; }
 };
 
-// Grouped / dense MXFP4 GEMM tile: out[BM rows x BN cols] = A times the weights (decoded).
-//   BM x BN workgroup tile, WM x WN waves, each wave a (BM/WM) x (BN/WN) tile of 16 x 16 MFMA
-//   fragments; KT 32-element blocks per pipeline stage; STAGES (2 or 3) stages in flight.
-//   AFP4 = false: A is bf16 and the weights are decoded to bf16 for v_mfma_f32_16x16x32_bf16.
-//   AFP4 = true:  A is MXFP4 too (packed codes + E8M0 scales, same layout as the weights) and
-//                 each 16 x 16 x 128 slice is one v_mfma_scale_f32_16x16x128_f8f6f4 with both
-//                 operands' block scales, so nothing is decoded.
-// Per stage a workgroup moves A chunks, B chunks and their scale bytes straight into LDS.
-template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4>
-__device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
-  constexpr int NW = WM * WN;
-  constexpr int NT = NW * 64;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr bool SWIGLU = (MODE == MODE_GATE_UP);
-  constexpr int BNH = BN / 2;
-  constexpr int A_ROW = AFP4 ? KT * 16 : KT * 64, B_ROW = KT * 16;
-  constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * B_ROW;
-  using PA = DmaPlan<A_STAGE / 1024, NW>;
-  using PB = DmaPlan<B_STAGE / 1024, NW>;
-  using PS = DmaPlan<BN * KT / 64, NW>;                    // weight scale bytes
-  using PSA = DmaPlan<AFP4 ? BM * KT / 64 : 1, NW>;         // activation scale bytes
-  constexpr int IA = PA::I, IB = PB::I, IS = PS::I, ISA = AFP4 ? PSA::I : 0;
-  constexpr int SS = KT / 4;                               // super-steps per stage
-  constexpr int LPS = IS + ISA + IA + IB;                  // vector-memory ops per wave per stage
-  static_assert(A_STAGE % 1024 == 0 && B_STAGE % 1024 == 0, "stage split");
-  static_assert((BN * KT) % 64 == 0 && (!AFP4 || (BM * KT) % 64 == 0), "scale split");
-  static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "wave tile");
-  static_assert(!SWIGLU || FN % 2 == 0, "gate/up fragment pairs");
-  static_assert(KT % 4 == 0 && (AFP4 || A_ROW >= 256) && (STAGES == 2 || STAGES == 3), "pipeline");
-  static_assert(2 * LPS < 64, "vmcnt range");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t sA[STAGES][A_STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB[STAGES][B_STAGE];
-  __shared__ uint32_t sSc[STAGES][BN * KT];                 // one E8M0 byte per dword
-  __shared__ uint32_t sSa[AFP4 ? STAGES : 1][AFP4 ? BM * KT : 1];
-  __shared__ int sArow[BM];
-
-  // ---- which tile ----
-  // Workgroups go round-robin to the 8 XCDs (each with its own L2). XCD x takes super-tiles
-  // x, x+8, ...; a super-tile is GM x GN (m, n) tiles, and its GM*GN workgroups run together on
-  // the XCD, so at every K stage they share GM activation tiles and GN weight tiles in L2.
+// ---- which tile ----
+// Workgroups go round-robin to the 8 XCDs (each with its own L2). XCD x takes super-tiles x, x+8,
+// ...; a super-tile is GM x GN (m, n) tiles, and its GM*GN workgroups run together on the XCD, so
+// at every K stage they share GM activation tiles and GN weight tiles in L2. Returns false for a
+// workgroup past the last tile. Grouped tiles come from the tile list: (expert, first row).
+template <int BM, int GM>
+__device__ __forceinline__ bool pick_tile(const GemmKArgs& p, int& e, int& r0, int& row_end,
+                                          int& nt) {
   constexpr int GN = 32 / GM;
   const bool grouped = p.tiles != nullptr;
   const int num_mt = grouped ? *p.num_tiles : (p.M + BM - 1) / BM;
   const int sm_count = (num_mt + GM - 1) / GM, sn_count = (p.n_tiles + GN - 1) / GN;
   const int slot = blockIdx.x >> 3;
   const int super_tile = (blockIdx.x & 7) + 8 * (slot / (GM * GN));
-  if (super_tile >= sm_count * sn_count) return;
+  if (super_tile >= sm_count * sn_count) return false;
   const int pos = slot % (GM * GN);
   const int mt = (super_tile % sm_count) * GM + pos / GN;
-  const int nt = (super_tile / sm_count) * GN + pos % GN;
-  if (mt >= num_mt || nt >= p.n_tiles) return;
-  int e, r0, row_end;
+  nt = (super_tile / sm_count) * GN + pos % GN;
+  if (mt >= num_mt || nt >= p.n_tiles) return false;
   if (grouped) {
     const int2 tl = p.tiles[mt];
     e = __builtin_amdgcn_readfirstlane(tl.x);
@@ -171,204 +163,36 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     r0 = mt * BM;
     row_end = p.M;
   }
-  const int K = p.K;
-  const int nb = K >> 5;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets go in M0
-  const int wm = wave / WN, wn = wave % WN;
-  const int ln = lane & 15, g = lane >> 4;
+  return true;
+}
 
-  // ---- weight rows (within the expert) ----
-  auto weight_row = [&](int lrow) -> int {
-    if (SWIGLU)
-      return lrow < BNH ? min(nt * BNH + lrow, p.F - 1) : p.F + min(nt * BNH + lrow - BNH, p.F - 1);
-    return min(nt * BN + lrow, p.N - 1);
-  };
-  const int64_t rpe = p.b_rows_per_expert;
-  const __amdgpu_buffer_rsrc_t rB = make_buf(p.Bp + (int64_t)e * rpe * (K >> 1), rpe * (K >> 1));
-  const __amdgpu_buffer_rsrc_t rS = make_buf(p.Bs + (int64_t)e * rpe * nb, rpe * nb);
-  const __amdgpu_buffer_rsrc_t rA = make_buf(p.A, p.a_rows * (AFP4 ? (K >> 1) : K * 2));
-  const __amdgpu_buffer_rsrc_t rSA = make_buf(p.Asc, AFP4 ? p.a_rows * nb : 0);
-  uint32_t voffB[IB];
-  int bblk[IB];
-#pragma unroll
-  for (int q = 0; q < IB; ++q) {
-    const int off = PB::instr(wave, q) * 1024 + lane * 16;
-    const int lrow = off / B_ROW;
-    const int chunk = ((off % B_ROW) >> 4) ^ swz_b<KT>(lrow);
-    bblk[q] = chunk;
-    voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
-  }
-  // scale dword idx of a stage's scale area holds (row, block) = (idx / KT, idx % KT)
-  uint32_t voffS[IS];
-  int sblk[IS];
-#pragma unroll
-  for (int q = 0; q < IS; ++q) {
-    const int idx = PS::instr(wave, q) * 64 + lane;
-    sblk[q] = idx % KT;
-    voffS[q] = (uint32_t)weight_row(idx / KT) * (uint32_t)nb + sblk[q];
-  }
-  int brow[FN];
-#pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    int base;
-    if (SWIGLU)
-      base = (f < FN / 2) ? wn * (BNH / WN) + f * 16 : BNH + wn * (BNH / WN) + (f - FN / 2) * 16;
-    else
-      base = wn * TN + f * 16;
-    brow[f] = base + ln;
-  }
+// Weight row (within the expert) of local tile row lrow; gate_up tiles hold BN/2 gate rows then
+// the matching BN/2 up rows. Rows past the end repeat the last one (their results are dropped).
+template <int MODE, int BN>
+__device__ __forceinline__ int weight_row_of(const GemmKArgs& p, int nt, int lrow) {
+  constexpr int BNH = BN / 2;
+  if (MODE == MODE_GATE_UP)
+    return lrow < BNH ? min(nt * BNH + lrow, p.F - 1) : p.F + min(nt * BNH + lrow - BNH, p.F - 1);
+  return min(nt * BN + lrow, p.N - 1);
+}
 
-  // ---- activation rows ----
-  for (int i = tid; i < BM; i += NT) {
-    const int r = min(r0 + i, row_end - 1);
-    sArow[i] = p.a_gather ? p.a_gather[r] / p.a_div : r;
-  }
-  __syncthreads();
-  uint32_t voffA[IA];
-  int ablk[IA];
-#pragma unroll
-  for (int q = 0; q < IA; ++q) {
-    const int off = PA::instr(wave, q) * 1024 + lane * 16;
-    const int lrow = off / A_ROW;
-    if constexpr (AFP4) {
-      const int chunk = ((off % A_ROW) >> 4) ^ swz_b<KT>(lrow);
-      ablk[q] = chunk;
-      voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K >> 1) + chunk * 16;
-    } else {
-      const int chunk = ((off % A_ROW) >> 4) ^ swz_a(lrow);
-      ablk[q] = chunk >> 2;
-      voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
-    }
-  }
-  uint32_t voffSA[ISA > 0 ? ISA : 1];
-  int sablk[ISA > 0 ? ISA : 1];
-#pragma unroll
-  for (int q = 0; q < ISA; ++q) {
-    const int idx = PSA::instr(wave, q) * 64 + lane;
-    sablk[q] = idx % KT;
-    voffSA[q] = (uint32_t)sArow[idx / KT] * (uint32_t)nb + sablk[q];
-  }
+// Local tile row of fragment f of wave column wn (lane row ln): gate_up waves take FN/2 gate
+// fragments and the FN/2 up fragments of the same output columns.
+template <int MODE, int BN, int WN, int FN>
+__device__ __forceinline__ int frag_row(int wn, int f, int ln) {
+  constexpr int BNH = BN / 2, TN = BN / WN;
+  if (MODE == MODE_GATE_UP)
+    return ((f < FN / 2) ? wn * (BNH / WN) + f * 16 : BNH + wn * (BNH / WN) + (f - FN / 2) * 16) + ln;
+  return wn * TN + f * 16 + ln;
+}
 
-  // Issue one stage: scale bytes, A chunks and B chunks, all straight into LDS. Every wave issues
-  // exactly LPS vector-memory ops. Full stages add the K offset as a scalar; the stage that holds
-  // the end of K moves it into the lane offsets and sends blocks past K out of range (zeros).
-  auto issue = [&](int kt, int st) {
-    const bool full = (kt + 1) * KT <= nb;
-    const int kb = kt * KT;
-#pragma unroll
-    for (int q = 0; q < IS; ++q) {
-      const uint32_t vo = full ? voffS[q] : (kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rS, (lds_ptr_t)&sSc[st][PS::instr(wave, q) * 64], 1,
-                                               vo, full ? kb : 0, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < ISA; ++q) {
-      const uint32_t vo = full ? voffSA[q] : (kb + sablk[q] < nb ? voffSA[q] + kb : kOutOfRange);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rSA, (lds_ptr_t)&sSa[st][PSA::instr(wave, q) * 64], 1,
-                                               vo, full ? kb : 0, 0, 0);
-    }
-    constexpr int A_KB = AFP4 ? 16 : 64;  // bytes of A per 32-element block
-#pragma unroll
-    for (int q = 0; q < IA; ++q) {
-      const uint32_t vo = full ? voffA[q] : (kb + ablk[q] < nb ? voffA[q] + kb * A_KB : kOutOfRange);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_ptr_t)&sA[st][PA::instr(wave, q) * 1024], 16,
-                                               vo, full ? kb * A_KB : 0, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < IB; ++q) {
-      const uint32_t vo = full ? voffB[q] : (kb + bblk[q] < nb ? voffB[q] + kb * 16 : kOutOfRange);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_ptr_t)&sB[st][PB::instr(wave, q) * 1024], 16,
-                                               vo, full ? kb * 16 : 0, 0, 0);
-    }
-  };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // One stage of MFMAs.
-  //   bf16 A: per super-step, read the wave's A fragments and packed B blocks; decode B fragment
-  //   f+1 (two codes per cvt, other register set) while the 4 x FM MFMAs of fragment f run.
-  //   FP4 A: per super-step and fragment pair, one scaled MFMA on the raw blocks and scale bytes.
-  auto compute = [&](int st) {
-    const uint8_t* As = sA[st];
-    const uint8_t* Bsm = sB[st];
-    const uint32_t* Sc = sSc[st];
-#pragma unroll
-    for (int j = 0; j < SS; ++j) {
-      u32x4 w[FN];
-      uint32_t scb[FN];
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int r = brow[f];
-        w[f] = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-        scb[f] = Sc[r * KT + 4 * j + g];
-      }
-      if constexpr (AFP4) {
-        u32x4 a[FM];
-        uint32_t sca[FM];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 16 + ln;
-          a[i] = lds_read_b128(As + r * A_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-          sca[i] = sSa[st][r * KT + 4 * j + g];
-        }
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-            acc[i][f] = mfma_fp4_16x16x128(a[i], w[f], sca[i], scb[f], acc[i][f]);
-      } else {
-        bf16x8 a[FM][4];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 16 + ln;
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-            a[i][s] = u32x4_as_bf16x8(
-                lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ swz_a(r)) << 4)));
-        }
-        float sc[FN];
-#pragma unroll
-        for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f] & 0xffu);
-        bf16x8 b[2][4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
-#pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          if (f + 1 < FN) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) b[(f + 1) & 1][s] = fp4x8_to_bf16x8(w[f + 1][s], sc[f + 1]);
-          }
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
-        }
-      }
-    }
-  };
-
-  // Pipeline: stage kt+STAGES-1 is issued in iteration kt. At iteration kt the loads of stage kt
-  // must have landed; with 3 stages those of stage kt+1 may still be in flight.
-  const int ntk = (nb + KT - 1) / KT;
-  issue(0, 0);
-  if (STAGES == 3 && ntk > 1) issue(1, 1);
-  int st = 0;
-  for (int kt = 0; kt < ntk; ++kt) {
-    if (STAGES == 3 && kt + 1 < ntk) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
-    barrier_lds();
-    if (kt + STAGES - 1 < ntk) issue(kt + STAGES - 1, st == 0 ? STAGES - 1 : st - 1);
-    compute(st);
-    st = (st == STAGES - 1) ? 0 : st + 1;
-  }
-
-  // ---- epilogue ----
+// Epilogue of a wave's FM x FN fragments (rows r0 + wm*TM + 16i + 4g + q, column lane ln):
+// gate_up -> SwiGLU in fp32 -> bf16 h; down -> times the pair's routing weight, stored at the
+// pair's own row (un-permuted); linear -> fp32 or bf16.
+template <int MODE, int FM, int FN, int TM, int BN, int WN>
+__device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc)[FM][FN], int r0,
+                                           int row_end, int nt, int wm, int wn, int g, int ln) {
+  constexpr int BNH = BN / 2, TN = BN / WN;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -410,20 +234,290 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   }
 }
 
-// One kernel name per role, so profiles show which product a launch is.
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, bool AFP4>
-__global__ __launch_bounds__(WM * WN * 64) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4>(p);
-}
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, bool AFP4>
-__global__ __launch_bounds__(WM * WN * 64) void moe_down_weighted_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4>(p);
-}
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, bool AFP4>
-__global__ __launch_bounds__(WM * WN * 64) void linear_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4>(p);
+// Grouped / dense MXFP4 GEMM tile: out[BM rows x BN cols] = A times the weights (decoded).
+//   BM x BN workgroup tile, WM x WN waves, each wave a (BM/WM) x (BN/WN) tile of 16 x 16 MFMA
+//   fragments; KT 32-element blocks per pipeline stage; STAGES (2 or 3) stages in flight.
+//   AFP4 = false: A is bf16 and the weights are decoded to bf16 for v_mfma_f32_16x16x32_bf16.
+//   AFP4 = true:  A is MXFP4 too (packed codes + E8M0 scales, same layout as the weights) and
+//                 each 16 x 16 x 128 slice is one v_mfma_scale_f32_16x16x128_f8f6f4 with both
+//                 operands' block scales, so nothing is decoded.
+// Per stage a workgroup moves A chunks, B chunks and their scale bytes straight into LDS.
+template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4>
+__device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
+  constexpr int NW = WM * WN;
+  constexpr int NT = NW * 64;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr bool SWIGLU = (MODE == MODE_GATE_UP);
+  constexpr int BNH = BN / 2;
+  constexpr int A_ROW = AFP4 ? KT * 16 : KT * 64, B_ROW = KT * 16;
+  constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * B_ROW;
+  using PA = DmaPlan<A_STAGE / 1024, NW>;
+  using PB = DmaPlan<B_STAGE / 1024, NW>;
+  using PS = DmaPlan<BN * KT / 64, NW>;                    // weight scale bytes
+  using PSA = DmaPlan<AFP4 ? BM * KT / 64 : 1, NW>;         // activation scale bytes
+  constexpr int IA = PA::I, IB = PB::I, IS = PS::I, ISA = AFP4 ? PSA::I : 0;
+  constexpr int SS = KT / 4;                               // super-steps per stage
+  constexpr int LPS = IS + ISA + IA + IB;                  // vector-memory ops per wave per stage
+  static_assert(A_STAGE % 1024 == 0 && B_STAGE % 1024 == 0, "stage split");
+  static_assert((BN * KT) % 64 == 0 && (!AFP4 || (BM * KT) % 64 == 0), "scale split");
+  static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "wave tile");
+  static_assert(!SWIGLU || FN % 2 == 0, "gate/up fragment pairs");
+  static_assert(KT % 4 == 0 && (AFP4 || A_ROW >= 256) && (STAGES == 2 || STAGES == 3), "pipeline");
+  static_assert(2 * LPS < 64, "vmcnt range");
+  static_assert(BM <= NT, "one gathered row per thread");
+
+  // One LDS variable per pipeline stage: the compiler orders LDS reads after direct-to-LDS
+  // loads by variable, so reads of stage s must not share a variable with the loads in flight
+  // into the other stages (else it waits for all of them before every read).
+  struct Stage {
+    uint8_t A[A_STAGE];
+    uint8_t B[B_STAGE];
+    uint32_t Sc[BN * KT];            // weight scale bytes, one per dword
+    uint32_t Sa[AFP4 ? BM * KT : 1];  // activation scale bytes (FP4 A)
+  };
+  __shared__ __attribute__((aligned(1024))) Stage st0;
+  __shared__ __attribute__((aligned(1024))) Stage st1;
+  __shared__ __attribute__((aligned(1024))) Stage st2;  // referenced only with 3 stages
+  __shared__ int sArow[BM];
+  auto stage = [&](auto S) -> Stage& {
+    if constexpr (decltype(S)::value == 0) return st0;
+    else if constexpr (decltype(S)::value == 1) return st1;
+    else return st2;
+  };
+
+  int e, r0, row_end, nt;
+  if (!pick_tile<BM, GM>(p, e, r0, row_end, nt)) return;
+  const int K = p.K;
+  const int nb = K >> 5;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets go in M0
+  const int wm = wave / WN, wn = wave % WN;
+  const int ln = lane & 15, g = lane >> 4;
+
+  // ---- weight rows (within the expert) ----
+  auto weight_row = [&](int lrow) -> int { return weight_row_of<MODE, BN>(p, nt, lrow); };
+  const int64_t rpe = p.b_rows_per_expert;
+  const i32x4 rB = make_res(p.Bp + (int64_t)e * rpe * (K >> 1), rpe * (K >> 1));
+  const i32x4 rS = make_res(p.Bs + (int64_t)e * rpe * nb, rpe * nb);
+  const i32x4 rA = make_res(p.A, p.a_rows * (AFP4 ? (K >> 1) : K * 2));
+  const i32x4 rSA = make_res(p.Asc, AFP4 ? p.a_rows * nb : 0);
+  uint32_t voffB[IB];
+  int bblk[IB];
+#pragma unroll
+  for (int q = 0; q < IB; ++q) {
+    const int off = PB::instr(wave, q) * 1024 + lane * 16;
+    const int lrow = off / B_ROW;
+    const int chunk = ((off % B_ROW) >> 4) ^ swz_b<KT>(lrow);
+    bblk[q] = chunk;
+    voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
+  }
+  // scale dword idx of a stage's scale area holds (row, block) = (idx / KT, idx % KT)
+  uint32_t voffS[IS];
+  int sblk[IS];
+#pragma unroll
+  for (int q = 0; q < IS; ++q) {
+    const int idx = PS::instr(wave, q) * 64 + lane;
+    sblk[q] = idx % KT;
+    voffS[q] = (uint32_t)weight_row(idx / KT) * (uint32_t)nb + sblk[q];
+  }
+  int brow[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) brow[f] = frag_row<MODE, BN, WN, FN>(wn, f, ln);
+
+  // ---- activation rows, weight prefetch ----
+  // The activation rows of a gathered tile depend on a chain of loads (tile -> perm -> row). The
+  // row indices are read first, with scalar loads (uniform addresses, so they count on lgkmcnt),
+  // and the first stages' weight loads go out right behind them: the weights stream while the
+  // chain resolves. Rows past the tile's expert read some valid row; their results are dropped.
+  int gv[BM];  // perm is padded by the tile height: BM entries from r0 exist
+  if (p.a_gather != nullptr) {
+#pragma unroll
+    for (int q = 0; q < BM; ++q) gv[q] = p.a_gather[r0 + q];
+  }
+  auto issue_w = [&](Stage& sg, int kt) {
+    const bool full = (kt + 1) * KT <= nb;
+    const int kb = kt * KT;
+#pragma unroll
+    for (int q = 0; q < IS; ++q) {
+      const uint32_t vo = full ? voffS[q] : (kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange);
+      dma_b8(rS, vo, full ? kb : 0, &sg.Sc[PS::instr(wave, q) * 64]);
+    }
+#pragma unroll
+    for (int q = 0; q < IB; ++q) {
+      const uint32_t vo = full ? voffB[q] : (kb + bblk[q] < nb ? voffB[q] + kb * 16 : kOutOfRange);
+      dma_b128(rB, vo, full ? kb * 16 : 0, &sg.B[PB::instr(wave, q) * 1024]);
+    }
+  };
+  const int ntk = (nb + KT - 1) / KT;
+  issue_w(st0, 0);
+  if (STAGES == 3 && ntk > 1) issue_w(st1, 1);
+  if (p.a_gather != nullptr) {  // consumed only now, after the weight loads went out
+    int gathered = gv[0];
+#pragma unroll
+    for (int q = 1; q < BM; ++q) gathered = (tid == q) ? gv[q] : gathered;
+    if (tid < BM) sArow[tid] = gathered / p.a_div;
+  } else if (tid < BM) {
+    sArow[tid] = min(r0 + tid, p.rows_total - 1);
+  }
+  barrier_lds();
+  uint32_t voffA[IA];
+  int ablk[IA];
+#pragma unroll
+  for (int q = 0; q < IA; ++q) {
+    const int off = PA::instr(wave, q) * 1024 + lane * 16;
+    const int lrow = off / A_ROW;
+    if constexpr (AFP4) {
+      const int chunk = ((off % A_ROW) >> 4) ^ swz_b<KT>(lrow);
+      ablk[q] = chunk;
+      voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K >> 1) + chunk * 16;
+    } else {
+      const int chunk = ((off % A_ROW) >> 4) ^ swz_a(lrow);
+      ablk[q] = chunk >> 2;
+      voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
+    }
+  }
+  uint32_t voffSA[ISA > 0 ? ISA : 1];
+  int sablk[ISA > 0 ? ISA : 1];
+#pragma unroll
+  for (int q = 0; q < ISA; ++q) {
+    const int idx = PSA::instr(wave, q) * 64 + lane;
+    sablk[q] = idx % KT;
+    voffSA[q] = (uint32_t)sArow[idx / KT] * (uint32_t)nb + sablk[q];
+  }
+  auto issue_a = [&](Stage& sg, int kt) {
+    const bool full = (kt + 1) * KT <= nb;
+    const int kb = kt * KT;
+#pragma unroll
+    for (int q = 0; q < ISA; ++q) {
+      const uint32_t vo = full ? voffSA[q] : (kb + sablk[q] < nb ? voffSA[q] + kb : kOutOfRange);
+      dma_b8(rSA, vo, full ? kb : 0, &sg.Sa[PSA::instr(wave, q) * 64]);
+    }
+    constexpr int A_KB = AFP4 ? 16 : 64;  // bytes of A per 32-element block
+#pragma unroll
+    for (int q = 0; q < IA; ++q) {
+      const uint32_t vo = full ? voffA[q] : (kb + ablk[q] < nb ? voffA[q] + kb * A_KB : kOutOfRange);
+      dma_b128(rA, vo, full ? kb * A_KB : 0, &sg.A[PA::instr(wave, q) * 1024]);
+    }
+  };
+  issue_a(st0, 0);
+  if (STAGES == 3 && ntk > 1) issue_a(st1, 1);
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One stage of MFMAs.
+  //   bf16 A: per super-step, read the wave's A fragments and packed B blocks; decode B fragment
+  //   f+1 (two codes per cvt, other register set) while the 4 x FM MFMAs of fragment f run.
+  //   FP4 A: per super-step and fragment pair, one scaled MFMA on the raw blocks and scale bytes.
+  auto compute = [&](const Stage& sg) {
+    const uint8_t* As = sg.A;
+    const uint8_t* Bsm = sg.B;
+    const uint32_t* Sc = sg.Sc;
+#pragma unroll
+    for (int j = 0; j < SS; ++j) {
+      u32x4 w[FN];
+      uint32_t scb[FN];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int r = brow[f];
+        w[f] = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
+        scb[f] = Sc[r * KT + 4 * j + g];
+      }
+      if constexpr (AFP4) {
+        u32x4 a[FM];
+        uint32_t sca[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * TM + i * 16 + ln;
+          a[i] = lds_read_b128(As + r * A_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
+          sca[i] = sg.Sa[r * KT + 4 * j + g];
+        }
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+            acc[i][f] = mfma_fp4_16x16x128(a[i], w[f], sca[i], scb[f], acc[i][f]);
+      } else {
+        bf16x8 a[FM][4];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * TM + i * 16 + ln;
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            a[i][s] = u32x4_as_bf16x8(
+                lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ swz_a(r)) << 4)));
+        }
+        float sc[FN];
+#pragma unroll
+        for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f] & 0xffu);
+        bf16x8 b[2][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
+#pragma unroll
+        for (int f = 0; f < FN; ++f) {
+          if (f + 1 < FN) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) b[(f + 1) & 1][s] = fp4x8_to_bf16x8(w[f + 1][s], sc[f + 1]);
+          }
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
+        }
+      }
+    }
+  };
+
+  // Pipeline: stage kt+STAGES-1 is issued in iteration kt, weights and activations of a stage
+  // back to back (LPS vector-memory ops per wave). At iteration kt the loads of stage kt must
+  // have landed; with 3 stages those of stage kt+1 may still be in flight. The prologue issued
+  // [weights 0][weights 1][activations 0][activations 1], so at iteration 0 only the
+  // activations of stage 1 may stay outstanding. The loop is unrolled by STAGES so that every
+  // stage buffer is named statically.
+  auto step = [&](auto S, int kt) {
+    constexpr int s = decltype(S)::value;
+    if (STAGES == 3 && kt + 1 < ntk) {
+      if (kt == 0) wait_vmcnt<ISA + IA>();
+      else wait_vmcnt<LPS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_lds();
+    if (kt + STAGES - 1 < ntk) {
+      Stage& sn = stage(IntC<(s + STAGES - 1) % STAGES>{});
+      issue_w(sn, kt + STAGES - 1);
+      issue_a(sn, kt + STAGES - 1);
+    }
+    compute(stage(S));
+  };
+  int kt0 = 0;
+  for (; kt0 + STAGES <= ntk; kt0 += STAGES)
+    static_for<0, STAGES>([&](auto S) { step(S, kt0 + decltype(S)::value); });
+  static_for<0, STAGES - 1>([&](auto S) {
+    if (kt0 + decltype(S)::value < ntk) step(S, kt0 + decltype(S)::value);
+  });
+
+  store_tile<MODE, FM, FN, TM, BN, WN>(p, acc, r0, row_end, nt, wm, wn, g, ln);
 }
 
+// One kernel name per role, so profiles show which product a launch is.
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4>
+__global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4>(p);
+}
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4>
+__global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_down_weighted_kernel(GemmKArgs p) {
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4>(p);
+}
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4>
+__global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_kernel(GemmKArgs p) {
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4>(p);
+}
 // out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
 // indices) contribute nothing.
 template <bool BF16_OUT>
@@ -454,14 +548,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles with a 2-stage pipeline, so
 // two workgroups fit in a CU's LDS and one's tile prologue / epilogue overlaps the other's MFMAs.
 // gate_up: four waves of 64 x 64; down: eight waves of 32 x 64 (measured best for each).
-// Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, weight
-// streaming dominates.
-struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4; };
-struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 2, WN = 4, KT = 4, ST = 2, GM = 4; };
-struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1; };
-struct CfgDecDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1; };
+// Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, 8 blocks per
+// stage and 2 stages; weight streaming dominates (best of the 16-row shapes measured with the
+// weights rotated through copies larger than the last-level cache).
+// OCC: workgroups per CU the register allocation must leave room for (the second launch bound
+// is in waves per SIMD).
+struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2; };
+struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 2, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2; };
+struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 8, ST = 2, GM = 1, OCC = 2; };
+struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 8, ST = 2, GM = 1, OCC = 2; };
 constexpr int kPrefillRows = 64;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
+static_assert(kPrefillRows <= kMaxTileRows, "perm padding");
 
 template <class C, int MODE, bool AFP4 = false>
 hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream) {
@@ -474,11 +572,11 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
   const int64_t supers = (int64_t)((m_tiles + C::GM - 1) / C::GM) * ((n_tiles + GN - 1) / GN);
   const dim3 grid((unsigned)(8 * 32 * ((supers + 7) / 8))), block(C::WM * C::WN * 64);
   if constexpr (MODE == MODE_GATE_UP)
-    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, AFP4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4>), grid, block, 0, stream, a);
   else if constexpr (MODE == MODE_DOWN)
-    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, AFP4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, AFP4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -499,6 +597,7 @@ GemmKArgs gate_up_args(const MoeGemmArgs& m) {
   g.tiles = m.tiles;
   g.num_tiles = m.num_tiles;
   g.offsets = m.offsets;
+  g.rows_total = m.T * m.k;
   g.F = m.F;
   g.out = m.h;
   return g;
@@ -519,6 +618,7 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
   d.tiles = m.tiles;
   d.num_tiles = m.num_tiles;
   d.offsets = m.offsets;
+  d.rows_total = m.T * m.k;
   d.F = m.F;
   d.out = m.y;
   d.perm = m.perm;
@@ -584,6 +684,7 @@ hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
   g.N = N;
   g.K = K;
   g.M = M;
+  g.rows_total = M;
   g.F = N;
   g.out = y;
   g.out_bf16 = y_bf16 ? 1 : 0;
@@ -605,6 +706,7 @@ hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int
   g.N = N;
   g.K = K;
   g.M = M;
+  g.rows_total = M;
   g.F = N;
   g.out = y;
   g.out_bf16 = y_bf16 ? 1 : 0;

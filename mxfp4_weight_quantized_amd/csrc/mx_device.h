@@ -1,5 +1,5 @@
 // mx_device.h -- device-side building blocks for gfx950 (CDNA4): vector types, MFMA and FP4
-// conversion wrappers, direct-to-LDS loads, wait counters and barriers.
+// conversion wrappers, wait counters and barriers.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -9,8 +9,8 @@ namespace mx {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -18,22 +18,12 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // ---------------------------------------------------------------------------------------------
 // Scalar helpers
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
-}
-
-// E8M0 scale byte -> fp32 scale operand of the scaled conversions (2^(b-127); b = 0 gives the
-// subnormal 2^-127, b = 255 a NaN).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
-  if (b == 0) return __uint_as_float(0x00400000u);
-  if (b == 255) return __uint_as_float(0x7fc00000u);
-  return __uint_as_float(b << 23);
 }
 
 // Eight E2M1 codes (one dword, element 0 in the low nibble) times a scale -> eight bf16 in the
@@ -72,20 +62,11 @@ __device__ __forceinline__ f32x4 mfma_fp4_16x16x128(u32x4 a, u32x4 b, uint32_t s
 // ---------------------------------------------------------------------------------------------
 // Memory helpers
 // ---------------------------------------------------------------------------------------------
-// 16-byte global -> LDS copy without a register round trip. `lds` must be wave-uniform: lane i
-// writes lds + 16*i.
-__device__ __forceinline__ void load_lds_16(const void* gptr, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gptr, (lds_ptr_t)lds_wave_base, 16, 0, 0);
-}
-
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkmcnt0() {
-  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));
 }
 
 // Workgroup barrier without the full memory fence of __syncthreads(): outstanding prefetches
@@ -97,8 +78,5 @@ __device__ __forceinline__ void barrier_lds() {
 __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
-
-// Wave-wide helpers (wave64).
-__device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 }  // namespace mx

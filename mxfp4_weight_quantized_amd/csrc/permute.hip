@@ -97,6 +97,10 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
     if (tile_rows > 0) *num_tiles = tbase[E];
     if (status != nullptr) *status = bad;
   }
+  // With a tile list, perm carries tile_rows entries of padding past P: rows past the last valid
+  // one (and the padding) hold pair 0, so a tile may read its whole row range of perm.
+  if (tile_rows > 0)
+    for (int i = tot[E] + threadIdx.x; i < P + tile_rows; i += blockDim.x) perm[i] = 0;
   __syncthreads();
 
   // 3. stable scatter, 64 pairs per step in (token, slot) order
