@@ -400,6 +400,26 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
     return out
 
 
+def summarize_trace(trace_dir, command, title):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv): calls,
+    average / min / max duration and share of GPU time per kernel."""
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no kernel_stats.csv under %s" % trace_dir)
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    out = ["# %s" % title, "", "Command (from the repository root, rocprofv3 output under "
+           "gpurun_out/):", "", "```", command, "```", "",
+           "| kernel | calls | avg us | min us | max us | share % |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"].replace("mx::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f |" % (
+            name[:110], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,7 +433,13 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-workload", default=None,
                     help="with --summarize-counters: workload name to file the numbers under")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "COMMAND", "TITLE"),
+                    help="print a markdown summary of a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(*args.summarize_trace))
+        return 0
 
     if args.summarize_counters:
         wl = args.traffic_workload or args.workload

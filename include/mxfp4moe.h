@@ -92,7 +92,8 @@ mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t
  * moe_route_topk -- router logits, top-k expert selection and softmax over the k selected
  * ([GGUF] "ggml Metal 커널 통합": top-k expert selection for MoE; the router itself is a reading).
  *   x [T][H] bf16, wr [E][H] bf16, br [E] fp32 or NULL (no bias).
- *   logits [T][E] fp32 out (may be NULL: not stored); topk_idx [T][k] int32 out, in rank order
+ *   logits [T][E] fp32 out (required: the selection pass reads it back); topk_idx [T][k] int32
+ *   out, in rank order
  *   (logit descending, lower expert index first on equal logits); topk_w [T][k] fp32 out.
  *   Limits: 1 <= k <= min(E, MX_MAX_TOPK), 1 <= E <= MX_MAX_EXPERTS, H % 32 == 0 (MX_ERR_SHAPE);
  *   x and wr 16-byte aligned (MX_ERR_ALIGN). Logits are fp32 sums of bf16 products; the top-k

@@ -157,12 +157,12 @@ def moe_route_topk(x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None, k
     T, H = x.shape
     E = wr.shape[0]
     dev = x.device
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check(lib().moe_route_topk(_ptr(x), _ptr(wr), _ptr(br), T, H, E, k, _ptr(logits), _ptr(idx),
                                 _ptr(w), _stream(stream)))
-    return logits, idx, w
+    return (logits if want_logits else None), idx, w
 
 
 def moe_permute(topk_idx: torch.Tensor, E: int, stream=None):

@@ -217,7 +217,8 @@ MX_API mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const flo
   if (st != MX_OK) return st;
   if (H % 32) return fail(MX_ERR_SHAPE, "H=%d must be a multiple of 32", H);
   if (T == 0) return ok();
-  if (!x || !wr || !topk_idx || !topk_w) return fail(MX_ERR_NULL, "x, wr, topk_idx and topk_w are required");
+  if (!x || !wr || !logits || !topk_idx || !topk_w)
+    return fail(MX_ERR_NULL, "x, wr, logits, topk_idx and topk_w are required");
   if (!aligned(x, 16) || !aligned(wr, 16)) return fail(MX_ERR_ALIGN, "x and wr must be 16-byte aligned");
   st = check_device();
   if (st != MX_OK) return st;

@@ -27,6 +27,8 @@ namespace mx {
 namespace {
 
 enum { MODE_LINEAR = 0, MODE_GATE_UP = 1, MODE_DOWN = 2 };
+enum { SCM_BYTE = 0, SCM_STAGE = 1, SCM_RESIDENT = 2 };  // how weight scales reach LDS
+constexpr int kResidentNb = 96;  // resident scales hold up to K = 3072 (32-blocks per row)
 
 struct GemmKArgs {
   const uint16_t* A;          // bf16 activation rows of length K
@@ -69,13 +71,15 @@ __device__ __forceinline__ void static_for(Fn&& fn) {
 // patterns were measured conflict-free on gfx950 for exactly that access (SQ_LDS_BANK_CONFLICT
 // = 0 for ds_read_b128 over 16 rows x 4 lane groups; e.g. "r & 15" on 256-byte rows costs 2x):
 //   A rows (KT*64 bytes, >= 16 chunks): swz = ((r & 7) << 1) | ((r >> 3) & 1).
-//   B rows (KT*16 bytes): KT = 4 -> ((r >> 2) ^ (r >> 1)) & 3; KT = 8 -> (r ^ (r >> 3)) & 7.
+//   B rows (KT*16 bytes): KT = 4 -> ((r >> 2) ^ (r >> 1)) & 3; KT = 8 -> (r ^ (r >> 3)) & 7;
+//   KT = 16 -> the A pattern.
 __device__ __forceinline__ int swz_a(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 template <int KT>
 __device__ __forceinline__ int swz_b(int row) {
-  static_assert(KT == 4 || KT == 8, "K tile");
+  static_assert(KT == 4 || KT == 8 || KT == 16, "K tile");
   if constexpr (KT == 4) return ((row >> 2) ^ (row >> 1)) & 3;
-  else return (row ^ (row >> 3)) & 7;
+  else if constexpr (KT == 8) return (row ^ (row >> 3)) & 7;
+  else return swz_a(row);  // 256-byte rows, as the bf16 A rows
 }
 
 // Buffer views. Loads go through buffer resources (base address, byte size): each lane keeps a
@@ -93,8 +97,9 @@ __device__ __forceinline__ i32x4 make_res(const void* base, int64_t bytes) {
                __builtin_amdgcn_readfirstlane(nrec), (int)kBufWord3};
 }
 
-// Direct global -> LDS loads (buffer_load ... lds): lane i writes lds + 16*i (16-byte form) or
-// one byte into the dword at lds + 4*i (byte form); lds must be wave-uniform. They are written as
+// Direct global -> LDS loads (buffer_load ... lds): lane i writes lds + 16*i (16-byte form),
+// lds + 4*i (dword form) or the first byte of the dword at lds + 4*i (byte form); lds must be
+// wave-uniform. They are written as
 // inline asm on purpose: the compiler orders each LDS read after every direct-to-LDS load it
 // cannot prove disjoint, and it does not tell the pipeline's stage buffers apart, so with the
 // builtin every LDS read of the current stage would also wait for the loads in flight into the
@@ -111,6 +116,13 @@ __device__ __forceinline__ void dma_b8(const i32x4& res, uint32_t voff, uint32_t
                                        const void* lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(res), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const i32x4& res, uint32_t voff, uint32_t soff,
+                                        const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :: "v"(voff), "s"(res), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
                : "memory", "m0");
 }
@@ -236,13 +248,24 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc
 
 // Grouped / dense MXFP4 GEMM tile: out[BM rows x BN cols] = A times the weights (decoded).
 //   BM x BN workgroup tile, WM x WN waves, each wave a (BM/WM) x (BN/WN) tile of 16 x 16 MFMA
-//   fragments; KT 32-element blocks per pipeline stage; STAGES (2 or 3) stages in flight.
+//   fragments; KT 32-element blocks per pipeline stage; STAGES (2 to 4) stages in flight.
 //   AFP4 = false: A is bf16 and the weights are decoded to bf16 for v_mfma_f32_16x16x32_bf16.
 //   AFP4 = true:  A is MXFP4 too (packed codes + E8M0 scales, same layout as the weights) and
 //                 each 16 x 16 x 128 slice is one v_mfma_scale_f32_16x16x128_f8f6f4 with both
 //                 operands' block scales, so nothing is decoded.
-// Per stage a workgroup moves A chunks, B chunks and their scale bytes straight into LDS.
-template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4>
+// Per stage a workgroup moves A chunks and B chunks straight into LDS. The weight scale bytes
+// come one of three ways (SCM):
+//   SCM_RESIDENT: all K/32 scale bytes of the tile's rows, once per tile. A tile's rows are one
+//     (two for gate_up) contiguous byte ranges, loaded as the aligned dwords that cover them:
+//     few, coalesced requests, which matters where streaming the weights is the bound.
+//   SCM_STAGE: per stage, each row's KT bytes as the SD = KT/4 + 1 aligned dwords that cover
+//     them (the first byte sits at a fixed shift, as stages advance by KT, a multiple of 4).
+//   SCM_BYTE: per stage, one byte per lane into its own dword (4x the LDS, exact at any size).
+// The dword forms may read past a row's last block (next row, or past K in the last stage):
+// those blocks have zero codes and their scale is read as 1.0. A dword the buffer size cuts
+// reads as zero, so weights whose scale array is not a whole number of dwords take SCM_BYTE.
+// Rows of the tile past its expert's last row are loaded as out-of-range (zeros, no traffic).
+template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4, int SCM>
 __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
@@ -254,17 +277,24 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * B_ROW;
   using PA = DmaPlan<A_STAGE / 1024, NW>;
   using PB = DmaPlan<B_STAGE / 1024, NW>;
-  using PS = DmaPlan<BN * KT / 64, NW>;                    // weight scale bytes
-  using PSA = DmaPlan<AFP4 ? BM * KT / 64 : 1, NW>;         // activation scale bytes
-  constexpr int IA = PA::I, IB = PB::I, IS = PS::I, ISA = AFP4 ? PSA::I : 0;
+  constexpr int SD = KT / 4 + 1;                           // scale dwords per row and stage
+  constexpr int S_DW = SCM == SCM_STAGE ? (BN * SD + 63) / 64 * 64 : SCM == SCM_BYTE ? BN * KT : 64;
+  constexpr int SBS = SCM == SCM_BYTE ? 4 : 1;             // LDS bytes between a row's scales
+  constexpr int SA_DW = (BM * SD + 63) / 64 * 64;          // activation scale dwords
+  // resident scales: region 1 (up rows of gate_up) starts at dword R1; whole instructions
+  constexpr int R1 = (BNH * kResidentNb + 8) / 4;
+  constexpr int RS_DW = ((SWIGLU ? 2 * R1 : (BN * kResidentNb + 8) / 4) + 63) / 64 * 64;
+  using PS = DmaPlan<S_DW / 64, NW>;
+  using PSA = DmaPlan<AFP4 ? SA_DW / 64 : 1, NW>;
+  using PR = DmaPlan<RS_DW / 64, NW>;
+  constexpr int IA = PA::I, IB = PB::I, IS = SCM == SCM_RESIDENT ? 0 : PS::I, ISA = AFP4 ? PSA::I : 0;
   constexpr int SS = KT / 4;                               // super-steps per stage
   constexpr int LPS = IS + ISA + IA + IB;                  // vector-memory ops per wave per stage
   static_assert(A_STAGE % 1024 == 0 && B_STAGE % 1024 == 0, "stage split");
-  static_assert((BN * KT) % 64 == 0 && (!AFP4 || (BM * KT) % 64 == 0), "scale split");
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "wave tile");
   static_assert(!SWIGLU || FN % 2 == 0, "gate/up fragment pairs");
-  static_assert(KT % 4 == 0 && (AFP4 || A_ROW >= 256) && (STAGES == 2 || STAGES == 3), "pipeline");
-  static_assert(2 * LPS < 64, "vmcnt range");
+  static_assert(KT % 4 == 0 && (AFP4 || A_ROW >= 256) && STAGES >= 2 && STAGES <= 4, "pipeline");
+  static_assert((STAGES - 1) * LPS < 64, "vmcnt range");
   static_assert(BM <= NT, "one gathered row per thread");
 
   // One LDS variable per pipeline stage: the compiler orders LDS reads after direct-to-LDS
@@ -273,17 +303,20 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   struct Stage {
     uint8_t A[A_STAGE];
     uint8_t B[B_STAGE];
-    uint32_t Sc[BN * KT];            // weight scale bytes, one per dword
-    uint32_t Sa[AFP4 ? BM * KT : 1];  // activation scale bytes (FP4 A)
+    uint32_t Sc[SCM == SCM_RESIDENT ? 1 : S_DW];  // weight scale bytes of the stage
+    uint32_t Sa[AFP4 ? SA_DW : 1];     // activation scale bytes (FP4 A), same layout
   };
   __shared__ __attribute__((aligned(1024))) Stage st0;
   __shared__ __attribute__((aligned(1024))) Stage st1;
-  __shared__ __attribute__((aligned(1024))) Stage st2;  // referenced only with 3 stages
+  __shared__ __attribute__((aligned(1024))) Stage st2;  // referenced only with >= 3 stages
+  __shared__ __attribute__((aligned(1024))) Stage st3;  // referenced only with 4 stages
+  __shared__ uint32_t sRes[SCM == SCM_RESIDENT ? RS_DW : 1];  // resident weight scales
   __shared__ int sArow[BM];
   auto stage = [&](auto S) -> Stage& {
     if constexpr (decltype(S)::value == 0) return st0;
     else if constexpr (decltype(S)::value == 1) return st1;
-    else return st2;
+    else if constexpr (decltype(S)::value == 2) return st2;
+    else return st3;
   };
 
   int e, r0, row_end, nt;
@@ -300,9 +333,11 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   auto weight_row = [&](int lrow) -> int { return weight_row_of<MODE, BN>(p, nt, lrow); };
   const int64_t rpe = p.b_rows_per_expert;
   const i32x4 rB = make_res(p.Bp + (int64_t)e * rpe * (K >> 1), rpe * (K >> 1));
-  const i32x4 rS = make_res(p.Bs + (int64_t)e * rpe * nb, rpe * nb);
+  const i32x4 rS = make_res(p.Bs, (int64_t)(e + 1) * rpe * nb);  // absolute, 4-aligned offsets
+  const int n_valid = min(BM, row_end - r0);                      // tile rows of this expert
   const i32x4 rA = make_res(p.A, p.a_rows * (AFP4 ? (K >> 1) : K * 2));
-  const i32x4 rSA = make_res(p.Asc, AFP4 ? p.a_rows * nb : 0);
+  // activation scales live in the library's workspace, padded past a whole dword
+  const i32x4 rSA = make_res(p.Asc, AFP4 ? (p.a_rows * nb + 3) / 4 * 4 : 0);
   uint32_t voffB[IB];
   int bblk[IB];
 #pragma unroll
@@ -313,18 +348,52 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     bblk[q] = chunk;
     voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
   }
-  // scale dword idx of a stage's scale area holds (row, block) = (idx / KT, idx % KT)
-  uint32_t voffS[IS];
-  int sblk[IS];
+  // scale dword idx of a stage's scale area is dword idx % SD covering row idx / SD
+  auto row_scale_off = [&](int lrow) -> uint32_t {
+    return ((uint32_t)e * (uint32_t)rpe + (uint32_t)weight_row(lrow)) * (uint32_t)nb;
+  };
+  // (byte mode: dword idx holds block idx % KT of row idx / KT)
+  uint32_t voffS[IS > 0 ? IS : 1];
+  int sblk[IS > 0 ? IS : 1];
 #pragma unroll
   for (int q = 0; q < IS; ++q) {
     const int idx = PS::instr(wave, q) * 64 + lane;
-    sblk[q] = idx % KT;
-    voffS[q] = (uint32_t)weight_row(idx / KT) * (uint32_t)nb + sblk[q];
+    if constexpr (SCM == SCM_STAGE) {
+      sblk[q] = 0;
+      voffS[q] = idx < BN * SD ? (row_scale_off(idx / SD) & ~3u) + 4 * (idx % SD) : kOutOfRange;
+    } else {
+      sblk[q] = idx % KT;
+      voffS[q] = row_scale_off(idx / KT) + sblk[q];
+    }
   }
-  int brow[FN];
+  // resident scales: the tile's rows as one range (two for gate_up: gate rows, then up rows)
+  int rg_rows[2] = {0, 0};
+  uint32_t rg_start[2] = {0u, 0u};
+  if constexpr (SCM == SCM_RESIDENT) {
+    if (SWIGLU) {
+      rg_rows[0] = rg_rows[1] = min(BNH, p.F - nt * BNH);
+      rg_start[0] = row_scale_off(0);
+      rg_start[1] = row_scale_off(BNH);
+    } else {
+      rg_rows[0] = min(BN, p.N - nt * BN);
+      rg_start[0] = row_scale_off(0);
+    }
+  }
+  int brow[FN], bsh[FN];
 #pragma unroll
-  for (int f = 0; f < FN; ++f) brow[f] = frag_row<MODE, BN, WN, FN>(wn, f, ln);
+  for (int f = 0; f < FN; ++f) {
+    brow[f] = frag_row<MODE, BN, WN, FN>(wn, f, ln);
+    // LDS byte of the row's block 0 (of the stage, or of K for resident scales)
+    if constexpr (SCM == SCM_RESIDENT) {
+      const int rg = (SWIGLU && brow[f] >= BNH) ? 1 : 0;
+      const int rr = min(brow[f] - rg * BNH, rg_rows[rg] - 1);
+      bsh[f] = rg * R1 * 4 + (int)(rg_start[rg] & 3u) + rr * nb;
+    } else if constexpr (SCM == SCM_STAGE) {
+      bsh[f] = brow[f] * SD * 4 + (int)(row_scale_off(brow[f]) & 3u);
+    } else {
+      bsh[f] = brow[f] * KT * 4;
+    }
+  }
 
   // ---- activation rows, weight prefetch ----
   // The activation rows of a gathered tile depend on a chain of loads (tile -> perm -> row). The
@@ -337,22 +406,41 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     for (int q = 0; q < BM; ++q) gv[q] = p.a_gather[r0 + q];
   }
   auto issue_w = [&](Stage& sg, int kt) {
-    const bool full = (kt + 1) * KT <= nb;
     const int kb = kt * KT;
 #pragma unroll
     for (int q = 0; q < IS; ++q) {
-      const uint32_t vo = full ? voffS[q] : (kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange);
-      dma_b8(rS, vo, full ? kb : 0, &sg.Sc[PS::instr(wave, q) * 64]);
+      if constexpr (SCM == SCM_STAGE)
+        dma_b32(rS, voffS[q] == kOutOfRange ? kOutOfRange : voffS[q] + kb, 0,
+                &sg.Sc[PS::instr(wave, q) * 64]);
+      else
+        dma_b8(rS, kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange, 0, &sg.Sc[PS::instr(wave, q) * 64]);
     }
+    if ((kt + 1) * KT <= nb) {  // full stage: the K offset goes in the scalar offset
 #pragma unroll
-    for (int q = 0; q < IB; ++q) {
-      const uint32_t vo = full ? voffB[q] : (kb + bblk[q] < nb ? voffB[q] + kb * 16 : kOutOfRange);
-      dma_b128(rB, vo, full ? kb * 16 : 0, &sg.B[PB::instr(wave, q) * 1024]);
+      for (int q = 0; q < IB; ++q) dma_b128(rB, voffB[q], kb * 16, &sg.B[PB::instr(wave, q) * 1024]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < IB; ++q)
+        dma_b128(rB, kb + bblk[q] < nb ? voffB[q] + kb * 16 : kOutOfRange, 0,
+                 &sg.B[PB::instr(wave, q) * 1024]);
     }
   };
   const int ntk = (nb + KT - 1) / KT;
-  issue_w(st0, 0);
-  if (STAGES == 3 && ntk > 1) issue_w(st1, 1);
+  if constexpr (SCM == SCM_RESIDENT) {  // first of all loads: every stage wait covers it
+#pragma unroll
+    for (int q = 0; q < PR::I; ++q) {
+      const int idx = PR::instr(wave, q) * 64 + lane;
+      const int rg = (SWIGLU && idx >= R1) ? 1 : 0;
+      const int d = idx - rg * R1;
+      const uint32_t a0 = rg_start[rg] & ~3u;
+      const uint32_t end = rg_start[rg] + (uint32_t)(rg_rows[rg] * nb);
+      const uint32_t vo = a0 + 4u * (uint32_t)d;
+      dma_b32(rS, (d >= 0 && vo < end) ? vo : kOutOfRange, 0, &sRes[PR::instr(wave, q) * 64]);
+    }
+  }
+  static_for<0, STAGES - 1>([&](auto S) {
+    if (decltype(S)::value < ntk) issue_w(stage(S), decltype(S)::value);
+  });
   if (p.a_gather != nullptr) {  // consumed only now, after the weight loads went out
     int gathered = gv[0];
 #pragma unroll
@@ -377,32 +465,44 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
       ablk[q] = chunk >> 2;
       voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
     }
+    if (lrow >= n_valid) voffA[q] = kOutOfRange;
   }
   uint32_t voffSA[ISA > 0 ? ISA : 1];
-  int sablk[ISA > 0 ? ISA : 1];
 #pragma unroll
   for (int q = 0; q < ISA; ++q) {
     const int idx = PSA::instr(wave, q) * 64 + lane;
-    sablk[q] = idx % KT;
-    voffSA[q] = (uint32_t)sArow[idx / KT] * (uint32_t)nb + sablk[q];
+    voffSA[q] = idx < n_valid * SD
+                    ? (((uint32_t)sArow[idx / SD] * (uint32_t)nb) & ~3u) + 4 * (idx % SD)
+                    : kOutOfRange;
+  }
+  int ash[AFP4 ? FM : 1];  // FP4 A: byte of block 0 of each fragment row's scales
+#pragma unroll
+  for (int i = 0; i < (AFP4 ? FM : 0); ++i) {
+    const int r = wm * TM + i * 16 + ln;
+    ash[i] = r * SD * 4 + (int)(((uint32_t)sArow[r] * (uint32_t)nb) & 3u);
   }
   auto issue_a = [&](Stage& sg, int kt) {
-    const bool full = (kt + 1) * KT <= nb;
     const int kb = kt * KT;
 #pragma unroll
-    for (int q = 0; q < ISA; ++q) {
-      const uint32_t vo = full ? voffSA[q] : (kb + sablk[q] < nb ? voffSA[q] + kb : kOutOfRange);
-      dma_b8(rSA, vo, full ? kb : 0, &sg.Sa[PSA::instr(wave, q) * 64]);
-    }
+    for (int q = 0; q < ISA; ++q)
+      dma_b32(rSA, voffSA[q] == kOutOfRange ? kOutOfRange : voffSA[q] + kb, 0,
+              &sg.Sa[PSA::instr(wave, q) * 64]);
     constexpr int A_KB = AFP4 ? 16 : 64;  // bytes of A per 32-element block
+    if ((kt + 1) * KT <= nb) {
 #pragma unroll
-    for (int q = 0; q < IA; ++q) {
-      const uint32_t vo = full ? voffA[q] : (kb + ablk[q] < nb ? voffA[q] + kb * A_KB : kOutOfRange);
-      dma_b128(rA, vo, full ? kb * A_KB : 0, &sg.A[PA::instr(wave, q) * 1024]);
+      for (int q = 0; q < IA; ++q)
+        dma_b128(rA, voffA[q] == kOutOfRange ? kOutOfRange : voffA[q] + kb * A_KB, 0,
+                 &sg.A[PA::instr(wave, q) * 1024]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < IA; ++q)
+        dma_b128(rA, (voffA[q] != kOutOfRange && kb + ablk[q] < nb) ? voffA[q] + kb * A_KB : kOutOfRange,
+                 0, &sg.A[PA::instr(wave, q) * 1024]);
     }
   };
-  issue_a(st0, 0);
-  if (STAGES == 3 && ntk > 1) issue_a(st1, 1);
+  static_for<0, STAGES - 1>([&](auto S) {
+    if (decltype(S)::value < ntk) issue_a(stage(S), decltype(S)::value);
+  });
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -414,19 +514,23 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   //   bf16 A: per super-step, read the wave's A fragments and packed B blocks; decode B fragment
   //   f+1 (two codes per cvt, other register set) while the 4 x FM MFMAs of fragment f run.
   //   FP4 A: per super-step and fragment pair, one scaled MFMA on the raw blocks and scale bytes.
-  auto compute = [&](const Stage& sg) {
+  auto compute = [&](const Stage& sg, int kt) {
     const uint8_t* As = sg.A;
     const uint8_t* Bsm = sg.B;
-    const uint32_t* Sc = sg.Sc;
+    const uint8_t* Scb = SCM == SCM_RESIDENT ? reinterpret_cast<const uint8_t*>(sRes) + kt * KT
+                                             : reinterpret_cast<const uint8_t*>(sg.Sc);
+    const uint8_t* Sab = reinterpret_cast<const uint8_t*>(sg.Sa);
+    const bool partial = (kt + 1) * KT > nb;  // blocks past K: zero codes, scale read as 1.0
 #pragma unroll
     for (int j = 0; j < SS; ++j) {
+      const bool past = partial && kt * KT + 4 * j + g >= nb;
       u32x4 w[FN];
       uint32_t scb[FN];
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
         const int r = brow[f];
         w[f] = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-        scb[f] = Sc[r * KT + 4 * j + g];
+        scb[f] = past ? 127u : (uint32_t)Scb[bsh[f] + (4 * j + g) * SBS];
       }
       if constexpr (AFP4) {
         u32x4 a[FM];
@@ -435,7 +539,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
         for (int i = 0; i < FM; ++i) {
           const int r = wm * TM + i * 16 + ln;
           a[i] = lds_read_b128(As + r * A_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-          sca[i] = sg.Sa[r * KT + 4 * j + g];
+          sca[i] = past ? 127u : (uint32_t)Sab[ash[i] + 4 * j + g];
         }
 #pragma unroll
         for (int f = 0; f < FN; ++f)
@@ -454,7 +558,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
         }
         float sc[FN];
 #pragma unroll
-        for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f] & 0xffu);
+        for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f]);
         bf16x8 b[2][4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
@@ -474,26 +578,36 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   };
 
   // Pipeline: stage kt+STAGES-1 is issued in iteration kt, weights and activations of a stage
-  // back to back (LPS vector-memory ops per wave). At iteration kt the loads of stage kt must
-  // have landed; with 3 stages those of stage kt+1 may still be in flight. The prologue issued
-  // [weights 0][weights 1][activations 0][activations 1], so at iteration 0 only the
-  // activations of stage 1 may stay outstanding. The loop is unrolled by STAGES so that every
-  // stage buffer is named statically.
+  // back to back (LPS vector-memory ops per wave). The prologue issued the weights of stages
+  // 0..STAGES-2, then their activations (LA ops each). At iteration kt the loads of stage kt must
+  // have landed; outstanding(kt) counts the loads issued after its last one, which may stay in
+  // flight (loads retire in issue order). The wait takes the largest fixed count not above it.
+  // The loop is unrolled by STAGES so that every stage buffer is named statically.
+  constexpr int LA = ISA + IA;
+  auto outstanding = [&](int kt) -> int {
+    const int P = min(STAGES - 1, ntk);
+    if (kt < P) return (P - 1 - kt) * LA + max(0, min(kt, ntk - STAGES + 1)) * LPS;
+    return max(0, min(STAGES - 2, ntk - kt - 1)) * LPS;
+  };
+  auto wait_stage = [&](int kt) {
+    const int n = outstanding(kt);
+    if (STAGES >= 4 && n >= 2 * LPS) wait_vmcnt<(STAGES >= 4 ? 2 * LPS : 0)>();
+    else if (STAGES >= 4 && n >= LA + LPS) wait_vmcnt<(STAGES >= 4 ? LA + LPS : 0)>();
+    else if (STAGES >= 3 && n >= LPS) wait_vmcnt<(STAGES >= 3 ? LPS : 0)>();
+    else if (STAGES >= 4 && n >= 2 * LA) wait_vmcnt<(STAGES >= 4 ? 2 * LA : 0)>();
+    else if (STAGES >= 3 && n >= LA) wait_vmcnt<(STAGES >= 3 ? LA : 0)>();
+    else wait_vmcnt<0>();
+  };
   auto step = [&](auto S, int kt) {
     constexpr int s = decltype(S)::value;
-    if (STAGES == 3 && kt + 1 < ntk) {
-      if (kt == 0) wait_vmcnt<ISA + IA>();
-      else wait_vmcnt<LPS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    wait_stage(kt);
     barrier_lds();
     if (kt + STAGES - 1 < ntk) {
       Stage& sn = stage(IntC<(s + STAGES - 1) % STAGES>{});
       issue_w(sn, kt + STAGES - 1);
       issue_a(sn, kt + STAGES - 1);
     }
-    compute(stage(S));
+    compute(stage(S), kt);
   };
   int kt0 = 0;
   for (; kt0 + STAGES <= ntk; kt0 += STAGES)
@@ -506,17 +620,17 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 }
 
 // One kernel name per role, so profiles show which product a launch is.
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4, SCM>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_down_weighted_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4, SCM>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM>(p);
 }
 // out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
 // indices) contribute nothing.
@@ -547,21 +661,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // ---- tile configurations ----
 // Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles with a 2-stage pipeline, so
 // two workgroups fit in a CU's LDS and one's tile prologue / epilogue overlaps the other's MFMAs.
-// gate_up: four waves of 64 x 64; down: eight waves of 32 x 64 (measured best for each).
-// Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, 8 blocks per
-// stage and 2 stages; weight streaming dominates (best of the 16-row shapes measured with the
-// weights rotated through copies larger than the last-level cache).
+// Both: four waves of 64 x 64 (measured best).
+// Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, the tile's
+// weight scales resident; gate_up 8 blocks x 2 stages, down 4 blocks x 3 stages. Weight
+// streaming dominates (best of the 16-row shapes measured with the weights rotated through
+// copies larger than the last-level cache).
 // OCC: workgroups per CU the register allocation must leave room for (the second launch bound
 // is in waves per SIMD).
-struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2; };
-struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 2, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2; };
-struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 8, ST = 2, GM = 1, OCC = 2; };
-struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 8, ST = 2, GM = 1, OCC = 2; };
+// SCM: how the weight scales reach LDS (resident per tile where weight streaming is the bound).
+struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2, SCM = SCM_STAGE; };
+struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2, SCM = SCM_STAGE; };
+struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 8, ST = 2, GM = 1, OCC = 2, SCM = SCM_RESIDENT; };
+struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 2, SCM = SCM_RESIDENT; };
 constexpr int kPrefillRows = 64;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
 static_assert(kPrefillRows <= kMaxTileRows, "perm padding");
 
-template <class C, int MODE, bool AFP4 = false>
+template <class C, int MODE, bool AFP4 = false, int SCM = C::SCM>
 hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream) {
   const int n_tiles = (MODE == MODE_GATE_UP) ? (n_cols + C::BN / 2 - 1) / (C::BN / 2)
                                              : (n_cols + C::BN - 1) / C::BN;
@@ -572,12 +688,29 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
   const int64_t supers = (int64_t)((m_tiles + C::GM - 1) / C::GM) * ((n_tiles + GN - 1) / GN);
   const dim3 grid((unsigned)(8 * 32 * ((supers + 7) / 8))), block(C::WM * C::WN * 64);
   if constexpr (MODE == MODE_GATE_UP)
-    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM>), grid, block, 0, stream, a);
   else if constexpr (MODE == MODE_DOWN)
-    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM>), grid, block, 0, stream, a);
   return hipGetLastError();
+}
+
+// Dense linear: 64-row tiles above 64 rows, else 16-row tiles. Weight scales are read as whole
+// dwords unless the scale array (N * K/32 bytes) is not a whole number of dwords.
+template <bool AFP4>
+hipError_t launch_linear_tiles(const GemmKArgs& g, int M, int N, hipStream_t stream) {
+  const int nb = g.K >> 5;
+  const bool dw = ((int64_t)N * nb) % 4 == 0;
+  if (M > 64) {
+    const int mt = (M + CfgPreGU::BM - 1) / CfgPreGU::BM;
+    return dw ? launch_gemm<CfgPreGU, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
+              : launch_gemm<CfgPreGU, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
+  }
+  const int mt = (M + CfgDecDn::BM - 1) / CfgDecDn::BM;
+  if (dw && nb <= kResidentNb) return launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_RESIDENT>(g, mt, N, stream);
+  return dw ? launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
+            : launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
 }
 
 bool use_prefill_tiles(int T, int k, int E) { return (int64_t)T * k >= 48LL * E; }
@@ -688,8 +821,7 @@ hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
   g.F = N;
   g.out = y;
   g.out_bf16 = y_bf16 ? 1 : 0;
-  if (M > 64) return launch_gemm<CfgPreGU, MODE_LINEAR>(g, (M + CfgPreGU::BM - 1) / CfgPreGU::BM, N, stream);
-  return launch_gemm<CfgDecDn, MODE_LINEAR>(g, (M + CfgDecDn::BM - 1) / CfgDecDn::BM, N, stream);
+  return launch_linear_tiles<false>(g, M, N, stream);
 }
 
 hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int K,
@@ -710,8 +842,7 @@ hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int
   g.F = N;
   g.out = y;
   g.out_bf16 = y_bf16 ? 1 : 0;
-  if (M > 64) return launch_gemm<CfgPreGU, MODE_LINEAR, true>(g, (M + CfgPreGU::BM - 1) / CfgPreGU::BM, N, stream);
-  return launch_gemm<CfgDecDn, MODE_LINEAR, true>(g, (M + CfgDecDn::BM - 1) / CfgDecDn::BM, N, stream);
+  return launch_linear_tiles<true>(g, M, N, stream);
 }
 
 hipError_t gemm_init() { return hipSuccess; }

@@ -20,7 +20,7 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
 
 // permute.hip: tiles/num_tiles may be NULL (tile_rows ignored then). With a tile list, perm must
 // hold P + tile_rows entries: the padding (and rows past the last valid pair) are set to pair 0.
-constexpr int kMaxTileRows = 64;
+constexpr int kMaxTileRows = 128;
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm,
                           int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
                           int32_t* num_tiles, hipStream_t stream);

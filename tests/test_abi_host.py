@@ -69,6 +69,7 @@ def test_route_and_permute_argument_errors(L):
     assert L.moe_route_topk(p, p, None, 4, 64, 32, 9, p, p, p, None) == mx.MX_ERR_SHAPE  # k > 8
     assert L.moe_route_topk(p, p, None, 4, 48, 32, 4, p, p, p, None) == mx.MX_ERR_SHAPE  # H % 32
     assert L.moe_route_topk(p, None, None, 4, 64, 32, 4, p, p, p, None) == mx.MX_ERR_NULL
+    assert L.moe_route_topk(p, p, None, 4, 64, 32, 4, None, p, p, None) == mx.MX_ERR_NULL  # logits
     assert L.moe_route_topk(p, p, None, 0, 64, 32, 4, p, p, p, None) == mx.MX_OK  # T = 0
     assert L.moe_permute(p, 4, 2, 8, None, p, p, None, None) == mx.MX_ERR_NULL
     assert L.moe_permute(p, 4, 0, 8, p, p, p, None, None) == mx.MX_ERR_SHAPE

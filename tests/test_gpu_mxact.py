@@ -32,7 +32,7 @@ def _linear_case(M, K, N, seed, out_dtype):
     return y, oracle.linear(x, p, s, mx_act=True)
 
 
-@pytest.mark.parametrize("M,N", [(1, 16), (37, 200), (130, 96)])
+@pytest.mark.parametrize("M,N", [(1, 16), (37, 200), (130, 96), (5, 17), (90, 7)])
 def test_linear_mxact_single_block_is_exact(M, N):
     """K = 32: one block per dot product, so every partial sum of the FP4 x FP4 products (codes
     with two significant bits, one shared pair of power-of-two scales) is exact in fp32 and the
@@ -51,7 +51,7 @@ def test_linear_mxact_decode_sweep(M):
 
 
 @pytest.mark.parametrize("M,K,N", [(17, 96, 200), (5, 64, 48), (100, 2880, 300), (130, 320, 130),
-                                   (3, 8192, 64), (257, 2880, 96)])
+                                   (3, 8192, 64), (257, 2880, 96), (9, 96, 33), (100, 160, 7)])
 def test_linear_mxact_ragged(M, K, N):
     y, ref = _linear_case(M, K, N, 7 + M, torch.float32)
     check_tolerance(to_f64(y), ref, "linear mx-act %dx%dx%d" % (M, K, N))
