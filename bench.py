@@ -383,16 +383,24 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
     ck = max(copy_k, key=lambda k: fetch[k])
     f_fetch = copy_bytes / (fetch[ck] * 1024.0)
     f_write = copy_bytes / (write[ck] * 1024.0)
-    kinds = {"moe_gate_up_swiglu": "moe_gate_up_swiglu_kernel", "moe_down_weighted":
-             "moe_down_weighted_kernel", "moe_combine": "combine_kernel", "route_topk":
-             "route_topk_kernel", "permute": "permute_kernel", "linear": "linear_kernel"}
+    # kind -> kernel symbols of one launch of it (the router is two kernels)
+    kinds = {"moe_gate_up_swiglu": ["moe_gate_up_swiglu_kernel"],
+             "moe_down_weighted": ["moe_down_weighted_kernel"], "moe_combine": ["combine_kernel"],
+             "route_topk": ["route_logits_kernel", "route_select_kernel"],
+             "permute": ["permute_kernel"], "linear": ["linear_kernel"]}
     out = {}
-    for kind, sym in kinds.items():
-        ks = [k for k in fetch if sym in k]
-        if not ks:
+    for kind, syms in kinds.items():
+        fk = wk = 0.0
+        found = False
+        for sym in syms:
+            ks = [k for k in fetch if sym in k]
+            if not ks:
+                continue
+            found = True
+            fk += sum(fetch[k] for k in ks) / len(ks)
+            wk += sum(write.get(k, 0.0) for k in ks) / len(ks)
+        if not found:
             continue
-        fk = sum(fetch[k] for k in ks) / len(ks)
-        wk = sum(write.get(k, 0.0) for k in ks) / len(ks)
         out[kind] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
                      "hbm_bytes_per_launch": int(fk * 1024 * f_fetch + wk * 1024 * f_write),
                      "copy_scale_fetch": round(f_fetch, 4), "copy_scale_write": round(f_write, 4),
