@@ -54,18 +54,6 @@ struct GemmKArgs {
   const float* rw;            // down: routing weight of each pair
 };
 
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-template <int B, int E, typename Fn>
-__device__ __forceinline__ void static_for(Fn&& fn) {
-  if constexpr (B < E) {
-    fn(IntC<B>{});
-    static_for<B + 1, E>(fn);
-  }
-}
-
 // LDS swizzles. A 16-byte chunk c of LDS row r is stored at slot c ^ swz(r). The per-lane
 // 16-byte reads of one MFMA operand cover 16 consecutive rows at the same chunk; these XOR
 // patterns were measured conflict-free on gfx950 for exactly that access (SQ_LDS_BANK_CONFLICT
@@ -97,6 +85,12 @@ __device__ __forceinline__ i32x4 make_res(const void* base, int64_t bytes) {
                __builtin_amdgcn_readfirstlane(nrec), (int)kBufWord3};
 }
 
+// LDS offset of a pointer into a __shared__ object: the low 32 bits of its generic address (the
+// shared aperture base has zero low bits), without the null check of an address-space cast.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
 // Direct global -> LDS loads (buffer_load ... lds): lane i writes lds + 16*i (16-byte form),
 // lds + 4*i (dword form) or the first byte of the dword at lds + 4*i (byte form); lds must be
 // wave-uniform. They are written as
@@ -107,21 +101,21 @@ __device__ __forceinline__ i32x4 make_res(const void* base, int64_t bytes) {
 // before reading what they wrote. The s_nop covers the M0-write -> LDS-DMA hazard.
 __device__ __forceinline__ void dma_b128(const i32x4& res, uint32_t voff, uint32_t soff,
                                          const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :: "v"(voff), "s"(res), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma_b8(const i32x4& res, uint32_t voff, uint32_t soff,
                                        const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_ubyte %0, %1, %2 offen lds"
                :: "v"(voff), "s"(res), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma_b32(const i32x4& res, uint32_t voff, uint32_t soff,
                                         const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
                :: "v"(voff), "s"(res), "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(m0)
                : "memory", "m0");
@@ -278,7 +272,9 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   using PA = DmaPlan<A_STAGE / 1024, NW>;
   using PB = DmaPlan<B_STAGE / 1024, NW>;
   constexpr int SD = KT / 4 + 1;                           // scale dwords per row and stage
-  constexpr int S_DW = SCM == SCM_STAGE ? (BN * SD + 63) / 64 * 64 : SCM == SCM_BYTE ? BN * KT : 64;
+  // (stage scale dwords padded to a whole number of instructions per wave: no repeated loads)
+  constexpr int S_DW = SCM == SCM_STAGE ? (BN * SD + 64 * NW - 1) / (64 * NW) * (64 * NW)
+                                        : SCM == SCM_BYTE ? BN * KT : 64;
   constexpr int SBS = SCM == SCM_BYTE ? 4 : 1;             // LDS bytes between a row's scales
   constexpr int SA_DW = (BM * SD + 63) / 64 * 64;          // activation scale dwords
   // resident scales: region 1 (up rows of gate_up) starts at dword R1; whole instructions
@@ -297,27 +293,19 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   static_assert((STAGES - 1) * LPS < 64, "vmcnt range");
   static_assert(BM <= NT, "one gathered row per thread");
 
-  // One LDS variable per pipeline stage: the compiler orders LDS reads after direct-to-LDS
-  // loads by variable, so reads of stage s must not share a variable with the loads in flight
-  // into the other stages (else it waits for all of them before every read).
-  struct Stage {
+  // The pipeline stages. The direct loads that fill them are inline asm the compiler does not
+  // see, so it neither orders LDS reads after them nor tracks them: the kernel waits itself.
+  // 1 KiB-aligned elements: the swizzles and 16-byte reads assume every stage starts on one.
+  struct __attribute__((aligned(1024))) Stage {
     uint8_t A[A_STAGE];
     uint8_t B[B_STAGE];
     uint32_t Sc[SCM == SCM_RESIDENT ? 1 : S_DW];  // weight scale bytes of the stage
     uint32_t Sa[AFP4 ? SA_DW : 1];     // activation scale bytes (FP4 A), same layout
   };
-  __shared__ __attribute__((aligned(1024))) Stage st0;
-  __shared__ __attribute__((aligned(1024))) Stage st1;
-  __shared__ __attribute__((aligned(1024))) Stage st2;  // referenced only with >= 3 stages
-  __shared__ __attribute__((aligned(1024))) Stage st3;  // referenced only with 4 stages
+  static_assert(sizeof(Stage) % 1024 == 0, "stage alignment");
+  __shared__ Stage stg[STAGES];
   __shared__ uint32_t sRes[SCM == SCM_RESIDENT ? RS_DW : 1];  // resident weight scales
   __shared__ int sArow[BM];
-  auto stage = [&](auto S) -> Stage& {
-    if constexpr (decltype(S)::value == 0) return st0;
-    else if constexpr (decltype(S)::value == 1) return st1;
-    else if constexpr (decltype(S)::value == 2) return st2;
-    else return st3;
-  };
 
   int e, r0, row_end, nt;
   if (!pick_tile<BM, GM>(p, e, r0, row_end, nt)) return;
@@ -438,9 +426,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
       dma_b32(rS, (d >= 0 && vo < end) ? vo : kOutOfRange, 0, &sRes[PR::instr(wave, q) * 64]);
     }
   }
-  static_for<0, STAGES - 1>([&](auto S) {
-    if (decltype(S)::value < ntk) issue_w(stage(S), decltype(S)::value);
-  });
+  for (int q = 0; q < STAGES - 1 && q < ntk; ++q) issue_w(stg[q], q);
   if (p.a_gather != nullptr) {  // consumed only now, after the weight loads went out
     int gathered = gv[0];
 #pragma unroll
@@ -500,9 +486,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
                  0, &sg.A[PA::instr(wave, q) * 1024]);
     }
   };
-  static_for<0, STAGES - 1>([&](auto S) {
-    if (decltype(S)::value < ntk) issue_a(stage(S), decltype(S)::value);
-  });
+  for (int q = 0; q < STAGES - 1 && q < ntk; ++q) issue_a(stg[q], q);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -582,7 +566,6 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   // 0..STAGES-2, then their activations (LA ops each). At iteration kt the loads of stage kt must
   // have landed; outstanding(kt) counts the loads issued after its last one, which may stay in
   // flight (loads retire in issue order). The wait takes the largest fixed count not above it.
-  // The loop is unrolled by STAGES so that every stage buffer is named statically.
   constexpr int LA = ISA + IA;
   auto outstanding = [&](int kt) -> int {
     const int P = min(STAGES - 1, ntk);
@@ -598,23 +581,18 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     else if (STAGES >= 3 && n >= LA) wait_vmcnt<(STAGES >= 3 ? LA : 0)>();
     else wait_vmcnt<0>();
   };
-  auto step = [&](auto S, int kt) {
-    constexpr int s = decltype(S)::value;
+  int st = 0;
+  for (int kt = 0; kt < ntk; ++kt) {
     wait_stage(kt);
     barrier_lds();
     if (kt + STAGES - 1 < ntk) {
-      Stage& sn = stage(IntC<(s + STAGES - 1) % STAGES>{});
+      Stage& sn = stg[st == 0 ? STAGES - 1 : st - 1];
       issue_w(sn, kt + STAGES - 1);
       issue_a(sn, kt + STAGES - 1);
     }
-    compute(stage(S), kt);
-  };
-  int kt0 = 0;
-  for (; kt0 + STAGES <= ntk; kt0 += STAGES)
-    static_for<0, STAGES>([&](auto S) { step(S, kt0 + decltype(S)::value); });
-  static_for<0, STAGES - 1>([&](auto S) {
-    if (kt0 + decltype(S)::value < ntk) step(S, kt0 + decltype(S)::value);
-  });
+    compute(stg[st], kt);
+    st = st == STAGES - 1 ? 0 : st + 1;
+  }
 
   store_tile<MODE, FM, FN, TM, BN, WN>(p, acc, r0, row_end, nt, wm, wn, g, ln);
 }
@@ -659,9 +637,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // ---- tile configurations ----
-// Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles with a 2-stage pipeline, so
-// two workgroups fit in a CU's LDS and one's tile prologue / epilogue overlaps the other's MFMAs.
-// Both: four waves of 64 x 64 (measured best).
+// Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles, four waves of 64 x 64, a
+// 2-stage pipeline of 4-block stages, two workgroups per CU so that one's barrier waits and tile
+// prologue overlap the other's MFMAs. Measured on the 20B prefill shapes: 128 x 256 (eight
+// waves, 2 or 3 stages) about 10% slower and 128 x 384 about 3% slower, both one workgroup per
+// CU whose eight waves stall at the same barriers.
 // Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, the tile's
 // weight scales resident; gate_up 8 blocks x 2 stages, down 4 blocks x 3 stages. Weight
 // streaming dominates (best of the 16-row shapes measured with the weights rotated through
@@ -713,7 +693,7 @@ hipError_t launch_linear_tiles(const GemmKArgs& g, int M, int N, hipStream_t str
             : launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
 }
 
-bool use_prefill_tiles(int T, int k, int E) { return (int64_t)T * k >= 48LL * E; }
+bool use_prefill_tiles(int T, int k, int E) { return (int64_t)T * k >= 64LL * E; }
 
 GemmKArgs gate_up_args(const MoeGemmArgs& m) {
   // A = x rows gathered through perm / k, B = W_gu[e] (2F rows), out = h [P][F]

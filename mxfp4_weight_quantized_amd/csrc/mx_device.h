@@ -13,8 +13,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 // ---------------------------------------------------------------------------------------------
 // Scalar helpers
 // ---------------------------------------------------------------------------------------------
