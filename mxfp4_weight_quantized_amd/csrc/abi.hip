@@ -127,7 +127,7 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
     return o;
   };
   const size_t T = (size_t)d.T, P = (size_t)d.T * d.k, E = (size_t)d.E;
-  L.tile_rows = mx::moe_tile_rows(d.T, d.k, d.E);
+  L.tile_rows = mx::moe_tile_rows(d.T, d.k, d.E, (d.flags & MX_ACT_MXFP4) != 0);
   L.max_tiles = mx::moe_max_tiles(d.T, d.k, d.E, L.tile_rows);
   L.status = take(256);  // int32 status, int32 tile count
   L.logits = take(T * E * 4);

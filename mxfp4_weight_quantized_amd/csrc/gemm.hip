@@ -653,9 +653,17 @@ struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4
 struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2, SCM = SCM_STAGE; };
 struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 8, ST = 2, GM = 1, OCC = 2, SCM = SCM_RESIDENT; };
 struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 2, SCM = SCM_RESIDENT; };
-constexpr int kPrefillRows = 64;
+// Activation variant, prefill-shaped: FP4 activations take a quarter of the LDS and need no
+// decode instructions, so wide tiles with fewer bytes per MFMA pay: 128 x 512 (gate_up, eight
+// waves of 64 x 128) and 128 x 384 (down: 2880 columns split into 7.5 rather than 5.6 tiles),
+// 3 stages. Measured on the 20B prefill shapes against 64 x 256 (about 15% slower), 128 x 256,
+// 128 x 384 with 2 or 4 stages and 8-block stages (spills).
+struct CfgPreGU4 { static constexpr int BM = 128, BN = 512, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE; };
+struct CfgPreDn4 { static constexpr int BM = 128, BN = 384, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE; };
+constexpr int kPrefillRows = 64, kPrefillRows4 = 128;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
-static_assert(kPrefillRows <= kMaxTileRows, "perm padding");
+static_assert(CfgPreGU4::BM == kPrefillRows4 && CfgPreDn4::BM == kPrefillRows4, "one tile list");
+static_assert(kPrefillRows <= kMaxTileRows && kPrefillRows4 <= kMaxTileRows, "perm padding");
 
 template <class C, int MODE, bool AFP4 = false, int SCM = C::SCM>
 hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream) {
@@ -676,16 +684,17 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
   return hipGetLastError();
 }
 
-// Dense linear: 64-row tiles above 64 rows, else 16-row tiles. Weight scales are read as whole
+// Dense linear: prefill tiles above 64 rows, else 16-row tiles. Weight scales are read as whole
 // dwords unless the scale array (N * K/32 bytes) is not a whole number of dwords.
 template <bool AFP4>
 hipError_t launch_linear_tiles(const GemmKArgs& g, int M, int N, hipStream_t stream) {
   const int nb = g.K >> 5;
   const bool dw = ((int64_t)N * nb) % 4 == 0;
   if (M > 64) {
-    const int mt = (M + CfgPreGU::BM - 1) / CfgPreGU::BM;
-    return dw ? launch_gemm<CfgPreGU, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
-              : launch_gemm<CfgPreGU, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
+    using C = std::conditional_t<AFP4, CfgPreGU4, CfgPreGU>;
+    const int mt = (M + C::BM - 1) / C::BM;
+    return dw ? launch_gemm<C, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
+              : launch_gemm<C, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
   }
   const int mt = (M + CfgDecDn::BM - 1) / CfgDecDn::BM;
   if (dw && nb <= kResidentNb) return launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_RESIDENT>(g, mt, N, stream);
@@ -741,7 +750,9 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
 
 }  // namespace
 
-int moe_tile_rows(int T, int k, int E) { return use_prefill_tiles(T, k, E) ? kPrefillRows : 16; }
+int moe_tile_rows(int T, int k, int E, bool mx_act) {
+  return use_prefill_tiles(T, k, E) ? (mx_act ? kPrefillRows4 : kPrefillRows) : 16;
+}
 
 int moe_max_tiles(int T, int k, int E, int tile_rows) {
   return (int)(((int64_t)T * k + tile_rows - 1) / tile_rows) + E;
@@ -753,7 +764,7 @@ hipError_t launch_moe_gate_up(const MoeGemmArgs& m, hipStream_t stream) {
   if (m.mx_act) {
     g.A = reinterpret_cast<const uint16_t*>(m.xq);  // packed codes, addressed in bytes
     g.Asc = m.xqs;
-    if (pre) return launch_gemm<CfgPreGU, MODE_GATE_UP, true>(g, m.max_tiles, m.F, stream);
+    if (pre) return launch_gemm<CfgPreGU4, MODE_GATE_UP, true>(g, m.max_tiles, m.F, stream);
     return launch_gemm<CfgDecGU, MODE_GATE_UP, true>(g, m.max_tiles, m.F, stream);
   }
   if (pre) return launch_gemm<CfgPreGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
@@ -766,7 +777,7 @@ hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
   if (m.mx_act) {
     d.A = reinterpret_cast<const uint16_t*>(m.hq);
     d.Asc = m.hqs;
-    if (pre) return launch_gemm<CfgPreDn, MODE_DOWN, true>(d, m.max_tiles, m.H, stream);
+    if (pre) return launch_gemm<CfgPreDn4, MODE_DOWN, true>(d, m.max_tiles, m.H, stream);
     return launch_gemm<CfgDecDn, MODE_DOWN, true>(d, m.max_tiles, m.H, stream);
   }
   if (pre) return launch_gemm<CfgPreDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);

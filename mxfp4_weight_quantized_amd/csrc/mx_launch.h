@@ -46,7 +46,7 @@ struct MoeGemmArgs {
   uint8_t *xq, *xqs, *hq, *hqs;
 };
 // Tile rows (BM) the grouped GEMMs use for this problem; the permutation's tile list must match.
-int moe_tile_rows(int T, int k, int E);
+int moe_tile_rows(int T, int k, int E, bool mx_act);
 int moe_max_tiles(int T, int k, int E, int tile_rows);
 hipError_t launch_moe_gate_up(const MoeGemmArgs& a, hipStream_t stream);
 hipError_t launch_moe_down(const MoeGemmArgs& a, hipStream_t stream);
