@@ -159,6 +159,13 @@ def bench_moe(args, name, shape, flags):
     s = shape
     want_cpu = not args.no_cpu_baseline
     weights, wr_np, br_np, host_w = setup_moe(s, flags, want_cpu)
+    tiled = not args.row_major_weights
+    if tiled:  # the kernels' weight layout, converted once (weights are static)
+        gp, gs, dp, ds = weights
+        weights = (*mx.mxfp4_tile_weights(gp, gs), *mx.mxfp4_tile_weights(dp, ds))
+        del gp, gs, dp, ds
+        torch.cuda.synchronize()
+    desc_flags = flags | (mx.MX_WEIGHTS_TILED if tiled else 0)
     wr = _upload_bf16(wr_np)
     br = torch.from_numpy(br_np).cuda() if br_np is not None else None
     layer_bytes = s.E * (2 * s.F * s.H + s.H * s.F) * 17 // 32
@@ -183,7 +190,7 @@ def bench_moe(args, name, shape, flags):
     for i in range(max(n_x, n_w)):
         gp, gs, dp, ds = wsets[i % n_w]
         descs.append(mx.make_moe_desc(xs[i % n_x], gp, gs, dp, ds, s.k, out, wr=wr, br=br,
-                                      flags=flags))
+                                      flags=desc_flags))
     ws_bytes = max(mx.mxfp4_moe_mlp_workspace(d) for d in descs)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     L = mx.lib()
@@ -240,7 +247,9 @@ def bench_moe(args, name, shape, flags):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp4" if flags else "bf16", "data": "synthetic",
         "config": {"workload": name, "T": s.T, "H": s.H, "F": s.F, "E": s.E, "k": s.k,
-                   "weights": "mxfp4 (e2m1 + e8m0 per 32)", "activations": "mxfp4" if flags else "bf16",
+                   "weights": "mxfp4 (e2m1 + e8m0 per 32)",
+                   "weight_layout": "tiled (converted once at load)" if tiled else "row-major",
+                   "activations": "mxfp4" if flags else "bf16",
                    "out_dtype": "bf16", "router_bias_std": s.bias_std, "seed": s.seed,
                    "parallelism": "single-gpu", "weight_copies": n_w, "token_batches": n_x},
         "step": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
@@ -436,6 +445,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--row-major-weights", action="store_true",
+                    help="feed the grouped GEMMs row-major weights instead of the tiled layout")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for counter scaling)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))

@@ -60,6 +60,8 @@ typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
 /* Activation variant: the GEMM A-operands (x along H, and the bf16 SwiGLU output h along F) are
  * themselves MXFP4-quantized with the rule above and multiplied on the scaled FP4 matrix cores. */
 #define MX_ACT_MXFP4 0x1u
+/* The expert weights of mxfp4_moe_mlp are in the tiled layout written by mxfp4_tile_weights. */
+#define MX_WEIGHTS_TILED 0x2u
 
 /* Upper limits checked on the host. */
 #define MX_MAX_EXPERTS 256
@@ -87,6 +89,21 @@ mx_status mxfp4_quantize(const void* src, mx_dtype src_dtype, int64_t rows, int6
  * ---------------------------------------------------------------------------------------------- */
 mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K,
                            void* dst, mx_dtype dst_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * mxfp4_tile_weights -- rearrange G packed matrices [R][K] into the layout in which the grouped
+ * GEMMs of mxfp4_moe_mlp (flag MX_WEIGHTS_TILED) read every weight stage as whole cache lines.
+ * Weights are static, so this runs once, when they are loaded. A pure permutation of bytes:
+ *   packed [G][R][K/2], scales [G][R][K/32] in (the layout above);
+ *   packed_t [G][R/16][K/32][16][16] out: the 16 code bytes of block b of rows 16q..16q+15 as
+ *     one 256-byte run, row r at byte 16*(r % 16);
+ *   scales_t [G][K/32][R] out: the scale byte of (row r, block b) at b*R + r.
+ *   R % 16 == 0, K % 32 == 0 (MX_ERR_SHAPE); packed and packed_t 16-byte aligned (MX_ERR_ALIGN);
+ *   outputs must not overlap the inputs. Buffers are owned by the caller.
+ * For the MoE weights: gate_up G = E, R = 2F, K = H; down G = E, R = H, K = F.
+ * ---------------------------------------------------------------------------------------------- */
+mx_status mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t G, int64_t R,
+                             int64_t K, uint8_t* packed_t, uint8_t* scales_t, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * moe_route_topk -- router logits, top-k expert selection and softmax over the k selected
@@ -128,17 +145,17 @@ mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, 
 typedef struct mx_moe_desc {
   size_t struct_size;          /* sizeof(mx_moe_desc); other values -> MX_ERR_UNSUPPORTED */
   int32_t T, H, F, E, k;       /* tokens, hidden, expert FFN width, experts, experts per token */
-  uint32_t flags;              /* 0 or MX_ACT_MXFP4 */
+  uint32_t flags;              /* MX_ACT_MXFP4 and/or MX_WEIGHTS_TILED, or 0 */
   mx_dtype out_dtype;          /* dtype of `out` */
   const uint16_t* x;           /* [T][H] bf16 */
   const uint16_t* wr;          /* [E][H] bf16 router weight; unused if topk_idx_in is given */
   const float* br;             /* [E] fp32 router bias, NULL = none */
   const int32_t* topk_idx_in;  /* [T][k] caller routing, NULL = route internally */
   const float* topk_w_in;      /* [T][k] caller routing weights (required with topk_idx_in) */
-  const uint8_t* gu_packed;    /* [E][2F][H/2] */
-  const uint8_t* gu_scales;    /* [E][2F][H/32] */
-  const uint8_t* dn_packed;    /* [E][H][F/2] */
-  const uint8_t* dn_scales;    /* [E][H][F/32] */
+  const uint8_t* gu_packed;    /* [E][2F][H/2] (MX_WEIGHTS_TILED: mxfp4_tile_weights layout) */
+  const uint8_t* gu_scales;    /* [E][2F][H/32] (tiled: [E][H/32][2F]) */
+  const uint8_t* dn_packed;    /* [E][H][F/2] (tiled: mxfp4_tile_weights layout) */
+  const uint8_t* dn_scales;    /* [E][H][F/32] (tiled: [E][F/32][H]) */
   void* out;                   /* [T][H] out_dtype */
   int32_t* topk_idx_out;       /* [T][k], NULL = not stored (internal routing only) */
   float* topk_w_out;           /* [T][k], NULL = not stored */

@@ -21,6 +21,7 @@ MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_DTYPE = 0, 1, 2, 3, 4
 MX_ERR_WORKSPACE, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 5, 6, 7
 MX_F32, MX_BF16 = 0, 1
 MX_ACT_MXFP4 = 0x1
+MX_WEIGHTS_TILED = 0x2
 STATUS_NAMES = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
                 4: "MX_ERR_DTYPE", 5: "MX_ERR_WORKSPACE", 6: "MX_ERR_UNSUPPORTED", 7: "MX_ERR_HIP"}
 
@@ -63,6 +64,7 @@ _VP, _I32, _I64, _U32, _SZ, _INT = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_in
 SIGNATURES = {
     "mxfp4_quantize": (_INT, [_VP, _INT, _I64, _I64, _VP, _VP, _VP]),
     "mxfp4_dequantize": (_INT, [_VP, _VP, _I64, _I64, _VP, _INT, _VP]),
+    "mxfp4_tile_weights": (_INT, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP]),
     "moe_route_topk": (_INT, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
     "moe_permute": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "mxfp4_moe_mlp_workspace": (_SZ, [ctypes.POINTER(MoeDesc)]),
@@ -151,6 +153,18 @@ def mxfp4_dequantize(packed: torch.Tensor, scales: torch.Tensor, dtype=torch.flo
     return out
 
 
+def mxfp4_tile_weights(packed: torch.Tensor, scales: torch.Tensor, stream=None):
+    """packed [G, R, K/2], scales [G, R, K/32] (or [R, K/2], [R, K/32]) -> (packed_t, scales_t)
+    of the same shapes holding the bytes in the tiled layout of the grouped GEMMs (pass
+    MX_WEIGHTS_TILED in the MoE flags to use them)."""
+    G = packed.shape[0] if packed.dim() == 3 else 1
+    R, K = packed.shape[-2], packed.shape[-1] * 2
+    packed_t, scales_t = torch.empty_like(packed), torch.empty_like(scales)
+    _check(lib().mxfp4_tile_weights(_ptr(packed), _ptr(scales), G, R, K, _ptr(packed_t),
+                                    _ptr(scales_t), _stream(stream)))
+    return packed_t, scales_t
+
+
 def moe_route_topk(x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None, k: int,
                    want_logits: bool = True, stream=None):
     """x [T, H] bf16, wr [E, H] bf16, br [E] fp32 or None -> (logits, topk_idx, topk_w)."""
@@ -206,7 +220,8 @@ def mxfp4_moe_mlp(x, gu_packed, gu_scales, dn_packed, dn_scales, k, wr=None, br=
                   topk_idx=None, topk_w=None, out_dtype=torch.bfloat16, flags=0, out=None,
                   workspace=None, return_routing=False, stream=None):
     """The whole MoE MLP. Weights: gu_packed [E, 2F, H/2], gu_scales [E, 2F, H/32],
-    dn_packed [E, H, F/2], dn_scales [E, H, F/32]. Routing: internal from (wr, br) unless
+    dn_packed [E, H, F/2], dn_scales [E, H, F/32] (with MX_WEIGHTS_TILED in flags: the same
+    shapes as written by mxfp4_tile_weights). Routing: internal from (wr, br) unless
     (topk_idx, topk_w) are given. Returns out [T, H] (and (logits, idx, w) if asked)."""
     T, H = x.shape
     dev = x.device

@@ -63,10 +63,10 @@ mx_status check_device() {
 
 // ---- opt-in per-kernel timing (benchmarks): HIP events on the caller's stream ----
 enum ProfKind { PK_QUANTIZE, PK_DEQUANTIZE, PK_ROUTE, PK_PERMUTE, PK_GATE_UP, PK_DOWN, PK_COMBINE,
-                PK_LINEAR, PK_COUNT };
+                PK_LINEAR, PK_TILE, PK_COUNT };
 const char* const kProfNames[PK_COUNT] = {"quantize", "dequantize", "route_topk", "permute",
                                           "moe_gate_up_swiglu", "moe_down_weighted", "moe_combine",
-                                          "linear"};
+                                          "linear", "tile_weights"};
 struct ProfRec {
   int kind;
   hipEvent_t a, b;
@@ -166,7 +166,7 @@ mx_status check_moe_desc(const mx_moe_desc* d) {
   if (d->H > MX_MAX_MOE_DIM || d->F > MX_MAX_MOE_DIM) return fail(MX_ERR_SHAPE, "H and F must be <= %d in the MoE MLP", MX_MAX_MOE_DIM);
   if ((int64_t)d->T * d->H * 2 >= (1LL << 31) || (int64_t)d->T * d->k * d->F * 2 >= (1LL << 31))
     return fail(MX_ERR_SHAPE, "T*H and T*k*F bf16 activations must stay below 2 GiB");
-  if (d->flags & ~MX_ACT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(MX_ACT_MXFP4 | MX_WEIGHTS_TILED)) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
   if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "out_dtype %d", (int)d->out_dtype);
   if (d->T == 0) return MX_OK;
   if (!d->x || !d->gu_packed || !d->gu_scales || !d->dn_packed || !d->dn_scales || !d->out)
@@ -208,6 +208,22 @@ MX_API mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, 
   ProfScope ps(PK_DEQUANTIZE, (hipStream_t)stream);
   hipError_t e = mx::launch_dequantize(packed, scales, rows * (K / 32), dst, dst_dtype == MX_BF16, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "dequantize launch");
+}
+
+MX_API mx_status mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t G,
+                                    int64_t R, int64_t K, uint8_t* packed_t, uint8_t* scales_t,
+                                    void* stream) {
+  if (G < 0 || R < 0 || K < 0 || R % 16 || K % 32 || R > INT32_MAX || K > INT32_MAX)
+    return fail(MX_ERR_SHAPE, "G=%lld R=%lld K=%lld (R a multiple of 16, K of 32)", (long long)G,
+                (long long)R, (long long)K);
+  if (G == 0 || R == 0 || K == 0) return ok();
+  if (!packed || !scales || !packed_t || !scales_t) return fail(MX_ERR_NULL, "packed, scales, packed_t and scales_t are required");
+  if (!aligned(packed, 16) || !aligned(packed_t, 16)) return fail(MX_ERR_ALIGN, "packed and packed_t must be 16-byte aligned");
+  mx_status st = check_device();
+  if (st != MX_OK) return st;
+  ProfScope ps(PK_TILE, (hipStream_t)stream);
+  hipError_t e = mx::launch_tile_weights(packed, scales, G, (int)R, (int)K, packed_t, scales_t, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "tile_weights launch");
 }
 
 MX_API mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int32_t T,
@@ -298,6 +314,7 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   mx::MoeGemmArgs g{};
   g.T = d.T; g.H = d.H; g.F = d.F; g.E = d.E; g.k = d.k;
   g.mx_act = mx_act;
+  g.tiled = (d.flags & MX_WEIGHTS_TILED) != 0;
   g.xq = reinterpret_cast<uint8_t*>(w + L.xq);
   g.xqs = reinterpret_cast<uint8_t*>(w + L.xqs);
   g.hq = reinterpret_cast<uint8_t*>(w + L.hq);

@@ -144,6 +144,31 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
 
 inline unsigned grid_for(int64_t nblocks) { return (unsigned)((nblocks * 8 + 255) / 256); }
 
+// Tiled weight layout of G matrices [R][K] (R % 16 == 0): codes [G][R/16][K/32][16][16 bytes]
+// (the 16-byte block b of rows 16q..16q+15 as one 256-byte run), scales [G][K/32][R]. One thread
+// per 16-byte code block, in source order (coalesced reads, 16-byte scattered writes).
+__global__ __launch_bounds__(256) void tile_codes_kernel(const uint4* __restrict__ src, int64_t rows,
+                                                         int nb, int R, uint4* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (matrix row, block)
+  if (i >= rows * nb) return;
+  const int64_t row = i / nb;                                   // over all G * R rows
+  const int b = (int)(i - row * nb);
+  const int64_t g = row / R;
+  const int r = (int)(row - g * R);
+  dst[((g * (R >> 4) + (r >> 4)) * nb + b) * 16 + (r & 15)] = src[i];
+}
+// One thread per scale byte, in destination order (coalesced writes).
+__global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restrict__ src, int64_t rows,
+                                                          int nb, int R, uint8_t* __restrict__ dst) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (matrix, block, row)
+  if (o >= rows * nb) return;
+  const int64_t gb = o / R;
+  const int r = (int)(o - gb * R);
+  const int64_t g = gb / nb;
+  const int b = (int)(gb - g * nb);
+  dst[o] = src[(g * R + r) * nb + b];
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8_t* packed,
@@ -155,6 +180,19 @@ hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8
   else
     hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid_for(nblocks)), dim3(256), 0, stream, src,
                        nblocks, packed, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t G, int R,
+                               int K, uint8_t* packed_t, uint8_t* scales_t, hipStream_t stream) {
+  const int64_t rows = G * R;
+  const int nb = K >> 5;
+  if (rows == 0 || nb == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((rows * nb + 255) / 256);
+  hipLaunchKernelGGL(tile_codes_kernel, dim3(grid), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(packed), rows, nb, R, reinterpret_cast<uint4*>(packed_t));
+  hipLaunchKernelGGL(tile_scales_kernel, dim3(grid), dim3(256), 0, stream, scales, rows, nb, R,
+                     scales_t);
   return hipGetLastError();
 }
 

@@ -259,7 +259,8 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc
 // those blocks have zero codes and their scale is read as 1.0. A dword the buffer size cuts
 // reads as zero, so weights whose scale array is not a whole number of dwords take SCM_BYTE.
 // Rows of the tile past its expert's last row are loaded as out-of-range (zeros, no traffic).
-template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4, int SCM>
+template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4, int SCM,
+          bool TW>
 __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
@@ -273,13 +274,15 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   using PB = DmaPlan<B_STAGE / 1024, NW>;
   constexpr int SD = KT / 4 + 1;                           // scale dwords per row and stage
   // (stage scale dwords padded to a whole number of instructions per wave: no repeated loads)
-  constexpr int S_DW = SCM == SCM_STAGE ? (BN * SD + 64 * NW - 1) / (64 * NW) * (64 * NW)
+  constexpr int S_DW = SCM == SCM_STAGE ? ((TW ? KT * BN / 4 : BN * SD) + 64 * NW - 1) / (64 * NW) * (64 * NW)
                                         : SCM == SCM_BYTE ? BN * KT : 64;
-  constexpr int SBS = SCM == SCM_BYTE ? 4 : 1;             // LDS bytes between a row's scales
+  // LDS bytes between a row's consecutive block scales (tiled weights: [block][row] bytes)
+  constexpr int SBS = TW ? BN : SCM == SCM_BYTE ? 4 : 1;
+  constexpr int B_KB = TW ? 256 : 16;                      // weight bytes between blocks of a row
   constexpr int SA_DW = (BM * SD + 63) / 64 * 64;          // activation scale dwords
   // resident scales: region 1 (up rows of gate_up) starts at dword R1; whole instructions
   constexpr int R1 = (BNH * kResidentNb + 8) / 4;
-  constexpr int RS_DW = ((SWIGLU ? 2 * R1 : (BN * kResidentNb + 8) / 4) + 63) / 64 * 64;
+  constexpr int RS_DW = ((TW ? kResidentNb * BN / 4 : SWIGLU ? 2 * R1 : (BN * kResidentNb + 8) / 4) + 63) / 64 * 64;
   using PS = DmaPlan<S_DW / 64, NW>;
   using PSA = DmaPlan<AFP4 ? SA_DW / 64 : 1, NW>;
   using PR = DmaPlan<RS_DW / 64, NW>;
@@ -292,6 +295,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   static_assert(KT % 4 == 0 && (AFP4 || A_ROW >= 256) && STAGES >= 2 && STAGES <= 4, "pipeline");
   static_assert((STAGES - 1) * LPS < 64, "vmcnt range");
   static_assert(BM <= NT, "one gathered row per thread");
+  static_assert(!TW || (SCM != SCM_BYTE && BNH % 16 == 0), "tiled weights: dword scales, row groups");
 
   // The pipeline stages. The direct loads that fill them are inline asm the compiler does not
   // see, so it neither orders LDS reads after them nor tracks them: the kernel waits itself.
@@ -319,6 +323,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 
   // ---- weight rows (within the expert) ----
   auto weight_row = [&](int lrow) -> int { return weight_row_of<MODE, BN>(p, nt, lrow); };
+  // Tiled weights: tile rows map to whole 16-row groups; rows past the matrix are not clamped
+  // (gate rows past F read up rows, rows past the end are out of range: zeros, dropped).
+  auto weight_row_u = [&](int lrow) -> int {
+    if constexpr (SWIGLU) return lrow < BNH ? nt * BNH + lrow : p.F + nt * BNH + lrow - BNH;
+    else return nt * BN + lrow;
+  };
   const int64_t rpe = p.b_rows_per_expert;
   const i32x4 rB = make_res(p.Bp + (int64_t)e * rpe * (K >> 1), rpe * (K >> 1));
   const i32x4 rS = make_res(p.Bs, (int64_t)(e + 1) * rpe * nb);  // absolute, 4-aligned offsets
@@ -334,7 +344,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     const int lrow = off / B_ROW;
     const int chunk = ((off % B_ROW) >> 4) ^ swz_b<KT>(lrow);
     bblk[q] = chunk;
-    voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
+    if constexpr (TW) {  // 16-row group gr/16, block chunk: 256 bytes, row gr%16 at 16 * (gr%16)
+      const uint32_t gr = (uint32_t)weight_row_u(lrow);
+      voffB[q] = (gr >> 4) * (uint32_t)(nb * 256) + (gr & 15u) * 16u + chunk * 256;
+    } else {
+      voffB[q] = (uint32_t)weight_row(lrow) * (uint32_t)(K >> 1) + chunk * 16;
+    }
   }
   // scale dword idx of a stage's scale area is dword idx % SD covering row idx / SD
   auto row_scale_off = [&](int lrow) -> uint32_t {
@@ -346,7 +361,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
   for (int q = 0; q < IS; ++q) {
     const int idx = PS::instr(wave, q) * 64 + lane;
-    if constexpr (SCM == SCM_STAGE) {
+    if constexpr (TW) {  // dword idx of [KT][BN]: rows 4*idx % BN .. +3 of block 4*idx / BN
+      sblk[q] = 4 * idx / BN;
+      voffS[q] = idx < KT * BN / 4
+                     ? (uint32_t)(e * nb + sblk[q]) * (uint32_t)rpe + (uint32_t)weight_row_u(4 * idx % BN)
+                     : kOutOfRange;
+    } else if constexpr (SCM == SCM_STAGE) {
       sblk[q] = 0;
       voffS[q] = idx < BN * SD ? (row_scale_off(idx / SD) & ~3u) + 4 * (idx % SD) : kOutOfRange;
     } else {
@@ -357,7 +377,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   // resident scales: the tile's rows as one range (two for gate_up: gate rows, then up rows)
   int rg_rows[2] = {0, 0};
   uint32_t rg_start[2] = {0u, 0u};
-  if constexpr (SCM == SCM_RESIDENT) {
+  if constexpr (SCM == SCM_RESIDENT && !TW) {
     if (SWIGLU) {
       rg_rows[0] = rg_rows[1] = min(BNH, p.F - nt * BNH);
       rg_start[0] = row_scale_off(0);
@@ -372,7 +392,9 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   for (int f = 0; f < FN; ++f) {
     brow[f] = frag_row<MODE, BN, WN, FN>(wn, f, ln);
     // LDS byte of the row's block 0 (of the stage, or of K for resident scales)
-    if constexpr (SCM == SCM_RESIDENT) {
+    if constexpr (TW) {
+      bsh[f] = brow[f];
+    } else if constexpr (SCM == SCM_RESIDENT) {
       const int rg = (SWIGLU && brow[f] >= BNH) ? 1 : 0;
       const int rr = min(brow[f] - rg * BNH, rg_rows[rg] - 1);
       bsh[f] = rg * R1 * 4 + (int)(rg_start[rg] & 3u) + rr * nb;
@@ -397,7 +419,10 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     const int kb = kt * KT;
 #pragma unroll
     for (int q = 0; q < IS; ++q) {
-      if constexpr (SCM == SCM_STAGE)
+      if constexpr (TW)
+        dma_b32(rS, (voffS[q] != kOutOfRange && kb + sblk[q] < nb) ? voffS[q] + (uint32_t)(kb * rpe) : kOutOfRange,
+                0, &sg.Sc[PS::instr(wave, q) * 64]);
+      else if constexpr (SCM == SCM_STAGE)
         dma_b32(rS, voffS[q] == kOutOfRange ? kOutOfRange : voffS[q] + kb, 0,
                 &sg.Sc[PS::instr(wave, q) * 64]);
       else
@@ -405,11 +430,11 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     }
     if ((kt + 1) * KT <= nb) {  // full stage: the K offset goes in the scalar offset
 #pragma unroll
-      for (int q = 0; q < IB; ++q) dma_b128(rB, voffB[q], kb * 16, &sg.B[PB::instr(wave, q) * 1024]);
+      for (int q = 0; q < IB; ++q) dma_b128(rB, voffB[q], kb * B_KB, &sg.B[PB::instr(wave, q) * 1024]);
     } else {
 #pragma unroll
       for (int q = 0; q < IB; ++q)
-        dma_b128(rB, kb + bblk[q] < nb ? voffB[q] + kb * 16 : kOutOfRange, 0,
+        dma_b128(rB, kb + bblk[q] < nb ? voffB[q] + kb * B_KB : kOutOfRange, 0,
                  &sg.B[PB::instr(wave, q) * 1024]);
     }
   };
@@ -418,6 +443,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
     for (int q = 0; q < PR::I; ++q) {
       const int idx = PR::instr(wave, q) * 64 + lane;
+      if constexpr (TW) {  // [block][row] bytes of the tile, blocks below nb
+        const int blk = 4 * idx / BN;
+        const uint32_t vo = (uint32_t)(e * nb + blk) * (uint32_t)rpe + (uint32_t)weight_row_u(4 * idx % BN);
+        dma_b32(rS, blk < nb ? vo : kOutOfRange, 0, &sRes[PR::instr(wave, q) * 64]);
+        continue;
+      }
       const int rg = (SWIGLU && idx >= R1) ? 1 : 0;
       const int d = idx - rg * R1;
       const uint32_t a0 = rg_start[rg] & ~3u;
@@ -501,7 +532,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   auto compute = [&](const Stage& sg, int kt) {
     const uint8_t* As = sg.A;
     const uint8_t* Bsm = sg.B;
-    const uint8_t* Scb = SCM == SCM_RESIDENT ? reinterpret_cast<const uint8_t*>(sRes) + kt * KT
+    const uint8_t* Scb = SCM == SCM_RESIDENT ? reinterpret_cast<const uint8_t*>(sRes) + kt * KT * SBS
                                              : reinterpret_cast<const uint8_t*>(sg.Sc);
     const uint8_t* Sab = reinterpret_cast<const uint8_t*>(sg.Sa);
     const bool partial = (kt + 1) * KT > nb;  // blocks past K: zero codes, scale read as 1.0
@@ -598,17 +629,17 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 }
 
 // One kernel name per role, so profiles show which product a launch is.
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM, bool TW>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4, SCM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4, SCM, TW>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM, bool TW>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_down_weighted_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4, SCM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4, SCM, TW>(p);
 }
 template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM, false>(p);
 }
 // out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
 // indices) contribute nothing.
@@ -665,7 +696,7 @@ static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one
 static_assert(CfgPreGU4::BM == kPrefillRows4 && CfgPreDn4::BM == kPrefillRows4, "one tile list");
 static_assert(kPrefillRows <= kMaxTileRows && kPrefillRows4 <= kMaxTileRows, "perm padding");
 
-template <class C, int MODE, bool AFP4 = false, int SCM = C::SCM>
+template <class C, int MODE, bool AFP4 = false, int SCM = C::SCM, bool TW = false>
 hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream) {
   const int n_tiles = (MODE == MODE_GATE_UP) ? (n_cols + C::BN / 2 - 1) / (C::BN / 2)
                                              : (n_cols + C::BN - 1) / C::BN;
@@ -676,9 +707,9 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
   const int64_t supers = (int64_t)((m_tiles + C::GM - 1) / C::GM) * ((n_tiles + GN - 1) / GN);
   const dim3 grid((unsigned)(8 * 32 * ((supers + 7) / 8))), block(C::WM * C::WN * 64);
   if constexpr (MODE == MODE_GATE_UP)
-    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, TW>), grid, block, 0, stream, a);
   else if constexpr (MODE == MODE_DOWN)
-    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, TW>), grid, block, 0, stream, a);
   else
     hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM>), grid, block, 0, stream, a);
   return hipGetLastError();
@@ -758,30 +789,45 @@ int moe_max_tiles(int T, int k, int E, int tile_rows) {
   return (int)(((int64_t)T * k + tile_rows - 1) / tile_rows) + E;
 }
 
-hipError_t launch_moe_gate_up(const MoeGemmArgs& m, hipStream_t stream) {
-  GemmKArgs g = gate_up_args(m);
+namespace {
+template <class C, int MODE, bool AFP4, bool TW>
+hipError_t launch_moe_gemm(const GemmKArgs& g, int m_tiles, int n_cols, hipStream_t stream) {
+  return launch_gemm<C, MODE, AFP4, C::SCM, TW>(g, m_tiles, n_cols, stream);
+}
+template <bool TW>
+hipError_t gate_up_tw(GemmKArgs g, const MoeGemmArgs& m, hipStream_t stream) {
   const bool pre = use_prefill_tiles(m.T, m.k, m.E);
   if (m.mx_act) {
     g.A = reinterpret_cast<const uint16_t*>(m.xq);  // packed codes, addressed in bytes
     g.Asc = m.xqs;
-    if (pre) return launch_gemm<CfgPreGU4, MODE_GATE_UP, true>(g, m.max_tiles, m.F, stream);
-    return launch_gemm<CfgDecGU, MODE_GATE_UP, true>(g, m.max_tiles, m.F, stream);
+    if (pre) return launch_moe_gemm<CfgPreGU4, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);
+    return launch_moe_gemm<CfgDecGU, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);
   }
-  if (pre) return launch_gemm<CfgPreGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
-  return launch_gemm<CfgDecGU, MODE_GATE_UP>(g, m.max_tiles, m.F, stream);
+  if (pre) return launch_moe_gemm<CfgPreGU, MODE_GATE_UP, false, TW>(g, m.max_tiles, m.F, stream);
+  return launch_moe_gemm<CfgDecGU, MODE_GATE_UP, false, TW>(g, m.max_tiles, m.F, stream);
 }
-
-hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
-  GemmKArgs d = down_args(m);
+template <bool TW>
+hipError_t down_tw(GemmKArgs d, const MoeGemmArgs& m, hipStream_t stream) {
   const bool pre = use_prefill_tiles(m.T, m.k, m.E);
   if (m.mx_act) {
     d.A = reinterpret_cast<const uint16_t*>(m.hq);
     d.Asc = m.hqs;
-    if (pre) return launch_gemm<CfgPreDn4, MODE_DOWN, true>(d, m.max_tiles, m.H, stream);
-    return launch_gemm<CfgDecDn, MODE_DOWN, true>(d, m.max_tiles, m.H, stream);
+    if (pre) return launch_moe_gemm<CfgPreDn4, MODE_DOWN, true, TW>(d, m.max_tiles, m.H, stream);
+    return launch_moe_gemm<CfgDecDn, MODE_DOWN, true, TW>(d, m.max_tiles, m.H, stream);
   }
-  if (pre) return launch_gemm<CfgPreDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
-  return launch_gemm<CfgDecDn, MODE_DOWN>(d, m.max_tiles, m.H, stream);
+  if (pre) return launch_moe_gemm<CfgPreDn, MODE_DOWN, false, TW>(d, m.max_tiles, m.H, stream);
+  return launch_moe_gemm<CfgDecDn, MODE_DOWN, false, TW>(d, m.max_tiles, m.H, stream);
+}
+}  // namespace
+
+hipError_t launch_moe_gate_up(const MoeGemmArgs& m, hipStream_t stream) {
+  const GemmKArgs g = gate_up_args(m);
+  return m.tiled ? gate_up_tw<true>(g, m, stream) : gate_up_tw<false>(g, m, stream);
+}
+
+hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
+  const GemmKArgs d = down_args(m);
+  return m.tiled ? down_tw<true>(d, m, stream) : down_tw<false>(d, m, stream);
 }
 
 hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {

@@ -12,6 +12,9 @@ hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8
                            uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t nblocks,
                              void* dst, bool bf16_out, hipStream_t stream);
+// G matrices [R][K] (R % 16 == 0, K % 32 == 0) into the tiled layout of the grouped GEMMs.
+hipError_t launch_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t G, int R,
+                               int K, uint8_t* packed_t, uint8_t* scales_t, hipStream_t stream);
 
 // route.hip
 hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
@@ -44,6 +47,8 @@ struct MoeGemmArgs {
   // activation variant: x and h MXFP4-quantized (packed [rows][K/2], scales [rows][K/32])
   bool mx_act;
   uint8_t *xq, *xqs, *hq, *hqs;
+  // expert weights in the tiled layout (codes [E][R/16][K/32][16][16], scales [E][K/32][R])
+  bool tiled;
 };
 // Tile rows (BM) the grouped GEMMs use for this problem; the permutation's tile list must match.
 int moe_tile_rows(int T, int k, int E, bool mx_act);

@@ -62,6 +62,17 @@ def test_quantize_argument_errors(L):
     assert L.mxfp4_dequantize(p, p, 0, 64, p, mx.MX_BF16, None) == mx.MX_OK
 
 
+def test_tile_weights_argument_errors(L):
+    p = _fake()
+    assert L.mxfp4_tile_weights(p, p, 2, 24, 64, p, p, None) == mx.MX_ERR_SHAPE  # R % 16
+    assert L.mxfp4_tile_weights(p, p, 2, 32, 48, p, p, None) == mx.MX_ERR_SHAPE  # K % 32
+    assert L.mxfp4_tile_weights(p, p, -1, 32, 64, p, p, None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_tile_weights(p, None, 2, 32, 64, p, p, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_tile_weights(p, p, 2, 32, 64, p, None, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_tile_weights(ctypes.c_void_p(0x10000008), p, 2, 32, 64, p, p, None) == mx.MX_ERR_ALIGN
+    assert L.mxfp4_tile_weights(p, p, 0, 32, 64, p, p, None) == mx.MX_OK  # empty: no-op
+
+
 def test_route_and_permute_argument_errors(L):
     p = _fake()
     assert L.moe_route_topk(p, p, None, 4, 64, 8, 9, p, p, p, None) == mx.MX_ERR_SHAPE  # k > E
@@ -104,6 +115,9 @@ def test_moe_workspace_query_and_errors(L):
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(H=48)), _fake(), 1 << 30, None) == mx.MX_ERR_SHAPE
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(k=9)), _fake(), 1 << 30, None) == mx.MX_ERR_SHAPE
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(flags=4)), _fake(), 1 << 30, None) == mx.MX_ERR_UNSUPPORTED
+    for fl in (mx.MX_WEIGHTS_TILED, mx.MX_WEIGHTS_TILED | mx.MX_ACT_MXFP4):  # accepted flags
+        assert L.mxfp4_moe_mlp(ctypes.byref(_desc(flags=fl, x=0)), _fake(), 1 << 30,
+                               None) == mx.MX_ERR_NULL
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(out_dtype=5)), _fake(), 1 << 30, None) == mx.MX_ERR_DTYPE
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(x=0)), _fake(), 1 << 30, None) == mx.MX_ERR_NULL
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(x=0x10000002)), _fake(), 1 << 30, None) == mx.MX_ERR_ALIGN

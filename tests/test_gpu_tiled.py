@@ -1,0 +1,130 @@
+"""GPU: the tiled weight layout (mxfp4_tile_weights) and the grouped GEMMs that read it.
+
+The layout is a byte permutation; it is checked bit-exactly against the same permutation written
+with numpy reshapes. On tiled weights the MoE MLP performs the same arithmetic in the same order
+as on row-major weights (only the addresses the weight stages come from differ), so its output
+must equal the row-major output bit for bit, for the bf16 path and the activation variant, on the
+decode-shaped and the prefill-shaped tile paths. The 20B and 120B shapes are also checked
+against the oracle directly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_weight_quantized_amd import inputs
+import mxfp4_weight_quantized_amd as mx
+from parity_util import (check_tolerance, moe_weights, moe_weights_dev, note, to_dev, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+TILED = mx.MX_WEIGHTS_TILED
+
+
+def _np_tile(packed, scales):
+    """codes [G][R][K/2] -> [G][R/16][K/32][16 rows][16 bytes]; scales [G][R][K/32] -> [G][K/32][R]
+    (returned with the input shapes, as the binding does)."""
+    G, R, Kh = packed.shape
+    nb = scales.shape[2]
+    pt = packed.reshape(G, R // 16, 16, nb, 16).transpose(0, 1, 3, 2, 4)
+    st = scales.transpose(0, 2, 1)
+    return np.ascontiguousarray(pt).reshape(G, R, Kh), np.ascontiguousarray(st).reshape(G, R, nb)
+
+
+@pytest.mark.parametrize("G,R,K", [(1, 16, 32), (3, 32, 64), (4, 192, 96), (2, 256, 2880),
+                                   (5, 48, 320)])
+def test_tile_weights_is_the_documented_permutation(G, R, K):
+    r = np.random.default_rng(G * 1000 + R + K)
+    packed = r.integers(0, 256, size=(G, R, K // 2), dtype=np.uint8)
+    scales = r.integers(0, 256, size=(G, R, K // 32), dtype=np.uint8)
+    note("tile_weights G=%d R=%d K=%d" % (G, R, K))
+    pt, st = mx.mxfp4_tile_weights(to_dev(packed), to_dev(scales))
+    torch.cuda.synchronize()
+    ept, est = _np_tile(packed, scales)
+    np.testing.assert_array_equal(pt.cpu().numpy(), ept)
+    np.testing.assert_array_equal(st.cpu().numpy(), est)
+
+
+def _tiled(wdev):
+    gp, gs, dp, ds = wdev
+    return (*mx.mxfp4_tile_weights(gp, gs), *mx.mxfp4_tile_weights(dp, ds))
+
+
+def _routing(T, E, k, seed):
+    r = np.random.default_rng(seed)
+    idx = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = r.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    return idx, w
+
+
+# decode-shaped tiles (T*k < 64E) and prefill-shaped tiles (T*k >= 64E), F below one tile too
+@pytest.mark.parametrize("T,H,F,E,k", [(1, 64, 64, 1, 1), (37, 256, 192, 8, 2), (7, 96, 320, 4, 4),
+                                       (513, 64, 128, 4, 2), (300, 128, 96, 4, 4),
+                                       (600, 256, 320, 2, 1)])
+@pytest.mark.parametrize("flags", [0, mx.MX_ACT_MXFP4])
+def test_moe_tiled_equals_row_major(T, H, F, E, k, flags):
+    seed = 300 + T
+    x = to_dev(inputs.activations(seed, T, H))
+    wd = moe_weights_dev(seed, E, H, F)
+    idx, w = _routing(T, E, k, seed)
+    idx_d, w_d = to_dev(idx), to_dev(w)
+    note("moe tiled vs row-major T=%d H=%d F=%d E=%d k=%d flags=%d" % (T, H, F, E, k, flags))
+    a = mx.mxfp4_moe_mlp(x, *wd, k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32,
+                         flags=flags)
+    b = mx.mxfp4_moe_mlp(x, *_tiled(wd), k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32,
+                         flags=flags | TILED)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("flags", [0, mx.MX_ACT_MXFP4])
+def test_moe_tiled_equals_row_major_20b_prefill(flags):
+    s = inputs.MOE_20B_PREFILL
+    x = to_dev(inputs.activations(s.seed, s.T, s.H))
+    wr, br = inputs.router(s.seed, s.E, s.H, s.bias_std)
+    wd = moe_weights_dev(s.seed, s.E, s.H, s.F)
+    note("moe tiled vs row-major %s flags=%d" % (s.name, flags))
+    kw = dict(wr=to_dev(wr), br=to_dev(br) if s.bias_std else None, out_dtype=torch.bfloat16)
+    a = mx.mxfp4_moe_mlp(x, *wd, s.k, flags=flags, **kw)
+    b = mx.mxfp4_moe_mlp(x, *_tiled(wd), s.k, flags=flags | TILED, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def _full_tiled(shape, n_sample):
+    s = shape
+    x = inputs.activations(s.seed, s.T, s.H)
+    wr, br = inputs.router(s.seed, s.E, s.H, s.bias_std)
+    wts = moe_weights(s.seed, s.E, s.H, s.F)
+    note("moe tiled full %s" % s.name)
+    out, (lg, idx, w) = mx.mxfp4_moe_mlp(
+        to_dev(x), *_tiled(moe_weights_dev(s.seed, s.E, s.H, s.F)), s.k, wr=to_dev(wr),
+        br=to_dev(br) if s.bias_std else None, out_dtype=torch.float32, flags=TILED,
+        return_routing=True)
+    torch.cuda.synchronize()
+    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    oidx, ow = oracle.topk_softmax(lg, s.k)
+    np.testing.assert_array_equal(idx, oidx)
+    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
+    r = np.random.default_rng(s.seed + 7)
+    busiest = np.bincount(idx.reshape(-1), minlength=s.E).argmax()
+    on_busiest = np.nonzero((idx == busiest).any(axis=1))[0]
+    toks = np.unique(np.concatenate([r.choice(s.T, size=min(s.T, n_sample), replace=False),
+                                     on_busiest[:4], [0, s.T - 1]])).astype(np.int32)
+    ref = oracle.moe_mlp(x, idx, w, *wts, E=s.E, tokens=toks)
+    return to_f64(out)[toks], ref
+
+
+def test_moe_tiled_20b_prefill_T8192_sampled():
+    got, ref = _full_tiled(inputs.MOE_20B_PREFILL, 24)
+    check_tolerance(got, ref, "20b prefill tiled")
+
+
+def test_moe_tiled_20b_decode_T64_full():
+    got, ref = _full_tiled(inputs.MOE_20B_DECODE, 64)
+    check_tolerance(got, ref, "20b decode tiled")
+
+
+def test_moe_tiled_120b_T4096_sampled():
+    got, ref = _full_tiled(inputs.MOE_120B[4096], 12)
+    check_tolerance(got, ref, "120b T=4096 tiled")
