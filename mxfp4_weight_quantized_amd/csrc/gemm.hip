@@ -674,16 +674,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // waves, 2 or 3 stages) about 10% slower and 128 x 384 about 3% slower, both one workgroup per
 // CU whose eight waves stall at the same barriers.
 // Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, the tile's
-// weight scales resident; gate_up 8 blocks x 2 stages, down 4 blocks x 3 stages. Weight
-// streaming dominates (best of the 16-row shapes measured with the weights rotated through
-// copies larger than the last-level cache).
+// weight scales resident, 4-block stages x 3, three workgroups per CU. Weight streaming
+// dominates and is bound by the loads in flight per CU: more resident workgroups beat deeper or
+// wider stages (measured on the 20B decode shapes, tiled weights rotated through copies larger
+// than the last-level cache: 8-block x 2 stages, 4 stages, 64-column down tiles and per-stage
+// scales all slower).
 // OCC: workgroups per CU the register allocation must leave room for (the second launch bound
 // is in waves per SIMD).
 // SCM: how the weight scales reach LDS (resident per tile where weight streaming is the bound).
 struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2, SCM = SCM_STAGE; };
 struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2, SCM = SCM_STAGE; };
-struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 8, ST = 2, GM = 1, OCC = 2, SCM = SCM_RESIDENT; };
-struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 2, SCM = SCM_RESIDENT; };
+struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT; };
+struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT; };
 // Activation variant, prefill-shaped: FP4 activations take a quarter of the LDS and need no
 // decode instructions, so wide tiles with fewer bytes per MFMA pay: 128 x 512 (gate_up, eight
 // waves of 64 x 128) and 128 x 384 (down: 2880 columns split into 7.5 rather than 5.6 tiles),
