@@ -137,7 +137,7 @@ mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, 
 
 /* ------------------------------------------------------------------------------------------------
  * mxfp4_moe_mlp -- the whole MoE MLP: route -> permute -> gate_up grouped GEMM with fused SwiGLU
- * -> down grouped GEMM scaled by the routing weight -> combine over the k experts. The grouped
+ * -> down grouped GEMM -> combine over the k experts, each scaled by its routing weight. The grouped
  * GEMMs read the packed weights and decode them in registers, never materializing bf16 weights
  * ([GGUF] "ggml Metal 커널 통합"; [EN] "MXFP4 4-Bit Quantization": MXFP4 weights served by
  * dedicated kernels instead of a bf16 fallback).

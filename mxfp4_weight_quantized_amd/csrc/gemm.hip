@@ -50,8 +50,6 @@ struct GemmKArgs {
   int F;                      // gate_up: up rows start at F
   void* out;
   int out_bf16;
-  const int32_t* perm;        // down: output row index perm[r]
-  const float* rw;            // down: routing weight of each pair
 };
 
 // LDS swizzles. A 16-byte chunk c of LDS row r is stored at slot c ^ swz(r). The per-lane
@@ -121,12 +119,17 @@ __device__ __forceinline__ void dma_b32(const i32x4& res, uint32_t voff, uint32_
                : "memory", "m0");
 }
 
-// E8M0 byte -> fp32 scale operand, without branches (b = 0: 2^-127; b = 255: NaN).
+// E8M0 byte -> fp32 scale operand 2^(b-127), without branches: 2^-127 * 2^b is exact for every
+// b (b = 0 gives the subnormal 2^-127), b = 255 overflows to +Inf, and s - (s - s) keeps every
+// finite s and turns Inf into NaN, the value of that byte.
 __device__ __forceinline__ float e8m0_scale(uint32_t b) {
-  uint32_t u = b << 23;
-  u = (b == 0u) ? 0x00400000u : u;
-  u = (b == 255u) ? 0x7fc00000u : u;
-  return __uint_as_float(u);
+  const float s = __builtin_amdgcn_ldexpf(0x1p-127f, (int)b);
+  return s - (s - s);
+}
+
+// Lane offset plus a stage offset, saturating: the out-of-range marker stays out of range.
+__device__ __forceinline__ uint32_t off_add(uint32_t voff, uint32_t add) {
+  return __builtin_elementwise_add_sat(voff, add);
 }
 
 // 32-bit lane offsets of the direct loads of one LDS region. A region of `bytes` bytes is filled
@@ -193,8 +196,8 @@ __device__ __forceinline__ int frag_row(int wn, int f, int ln) {
 }
 
 // Epilogue of a wave's FM x FN fragments (rows r0 + wm*TM + 16i + 4g + q, column lane ln):
-// gate_up -> SwiGLU in fp32 -> bf16 h; down -> times the pair's routing weight, stored at the
-// pair's own row (un-permuted); linear -> fp32 or bf16.
+// gate_up -> SwiGLU in fp32 -> bf16 h; down -> fp32 at the permuted row (the combine applies the
+// routing weights: the epilogue needs no index or weight loads); linear -> fp32 or bf16.
 template <int MODE, int FM, int FN, int TM, int BN, int WN>
 __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc)[FM][FN], int r0,
                                            int row_end, int nt, int wm, int wn, int g, int ln) {
@@ -216,13 +219,11 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc
           h[(int64_t)r * p.F + col] = (uint16_t)f32_to_bf16_bits(hv);
         }
       } else if constexpr (MODE == MODE_DOWN) {
-        const int pair = p.perm[r];
-        const float wgt = p.rw[pair];
         float* y = reinterpret_cast<float*>(p.out);
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           const int col = nt * BN + wn * TN + f * 16 + ln;
-          if (col < p.N) y[(int64_t)pair * p.N + col] = acc[i][f][q] * wgt;
+          if (col < p.N) y[(int64_t)r * p.N + col] = acc[i][f][q];
         }
       } else {
 #pragma unroll
@@ -419,12 +420,11 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     const int kb = kt * KT;
 #pragma unroll
     for (int q = 0; q < IS; ++q) {
-      if constexpr (TW)
-        dma_b32(rS, (voffS[q] != kOutOfRange && kb + sblk[q] < nb) ? voffS[q] + (uint32_t)(kb * rpe) : kOutOfRange,
-                0, &sg.Sc[PS::instr(wave, q) * 64]);
-      else if constexpr (SCM == SCM_STAGE)
-        dma_b32(rS, voffS[q] == kOutOfRange ? kOutOfRange : voffS[q] + kb, 0,
+      if constexpr (TW)  // blocks past K (last stage only) are out of range: zero scales
+        dma_b32(rS, kb + sblk[q] < nb ? off_add(voffS[q], (uint32_t)(kb * rpe)) : kOutOfRange, 0,
                 &sg.Sc[PS::instr(wave, q) * 64]);
+      else if constexpr (SCM == SCM_STAGE)
+        dma_b32(rS, off_add(voffS[q], (uint32_t)kb), 0, &sg.Sc[PS::instr(wave, q) * 64]);
       else
         dma_b8(rS, kb + sblk[q] < nb ? voffS[q] + kb : kOutOfRange, 0, &sg.Sc[PS::instr(wave, q) * 64]);
     }
@@ -502,18 +502,18 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     const int kb = kt * KT;
 #pragma unroll
     for (int q = 0; q < ISA; ++q)
-      dma_b32(rSA, voffSA[q] == kOutOfRange ? kOutOfRange : voffSA[q] + kb, 0,
+      dma_b32(rSA, off_add(voffSA[q], (uint32_t)kb), 0,
               &sg.Sa[PSA::instr(wave, q) * 64]);
     constexpr int A_KB = AFP4 ? 16 : 64;  // bytes of A per 32-element block
     if ((kt + 1) * KT <= nb) {
 #pragma unroll
       for (int q = 0; q < IA; ++q)
-        dma_b128(rA, voffA[q] == kOutOfRange ? kOutOfRange : voffA[q] + kb * A_KB, 0,
+        dma_b128(rA, off_add(voffA[q], (uint32_t)(kb * A_KB)), 0,
                  &sg.A[PA::instr(wave, q) * 1024]);
     } else {
 #pragma unroll
       for (int q = 0; q < IA; ++q)
-        dma_b128(rA, (voffA[q] != kOutOfRange && kb + ablk[q] < nb) ? voffA[q] + kb * A_KB : kOutOfRange,
+        dma_b128(rA, kb + ablk[q] < nb ? off_add(voffA[q], (uint32_t)(kb * A_KB)) : kOutOfRange,
                  0, &sg.A[PA::instr(wave, q) * 1024]);
     }
   };
@@ -545,7 +545,8 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
       for (int f = 0; f < FN; ++f) {
         const int r = brow[f];
         w[f] = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-        scb[f] = past ? 127u : (uint32_t)Scb[bsh[f] + (4 * j + g) * SBS];
+        // (tiled weights: blocks past K hold zero codes and zero scales, 0 * 2^-127 = 0)
+        scb[f] = (!TW && past) ? 127u : (uint32_t)Scb[bsh[f] + (4 * j + g) * SBS];
       }
       if constexpr (AFP4) {
         u32x4 a[FM];
@@ -641,12 +642,13 @@ template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool 
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_kernel(GemmKArgs p) {
   gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM, false>(p);
 }
-// out[t][n] = sum_{j < k} Y[t*k + j][n] in slot order; pairs with inv < 0 (skipped routing
-// indices) contribute nothing.
+// out[t][n] = sum_{j < k} w[t][j] * Y[inv[t*k + j]][n] in slot order (each product rounded to
+// fp32, then summed); pairs with inv < 0 (skipped routing indices) contribute nothing.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
-                                                      const int32_t* __restrict__ inv, int T,
-                                                      int H, int k, void* __restrict__ out) {
+                                                      const int32_t* __restrict__ inv,
+                                                      const float* __restrict__ w, int T, int H,
+                                                      int k, void* __restrict__ out) {
   const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int h4 = H >> 2;
   if (i4 >= (int64_t)T * h4) return;
@@ -654,9 +656,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int c = (int)(i4 % h4) * 4;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
-    if (inv[(int64_t)t * k + j] < 0) continue;
-    const float4 v = *reinterpret_cast<const float4*>(Y + ((int64_t)t * k + j) * H + c);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    const int r = inv[(int64_t)t * k + j];
+    if (r < 0) continue;
+    const float wj = w[(int64_t)t * k + j];
+    const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)r * H + c);
+    s.x += __fmul_rn(v.x, wj); s.y += __fmul_rn(v.y, wj);
+    s.z += __fmul_rn(v.z, wj); s.w += __fmul_rn(v.w, wj);
   }
   if (BF16_OUT) {
     const uint32_t lo = f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16);
@@ -759,7 +764,7 @@ GemmKArgs gate_up_args(const MoeGemmArgs& m) {
 }
 
 GemmKArgs down_args(const MoeGemmArgs& m) {
-  // A = h rows (permuted order), B = W_dn[e] (H rows), out = Y[pair] * routing weight
+  // A = h rows (permuted order), B = W_dn[e] (H rows), out = Y rows (permuted order)
   GemmKArgs d{};
   d.A = m.h;
   d.a_rows = (int64_t)m.T * m.k;
@@ -776,8 +781,6 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
   d.rows_total = m.T * m.k;
   d.F = m.F;
   d.out = m.y;
-  d.perm = m.perm;
-  d.rw = m.topk_w;
   return d;
 }
 
@@ -836,11 +839,11 @@ hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {
   const int64_t n4 = (int64_t)m.T * (m.H / 4);
   const unsigned grid = (unsigned)((n4 + 255) / 256);
   if (m.out_bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, stream, m.y, m.inv, m.T, m.H,
-                       m.k, m.out);
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, stream, m.y, m.inv,
+                       m.topk_w, m.T, m.H, m.k, m.out);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, stream, m.y, m.inv, m.T,
-                       m.H, m.k, m.out);
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, stream, m.y, m.inv,
+                       m.topk_w, m.T, m.H, m.k, m.out);
   return hipGetLastError();
 }
 
