@@ -643,32 +643,40 @@ __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_
   gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM, false>(p);
 }
 // out[t][n] = sum_{j < k} w[t][j] * Y[inv[t*k + j]][n] in slot order (each product rounded to
-// fp32, then summed); pairs with inv < 0 (skipped routing indices) contribute nothing.
+// fp32, then summed); pairs with inv < 0 (skipped routing indices) contribute nothing. Eight
+// columns per thread (two 16-byte loads per row in flight).
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int T, int H,
                                                       int k, void* __restrict__ out) {
-  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int h4 = H >> 2;
-  if (i4 >= (int64_t)T * h4) return;
-  const int t = (int)(i4 / h4);
-  const int c = (int)(i4 % h4) * 4;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int64_t i8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int h8 = H >> 3;
+  if (i8 >= (int64_t)T * h8) return;
+  const int t = (int)(i8 / h8);
+  const int c = (int)(i8 % h8) * 8;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const int r = inv[(int64_t)t * k + j];
     if (r < 0) continue;
     const float wj = w[(int64_t)t * k + j];
-    const float4 v = *reinterpret_cast<const float4*>(Y + (int64_t)r * H + c);
-    s.x += __fmul_rn(v.x, wj); s.y += __fmul_rn(v.y, wj);
-    s.z += __fmul_rn(v.z, wj); s.w += __fmul_rn(v.w, wj);
+    const float4 v0 = *reinterpret_cast<const float4*>(Y + (int64_t)r * H + c);
+    const float4 v1 = *reinterpret_cast<const float4*>(Y + (int64_t)r * H + c + 4);
+    s[0] += __fmul_rn(v0.x, wj); s[1] += __fmul_rn(v0.y, wj);
+    s[2] += __fmul_rn(v0.z, wj); s[3] += __fmul_rn(v0.w, wj);
+    s[4] += __fmul_rn(v1.x, wj); s[5] += __fmul_rn(v1.y, wj);
+    s[6] += __fmul_rn(v1.z, wj); s[7] += __fmul_rn(v1.w, wj);
   }
   if (BF16_OUT) {
-    const uint32_t lo = f32_to_bf16_bits(s.x) | (f32_to_bf16_bits(s.y) << 16);
-    const uint32_t hi = f32_to_bf16_bits(s.z) | (f32_to_bf16_bits(s.w) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + (int64_t)t * H + c) = make_uint2(lo, hi);
+    uint32_t q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = f32_to_bf16_bits(s[2 * u]) | (f32_to_bf16_bits(s[2 * u + 1]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)t * H + c) =
+        make_uint4(q[0], q[1], q[2], q[3]);
   } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (int64_t)t * H + c) = s;
+    float* o = reinterpret_cast<float*>(out) + (int64_t)t * H + c;
+    *reinterpret_cast<float4*>(o) = make_float4(s[0], s[1], s[2], s[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(s[4], s[5], s[6], s[7]);
   }
 }
 
@@ -836,8 +844,8 @@ hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
 }
 
 hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {
-  const int64_t n4 = (int64_t)m.T * (m.H / 4);
-  const unsigned grid = (unsigned)((n4 + 255) / 256);
+  const int64_t n8 = (int64_t)m.T * (m.H / 8);
+  const unsigned grid = (unsigned)((n8 + 255) / 256);
   if (m.out_bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, stream, m.y, m.inv,
                        m.topk_w, m.T, m.H, m.k, m.out);

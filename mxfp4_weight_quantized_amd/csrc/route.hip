@@ -11,7 +11,8 @@
 // in L2) and the partial tiles meet in LDS, summed in a fixed order so that the logits do not
 // depend on timing. With few tokens G = 1 and the groups spread over many workgroups, so a decode
 // batch is not left to a handful of CUs; with many tokens G covers all experts and each token
-// tile is read once. route_select_kernel: one wave per token ranks the logits (wave-wide argmax
+// tile is read once, and the same workgroup then ranks its tokens' logits from LDS (no second
+// kernel). Otherwise route_select_kernel: one wave per token ranks the logits (wave-wide argmax
 // k times) and writes the top-k indices and their softmax.
 #include "mx_device.h"
 #include "mx_launch.h"
@@ -20,16 +21,86 @@ namespace mx {
 namespace {
 
 constexpr int kTokPerWG = 16;
+// Below this many (token tile, expert group) pairs each workgroup takes one expert group, so a
+// small batch spreads over more CUs (and selection runs as its own kernel).
+constexpr int kSpreadBelow = 512;
 
 // (value desc, index asc) ordering: true if (va, ia) ranks before (vb, ib).
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// One wave ranks the E logits of token t (logit_of(e) for e < E; lane l holds experts l, l+64,
+// l+128, l+192): k rounds of a wave-wide argmax under (logit desc, expert index asc), then the
+// softmax of the k selected logits; lane j < k writes entry j.
+template <class LogitOf>
+__device__ __forceinline__ void select_topk_wave(LogitOf logit_of, int lane, int t, int E, int k,
+                                                 int32_t* __restrict__ idx_out,
+                                                 float* __restrict__ w_out) {
+  float cv[4];
+  int ci[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    ci[q] = e;
+    cv[q] = (e < E) ? logit_of(e) : -INFINITY;
+  }
+  bool used[4] = {false, false, false, false};
+  float sel_v[8];
+  int sel_i[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (!used[q] && ci[q] < E && (bi == 0x7fffffff || ranks_before(cv[q], ci[q], bv, bi))) {
+        bv = cv[q];
+        bi = ci[q];
+      }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    sel_v[j] = bv;
+    sel_i[j] = bi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (ci[q] == bi) used[q] = true;
+  }
+  float sum = 0.f, mine = 0.f;
+  int mine_i = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const float ev = expf(sel_v[j] - sel_v[0]);
+    sum += ev;
+    if (lane == j) {
+      mine = ev;
+      mine_i = sel_i[j];
+    }
+  }
+  if (lane < k) {
+    idx_out[(int64_t)t * k + lane] = mine_i;
+    w_out[(int64_t)t * k + lane] = mine / sum;
+  }
+}
+
+// SELECT: the workgroup covers all experts of its tokens (n_groups * 16 >= E); it keeps the
+// logits tile in LDS and its waves (one per token) also make the top-k selection.
+template <bool SELECT>
 __global__ __launch_bounds__(1024) void route_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ br,
-    int T, int H, int E, int n_groups, int n_splits, float* __restrict__ logits) {
+    int T, int H, int E, int n_groups, int n_splits, float* __restrict__ logits, int k,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   __shared__ float part[16][kTokPerWG][16];  // per wave: its partial 16 x 16 tile
+  __shared__ float tile[SELECT ? kTokPerWG : 1][SELECT ? 257 : 1];  // the workgroup's logits
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * kTokPerWG;
@@ -82,72 +153,26 @@ __global__ __launch_bounds__(1024) void route_logits_kernel(
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 4 * g + i;
         if (t < T) logits[(int64_t)t * E + e] = acc[i] + bias;
+        if constexpr (SELECT) tile[4 * g + i][e] = acc[i] + bias;
       }
     }
   }
+  if constexpr (SELECT) {
+    __syncthreads();
+    const int nwaves = blockDim.x >> 6;  // n_groups * n_splits, at least 1
+    for (int tt = wave; tt < kTokPerWG && t0 + tt < T; tt += nwaves)
+      select_topk_wave([&](int e) { return tile[tt][e]; }, lane, t0 + tt, E, k, idx_out, w_out);
+  }
 }
 
-// One wave per token: lane l holds the logits of experts l, l+64, l+128, l+192.
+// One wave per token, logits read back from memory.
 __global__ __launch_bounds__(256) void route_select_kernel(const float* __restrict__ logits, int T,
                                                            int E, int k, int32_t* __restrict__ idx_out,
                                                            float* __restrict__ w_out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float cv[4];
-  int ci[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    ci[q] = e;
-    cv[q] = (e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
-  }
-  bool used[4] = {false, false, false, false};
-  float sel_v[8];
-  int sel_i[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (!used[q] && ci[q] < E && (bi == 0x7fffffff || ranks_before(cv[q], ci[q], bv, bi))) {
-        bv = cv[q];
-        bi = ci[q];
-      }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    sel_v[j] = bv;
-    sel_i[j] = bi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (ci[q] == bi) used[q] = true;
-  }
-  // softmax over the k selected (lane j < k writes entry j)
-  float sum = 0.f, mine = 0.f;
-  int mine_i = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    const float ev = expf(sel_v[j] - sel_v[0]);
-    sum += ev;
-    if (lane == j) {
-      mine = ev;
-      mine_i = sel_i[j];
-    }
-  }
-  if (lane < k) {
-    idx_out[(int64_t)t * k + lane] = mine_i;
-    w_out[(int64_t)t * k + lane] = mine / sum;
-  }
+  select_topk_wave([&](int e) { return logits[(int64_t)t * E + e]; }, lane, t, E, k, idx_out, w_out);
 }
 
 }  // namespace
@@ -158,10 +183,15 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
   if (T == 0) return hipSuccess;
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
   // G groups per workgroup, H split so that G x splits fills up to 16 waves
-  const int G = (tiles * groups <= 512) ? 1 : groups;
+  const int G = (tiles * groups <= kSpreadBelow) ? 1 : groups;
   const int splits = min(16 / G, H / 32);
-  hipLaunchKernelGGL(route_logits_kernel, dim3(tiles, groups / G), dim3(64 * G * splits), 0, stream,
-                     x, wr, br, T, H, E, G, splits, logits);
+  if (G == groups) {  // one workgroup covers all experts of its tokens: select in the same kernel
+    hipLaunchKernelGGL(route_logits_kernel<true>, dim3(tiles, 1), dim3(64 * G * splits), 0, stream,
+                       x, wr, br, T, H, E, G, splits, logits, k, idx, w);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(route_logits_kernel<false>, dim3(tiles, groups / G), dim3(64 * G * splits), 0,
+                     stream, x, wr, br, T, H, E, G, splits, logits, k, idx, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k,
