@@ -209,12 +209,34 @@ def bench_moe(args, name, shape, flags):
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
+    if args.graph:
+        # one HIP graph holds one rotation of the step over the token batches / weight copies;
+        # the timed steps are whole rotations (steps rounded up to a multiple of the period)
+        period = len(refs)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(period):
+                st = L.mxfp4_moe_mlp(refs[i], ws.data_ptr(), ws_bytes, cap)
+                if st != 0:
+                    raise mx.MXError(st, mx.last_error())
+        reps = max(1, -(-args.steps // period))
+        g.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        timed_steps = reps * period
+    else:
+        t0.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        timed_steps = args.steps
+    ms = t0.elapsed_time(t1) / timed_steps
 
     # per-kernel times over a second pass of the same steps (events recorded by the library)
     mx.mx_profile_enable(True)
@@ -243,7 +265,7 @@ def bench_moe(args, name, shape, flags):
     layer_traffic = touched * layer_bytes / s.E + s.T * s.H * 2 * 2
     result = {
         "metric": METRIC, "value": round(s.T / (ms * 1e-3), 2), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "n_gpus": 1, "steps": timed_steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp4" if flags else "bf16", "data": "synthetic",
         "config": {"workload": name, "T": s.T, "H": s.H, "F": s.F, "E": s.E, "k": s.k,
@@ -251,7 +273,8 @@ def bench_moe(args, name, shape, flags):
                    "weight_layout": "tiled (converted once at load)" if tiled else "row-major",
                    "activations": "mxfp4" if flags else "bf16",
                    "out_dtype": "bf16", "router_bias_std": s.bias_std, "seed": s.seed,
-                   "parallelism": "single-gpu", "weight_copies": n_w, "token_batches": n_x},
+                   "parallelism": "single-gpu", "weight_copies": n_w, "token_batches": n_x,
+                   "launch": "hip graph per rotation" if args.graph else "eager"},
         "step": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
                  "hbm_gbs_algorithmic": round(layer_traffic / (ms * 1e-3) / 1e9, 1),
                  "touched_experts": touched},
@@ -445,6 +468,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the steps from a HIP graph instead of launching them one by one")
     ap.add_argument("--row-major-weights", action="store_true",
                     help="feed the grouped GEMMs row-major weights instead of the tiled layout")
     ap.add_argument("--calibrate-copy", action="store_true",
