@@ -304,12 +304,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   struct __attribute__((aligned(1024))) Stage {
     uint8_t A[A_STAGE];
     uint8_t B[B_STAGE];
-    uint32_t Sc[SCM == SCM_RESIDENT ? 1 : S_DW];  // weight scale bytes of the stage
-    uint32_t Sa[AFP4 ? SA_DW : 1];     // activation scale bytes (FP4 A), same layout
+    uint32_t Sc[SCM == SCM_RESIDENT ? 0 : S_DW];  // weight scale bytes of the stage
+    uint32_t Sa[AFP4 ? SA_DW : 0];     // activation scale bytes (FP4 A), same layout
   };
   static_assert(sizeof(Stage) % 1024 == 0, "stage alignment");
   __shared__ Stage stg[STAGES];
-  __shared__ uint32_t sRes[SCM == SCM_RESIDENT ? RS_DW : 1];  // resident weight scales
+  __shared__ uint32_t sRes[SCM == SCM_RESIDENT ? RS_DW : 1];  // resident weight scales (4 B if unused)
   __shared__ int sArow[BM];
 
   int e, r0, row_end, nt;
@@ -706,6 +706,11 @@ struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4
 // 128 x 384 with 2 or 4 stages and 8-block stages (spills).
 struct CfgPreGU4 { static constexpr int BM = 128, BN = 512, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE; };
 struct CfgPreDn4 { static constexpr int BM = 128, BN = 384, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE; };
+// Few pairs (a handful of experts touched): the down GEMM (2880 columns: 23 tiles of 128 per
+// expert) takes 64-column tiles, twice the workgroups to stream the few experts' weights
+// (120B-shaped decode, T = 1: 15.9 -> 14.1 us; gate_up, which has twice the columns, measured no
+// better with them).
+struct CfgTinyDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 4, SCM = SCM_RESIDENT; };
 constexpr int kPrefillRows = 64, kPrefillRows4 = 128;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
 static_assert(CfgPreGU4::BM == kPrefillRows4 && CfgPreDn4::BM == kPrefillRows4, "one tile list");
@@ -749,6 +754,10 @@ hipError_t launch_linear_tiles(const GemmKArgs& g, int M, int N, hipStream_t str
 }
 
 bool use_prefill_tiles(int T, int k, int E) { return (int64_t)T * k >= 64LL * E; }
+// at most min(T*k, E) experts touched: with 128-column tiles fewer than two workgroups per CU
+bool use_tiny_tiles(int T, int k, int E, int N) {
+  return (int64_t)std::min(T * k, E) * ((N + 127) / 128) < 512;
+}
 
 GemmKArgs gate_up_args(const MoeGemmArgs& m) {
   // A = x rows gathered through perm / k, B = W_gu[e] (2F rows), out = h [P][F]
@@ -829,6 +838,8 @@ hipError_t down_tw(GemmKArgs d, const MoeGemmArgs& m, hipStream_t stream) {
     return launch_moe_gemm<CfgDecDn, MODE_DOWN, true, TW>(d, m.max_tiles, m.H, stream);
   }
   if (pre) return launch_moe_gemm<CfgPreDn, MODE_DOWN, false, TW>(d, m.max_tiles, m.H, stream);
+  if (use_tiny_tiles(m.T, m.k, m.E, m.H))
+    return launch_moe_gemm<CfgTinyDn, MODE_DOWN, false, TW>(d, m.max_tiles, m.H, stream);
   return launch_moe_gemm<CfgDecDn, MODE_DOWN, false, TW>(d, m.max_tiles, m.H, stream);
 }
 }  // namespace
