@@ -279,15 +279,23 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   const int32_t* idx;
   const float* tw;
   hipError_t e;
+  // small batches: the router launch computes the logits only and the permutation launch makes
+  // the top-k selection first (one launch fewer)
+  bool select_in_permute = false;
+  const float* sel_logits = nullptr;
   if (d.topk_idx_in == nullptr) {
     float* logits = d.logits_out ? d.logits_out : reinterpret_cast<float*>(w + L.logits);
     int32_t* oi = d.topk_idx_out ? d.topk_idx_out : reinterpret_cast<int32_t*>(w + L.idx);
     float* ow = d.topk_w_out ? d.topk_w_out : reinterpret_cast<float*>(w + L.w);
+    select_in_permute = mx::route_logits_defers_select(d.T, d.E, d.k);
     {
       ProfScope ps(PK_ROUTE, s);
-      e = mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, s);
+      e = select_in_permute
+              ? mx::launch_route_logits(d.x, d.wr, d.br, d.T, d.H, d.E, logits, s)
+              : mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, s);
     }
     if (e != hipSuccess) return hip_fail(e, "route launch");
+    sel_logits = logits;
     idx = oi;
     tw = ow;
   } else {
@@ -300,7 +308,12 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   int2* tiles = reinterpret_cast<int2*>(w + L.tiles);
   {
     ProfScope ps(PK_PERMUTE, s);
-    e = mx::launch_permute(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows, tiles, status + 1, s);
+    e = select_in_permute
+            ? mx::launch_select_permute(sel_logits, d.T, d.k, d.E, const_cast<int32_t*>(idx),
+                                        const_cast<float*>(tw), offsets, perm, inv, status,
+                                        L.tile_rows, tiles, status + 1, s)
+            : mx::launch_permute(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows, tiles,
+                                 status + 1, s);
   }
   if (e != hipSuccess) return hip_fail(e, "permute launch");
   const bool mx_act = (d.flags & MX_ACT_MXFP4) != 0;

@@ -77,4 +77,74 @@ __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// ---- top-k selection (router and the fused selection in the permutation) ----
+// (value desc, index asc) ordering: true if (va, ia) ranks before (vb, ib).
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// One wave ranks the E logits of token t (logit_of(e) for e < E; lane l holds experts l, l+64,
+// l+128, l+192): k rounds of a wave-wide argmax under (logit desc, expert index asc), then the
+// softmax of the k selected logits; lane j < k writes entry j and returns its expert index.
+template <class LogitOf>
+__device__ __forceinline__ int select_topk_wave(LogitOf logit_of, int lane, int t, int E, int k,
+                                                int32_t* __restrict__ idx_out,
+                                                float* __restrict__ w_out) {
+  float cv[4];
+  int ci[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    ci[q] = e;
+    cv[q] = (e < E) ? logit_of(e) : -INFINITY;
+  }
+  bool used[4] = {false, false, false, false};
+  float sel_v[8];
+  int sel_i[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (!used[q] && ci[q] < E && (bi == 0x7fffffff || ranks_before(cv[q], ci[q], bv, bi))) {
+        bv = cv[q];
+        bi = ci[q];
+      }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    sel_v[j] = bv;
+    sel_i[j] = bi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (ci[q] == bi) used[q] = true;
+  }
+  float sum = 0.f, mine = 0.f;
+  int mine_i = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const float ev = expf(sel_v[j] - sel_v[0]);
+    sum += ev;
+    if (lane == j) {
+      mine = ev;
+      mine_i = sel_i[j];
+    }
+  }
+  if (lane < k) {
+    idx_out[(int64_t)t * k + lane] = mine_i;
+    w_out[(int64_t)t * k + lane] = mine / sum;
+  }
+  return mine_i;
+}
+
+
 }  // namespace mx

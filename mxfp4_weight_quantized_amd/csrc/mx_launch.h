@@ -20,13 +20,24 @@ hipError_t launch_tile_weights(const uint8_t* packed, const uint8_t* scales, int
 hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
                              int E, int k, float* logits, int32_t* idx, float* w,
                              hipStream_t stream);
+// Router logits only, when the selection can be left to launch_select_permute (small batches
+// whose logits kernel does not select itself); returns false (nothing launched) otherwise.
+bool route_logits_defers_select(int T, int E, int k);
+hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
+                               int H, int E, float* logits, hipStream_t stream);
 
 // permute.hip: tiles/num_tiles may be NULL (tile_rows ignored then). With a tile list, perm must
 // hold P + tile_rows entries: the padding (and rows past the last valid pair) are set to pair 0.
 constexpr int kMaxTileRows = 128;
+constexpr int kSelectMaxPairs = 2048;  // launch_select_permute: T * k at most this
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm,
                           int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
                           int32_t* num_tiles, hipStream_t stream);
+// The same after the top-k selection from the router logits (writes idx and w [T][k]).
+hipError_t launch_select_permute(const float* logits, int T, int k, int E, int32_t* idx, float* w,
+                                 int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
+                                 int tile_rows, int2* tiles, int32_t* num_tiles,
+                                 hipStream_t stream);
 
 // gemm.hip
 struct MoeGemmArgs {

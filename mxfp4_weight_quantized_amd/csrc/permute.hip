@@ -7,6 +7,10 @@
 // (expert, wave) gives every (wave, expert) its first output row, and each wave then scatters its
 // chunk 64 pairs at a time, ranking equal experts among the 64 lanes with ballots. The order is
 // the stable (token, slot) order by construction, so the result is deterministic.
+//
+// For small batches the same launch can first make the top-k selection from the router logits
+// (SELECT: one wave per token, the router's selection function), keeping the indices in LDS;
+// this saves the separate selection launch of the router in the MoE MLP.
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -34,17 +38,21 @@ __device__ int wave_exclusive_scan(int* v, int n, int lane) {
   return carry;
 }
 
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx, int P,
+template <bool SELECT>
+__global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx, int P,
                                                        int E, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm,
                                                        int32_t* __restrict__ inv,
                                                        int32_t* __restrict__ status, int tile_rows,
                                                        int2* __restrict__ tiles,
-                                                       int32_t* __restrict__ num_tiles) {
+                                                       int32_t* __restrict__ num_tiles,
+                                                       const float* __restrict__ logits, int k,
+                                                       float* __restrict__ w_out) {
   __shared__ int cnt[kWaves][kMaxE];
   __shared__ int tot[kMaxE + 1];
   __shared__ int tbase[kMaxE + 1];
   __shared__ int bad;
+  __shared__ int sidx[SELECT ? kSelectMaxPairs : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int chunk = (P + kWaves - 1) / kWaves;
@@ -53,11 +61,23 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
 
   for (int i = threadIdx.x; i < kWaves * kMaxE; i += blockDim.x) (&cnt[0][0])[i] = 0;
   if (threadIdx.x == 0) bad = 0;
+  if constexpr (SELECT) {  // 0. top-k of every token (P = T * k <= kSelectMaxPairs)
+    const int T = P / k;
+    for (int t = wave; t < T; t += kWaves) {
+      const int e = select_topk_wave([&](int x) { return logits[(int64_t)t * E + x]; }, lane, t,
+                                     E, k, idx, w_out);
+      if (lane < k) sidx[t * k + lane] = e;
+    }
+  }
   __syncthreads();
+  auto pair_expert = [&](int p) -> int {
+    if constexpr (SELECT) return sidx[p];
+    else return idx[p];
+  };
 
   // 1. per-wave histogram
   for (int p = p_begin + lane; p < p_end; p += 64) {
-    const int e = idx[p];
+    const int e = pair_expert(p);
     if (e >= 0 && e < E) atomicAdd(&cnt[wave][e], 1);
     else bad = 1;
   }
@@ -107,7 +127,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int g0 = p_begin; g0 < p_end; g0 += 64) {
     const int p = g0 + lane;
-    int e = (p < p_end) ? idx[p] : -1;
+    int e = (p < p_end) ? pair_expert(p) : -1;
     const bool ok = (e >= 0 && e < E);
     if (!ok) {
       if (p < p_end) inv[p] = -1;
@@ -140,8 +160,20 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
                           int32_t* num_tiles, hipStream_t stream) {
   const int P = T * k;
   if (tiles == nullptr || num_tiles == nullptr) tile_rows = 0;
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(64 * kWaves), 0, stream, idx, P, E, offsets,
-                     perm, inv, status, tile_rows, tiles, num_tiles);
+  hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(64 * kWaves), 0, stream,
+                     const_cast<int32_t*>(idx), P, E, offsets, perm, inv, status, tile_rows, tiles,
+                     num_tiles, nullptr, k, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_permute(const float* logits, int T, int k, int E, int32_t* idx, float* w,
+                                 int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
+                                 int tile_rows, int2* tiles, int32_t* num_tiles,
+                                 hipStream_t stream) {
+  const int P = T * k;
+  if (tiles == nullptr || num_tiles == nullptr) tile_rows = 0;
+  hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(64 * kWaves), 0, stream, idx, P, E,
+                     offsets, perm, inv, status, tile_rows, tiles, num_tiles, logits, k, w);
   return hipGetLastError();
 }
 

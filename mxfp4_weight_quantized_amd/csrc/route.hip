@@ -25,73 +25,6 @@ constexpr int kTokPerWG = 16;
 // small batch spreads over more CUs (and selection runs as its own kernel).
 constexpr int kSpreadBelow = 512;
 
-// (value desc, index asc) ordering: true if (va, ia) ranks before (vb, ib).
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-// One wave ranks the E logits of token t (logit_of(e) for e < E; lane l holds experts l, l+64,
-// l+128, l+192): k rounds of a wave-wide argmax under (logit desc, expert index asc), then the
-// softmax of the k selected logits; lane j < k writes entry j.
-template <class LogitOf>
-__device__ __forceinline__ void select_topk_wave(LogitOf logit_of, int lane, int t, int E, int k,
-                                                 int32_t* __restrict__ idx_out,
-                                                 float* __restrict__ w_out) {
-  float cv[4];
-  int ci[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    ci[q] = e;
-    cv[q] = (e < E) ? logit_of(e) : -INFINITY;
-  }
-  bool used[4] = {false, false, false, false};
-  float sel_v[8];
-  int sel_i[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (!used[q] && ci[q] < E && (bi == 0x7fffffff || ranks_before(cv[q], ci[q], bv, bi))) {
-        bv = cv[q];
-        bi = ci[q];
-      }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    sel_v[j] = bv;
-    sel_i[j] = bi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (ci[q] == bi) used[q] = true;
-  }
-  float sum = 0.f, mine = 0.f;
-  int mine_i = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    const float ev = expf(sel_v[j] - sel_v[0]);
-    sum += ev;
-    if (lane == j) {
-      mine = ev;
-      mine_i = sel_i[j];
-    }
-  }
-  if (lane < k) {
-    idx_out[(int64_t)t * k + lane] = mine_i;
-    w_out[(int64_t)t * k + lane] = mine / sum;
-  }
-}
-
 // SELECT: the workgroup covers all experts of its tokens (n_groups * 16 >= E); it keeps the
 // logits tile in LDS and its waves (one per token) also make the top-k selection.
 template <bool SELECT>
@@ -176,6 +109,24 @@ __global__ __launch_bounds__(256) void route_select_kernel(const float* __restri
 }
 
 }  // namespace
+
+// At most one token per wave of the permutation workgroup: each wave's selection then waits for
+// one round of logit loads (with more tokens per wave the rounds queue up and cost more than the
+// launch saved: 20B-shaped decode, T = 64, measured 10 us slower).
+bool route_logits_defers_select(int T, int E, int k) {
+  const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
+  return groups > 1 && tiles * groups <= kSpreadBelow && T <= 16 && (int64_t)T * k <= kSelectMaxPairs;
+}
+
+hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
+                               int H, int E, float* logits, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
+  const int splits = min(16, H / 32);
+  hipLaunchKernelGGL(route_logits_kernel<false>, dim3(tiles, groups), dim3(64 * splits), 0, stream,
+                     x, wr, br, T, H, E, 1, splits, logits, 0, nullptr, nullptr);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
                              int E, int k, float* logits, int32_t* idx, float* w,
