@@ -196,29 +196,19 @@ __device__ __forceinline__ int frag_row(int wn, int f, int ln) {
 }
 
 // Epilogue of a wave's FM x FN fragments (rows r0 + wm*TM + 16i + 4g + q, column lane ln):
-// gate_up -> SwiGLU in fp32 -> bf16 h; down -> fp32 at the permuted row (the combine applies the
-// routing weights: the epilogue needs no index or weight loads); linear -> fp32 or bf16.
+// down -> fp32 at the permuted row (the combine applies the routing weights: the epilogue needs
+// no index or weight loads); linear -> fp32 or bf16. (gate_up stores through LDS, below.)
 template <int MODE, int FM, int FN, int TM, int BN, int WN>
 __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc)[FM][FN], int r0,
                                            int row_end, int nt, int wm, int wn, int g, int ln) {
-  constexpr int BNH = BN / 2, TN = BN / WN;
+  constexpr int TN = BN / WN;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = r0 + wm * TM + i * 16 + 4 * g + q;
       if (r >= row_end) continue;
-      if constexpr (MODE == MODE_GATE_UP) {
-        uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
-#pragma unroll
-        for (int f = 0; f < FN / 2; ++f) {
-          const int col = nt * BNH + wn * (BNH / WN) + f * 16 + ln;
-          if (col >= p.F) continue;
-          const float gt = acc[i][f][q], up = acc[i][FN / 2 + f][q];
-          const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
-          h[(int64_t)r * p.F + col] = (uint16_t)f32_to_bf16_bits(hv);
-        }
-      } else if constexpr (MODE == MODE_DOWN) {
+      if constexpr (MODE == MODE_DOWN) {
         float* y = reinterpret_cast<float*>(p.out);
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
@@ -626,7 +616,39 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     st = st == STAGES - 1 ? 0 : st + 1;
   }
 
-  store_tile<MODE, FM, FN, TM, BN, WN>(p, acc, r0, row_end, nt, wm, wn, g, ln);
+  if constexpr (MODE == MODE_GATE_UP) {
+    // h goes out through LDS: SwiGLU into a BM x BN/2 bf16 tile (rows padded by 16 bytes: the
+    // four row groups of a fragment land on different banks) in the now idle stage buffers,
+    // then whole 16-byte chunks to global, so every store instruction writes full lines instead
+    // of 2-byte pieces of 16 columns x 4 rows.
+    constexpr int LDH = BNH + 8;
+    constexpr int CPR = BNH / 8;  // 16-byte chunks per row
+    static_assert(BM * LDH * 2 <= STAGES * (int)sizeof(Stage), "h tile fits the stage buffers");
+    uint16_t* sh = reinterpret_cast<uint16_t*>(&stg[0]);
+    barrier_lds();  // every wave is done reading the last stage (no loads are in flight)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int f = 0; f < FN / 2; ++f) {
+          const float gt = acc[i][f][q], up = acc[i][FN / 2 + f][q];
+          const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
+          sh[(wm * TM + i * 16 + 4 * g + q) * LDH + wn * (BNH / WN) + f * 16 + ln] =
+              (uint16_t)f32_to_bf16_bits(hv);
+        }
+    barrier_lds();
+    uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
+    for (int c = tid; c < BM * CPR; c += NT) {
+      const int lr = c / CPR, cc = c % CPR;
+      const int r = r0 + lr, col = nt * BNH + cc * 8;
+      if (r < row_end && col < p.F)
+        *reinterpret_cast<uint4*>(h + (int64_t)r * p.F + col) =
+            *reinterpret_cast<const uint4*>(sh + lr * LDH + cc * 8);
+    }
+  } else {
+    store_tile<MODE, FM, FN, TM, BN, WN>(p, acc, r0, row_end, nt, wm, wn, g, ln);
+  }
 }
 
 // One kernel name per role, so profiles show which product a launch is.
