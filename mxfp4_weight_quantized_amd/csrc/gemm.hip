@@ -646,6 +646,29 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
         *reinterpret_cast<uint4*>(h + (int64_t)r * p.F + col) =
             *reinterpret_cast<const uint4*>(sh + lr * LDH + cc * 8);
     }
+  } else if constexpr (MODE == MODE_DOWN && BM * (BN + 4) * 4 <= STAGES * (int)sizeof(Stage)) {
+    // Y the same way: the fp32 tile (rows padded by 16 bytes) in the stage buffers, then whole
+    // 16-byte chunks of each row to its permuted position
+    constexpr int LDY = BN + 4;
+    constexpr int CPR = BN / 4;
+    float* sy = reinterpret_cast<float*>(&stg[0]);
+    barrier_lds();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          sy[(wm * TM + i * 16 + 4 * g + q) * LDY + wn * TN + f * 16 + ln] = acc[i][f][q];
+    barrier_lds();
+    float* y = reinterpret_cast<float*>(p.out);
+    for (int c = tid; c < BM * CPR; c += NT) {
+      const int lr = c / CPR, cc = c % CPR;
+      const int r = r0 + lr, col = nt * BN + cc * 4;
+      if (r < row_end && col < p.N)
+        *reinterpret_cast<float4*>(y + (int64_t)r * p.N + col) =
+            *reinterpret_cast<const float4*>(sy + lr * LDY + cc * 4);
+    }
   } else {
     store_tile<MODE, FM, FN, TM, BN, WN>(p, acc, r0, row_end, nt, wm, wn, g, ln);
   }
