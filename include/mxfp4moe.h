@@ -135,6 +135,16 @@ mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const float* br,
 mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* offsets,
                       int32_t* perm, int32_t* inv, int32_t* status, void* stream);
 
+/* moe_permute_ws -- moe_permute with a caller-owned device workspace, which lets a large batch
+ * be permuted by many workgroups (a histogram of every 4096-pair slice, then each slice placed
+ * from all slice histograms; the same stable counting sort, so the same results element for
+ * element). ws: at least moe_permute_workspace(T, k, E) bytes, 256-byte aligned (may be NULL
+ * when that is 0: small batches take the one-workgroup path). */
+size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E);
+mx_status moe_permute_ws(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status, void* ws,
+                         size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------------------
  * mxfp4_moe_mlp -- the whole MoE MLP: route -> permute -> gate_up grouped GEMM with fused SwiGLU
  * -> down grouped GEMM -> combine over the k experts, each scaled by its routing weight. The grouped

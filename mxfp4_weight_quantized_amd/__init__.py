@@ -67,6 +67,8 @@ SIGNATURES = {
     "mxfp4_tile_weights": (_INT, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP]),
     "moe_route_topk": (_INT, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
     "moe_permute": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "moe_permute_workspace": (_SZ, [_I32, _I32, _I32]),
+    "moe_permute_ws": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxfp4_moe_mlp_workspace": (_SZ, [ctypes.POINTER(MoeDesc)]),
     "mxfp4_moe_mlp": (_INT, [ctypes.POINTER(MoeDesc), _VP, _SZ, _VP]),
     "mxfp4_linear_workspace": (_SZ, [_I32, _I32, _I32, _U32]),
@@ -179,16 +181,24 @@ def moe_route_topk(x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None, k
     return (logits if want_logits else None), idx, w
 
 
-def moe_permute(topk_idx: torch.Tensor, E: int, stream=None):
-    """topk_idx [T, k] int32 -> (offsets [E+1], perm [T*k], inv [T*k], status [1])."""
+def moe_permute(topk_idx: torch.Tensor, E: int, stream=None, use_workspace: bool = False):
+    """topk_idx [T, k] int32 -> (offsets [E+1], perm [T*k], inv [T*k], status [1]).
+    use_workspace: go through moe_permute_ws (many workgroups for large batches)."""
     T, k = topk_idx.shape
     dev = topk_idx.device
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    _check(lib().moe_permute(_ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(perm), _ptr(inv),
-                             _ptr(status), _stream(stream)))
+    if use_workspace:
+        nbytes = int(lib().moe_permute_workspace(T, k, E))
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _check(lib().moe_permute_ws(_ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(perm), _ptr(inv),
+                                    _ptr(status), _ptr(ws) if nbytes else None, nbytes,
+                                    _stream(stream)))
+    else:
+        _check(lib().moe_permute(_ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(perm), _ptr(inv),
+                                 _ptr(status), _stream(stream)))
     return offsets, perm, inv, status
 
 

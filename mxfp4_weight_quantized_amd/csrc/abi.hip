@@ -114,7 +114,8 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // ---- mxfp4_moe_mlp workspace layout ----
 struct MoeLayout {
-  size_t status, logits, idx, w, offsets, perm, inv, tiles, h, y, xq, xqs, hq, hqs, total;
+  size_t status, logits, idx, w, offsets, perm, inv, tiles, pcounts, h, y, xq, xqs, hq, hqs, total;
+  size_t pcounts_bytes;
   int tile_rows, max_tiles;
 };
 
@@ -137,6 +138,8 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
   L.perm = take((P + mx::kMaxTileRows) * 4);  // tile-row padding (see launch_permute)
   L.inv = take(P * 4);
   L.tiles = take((size_t)L.max_tiles * 8);
+  L.pcounts_bytes = mx::permute_sliced_workspace(d.T, d.k, d.E);  // 0: one-workgroup permutation
+  L.pcounts = take(L.pcounts_bytes);
   L.h = take(P * (size_t)d.F * 2);
   L.y = take(P * (size_t)d.H * 4);
   if (d.flags & MX_ACT_MXFP4) {
@@ -257,6 +260,32 @@ MX_API mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int3
   return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
 }
 
+MX_API size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E) {
+  if (check_routing_shape(T, 32, E, k) != MX_OK) return 0;
+  return align256(mx::permute_sliced_workspace(T, k, E));
+}
+
+MX_API mx_status moe_permute_ws(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
+                                void* ws, size_t ws_bytes, void* stream) {
+  mx_status st = check_routing_shape(T, 32, E, k);
+  if (st != MX_OK) return st;
+  if (!offsets) return fail(MX_ERR_NULL, "offsets is required");
+  if (T > 0 && (!topk_idx || !perm || !inv)) return fail(MX_ERR_NULL, "topk_idx, perm and inv are required");
+  const size_t need = align256(mx::permute_sliced_workspace(T, k, E));  // as moe_permute_workspace
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return fail(MX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (need > 0 && !aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
+  st = check_device();
+  if (st != MX_OK) return st;
+  ProfScope ps(PK_PERMUTE, (hipStream_t)stream);
+  hipError_t e = need > 0
+      ? mx::launch_permute_sliced(topk_idx, T, k, E, offsets, perm, inv, status, 0, nullptr, nullptr,
+                                  static_cast<int32_t*>(ws), (hipStream_t)stream)
+      : mx::launch_permute(topk_idx, T, k, E, offsets, perm, inv, status, 0, nullptr, nullptr,
+                           (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
+}
+
 MX_API size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc) {
   if (desc == nullptr || desc->struct_size != sizeof(mx_moe_desc)) return 0;
   if (check_routing_shape(desc->T, desc->H, desc->E, desc->k) != MX_OK || desc->F <= 0) return 0;
@@ -312,6 +341,9 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
             ? mx::launch_select_permute(sel_logits, d.T, d.k, d.E, const_cast<int32_t*>(idx),
                                         const_cast<float*>(tw), offsets, perm, inv, status,
                                         L.tile_rows, tiles, status + 1, s)
+        : L.pcounts_bytes > 0
+            ? mx::launch_permute_sliced(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows,
+                                        tiles, status + 1, reinterpret_cast<int32_t*>(w + L.pcounts), s)
             : mx::launch_permute(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows, tiles,
                                  status + 1, s);
   }

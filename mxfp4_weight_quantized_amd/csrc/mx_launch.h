@@ -30,9 +30,17 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
 // hold P + tile_rows entries: the padding (and rows past the last valid pair) are set to pair 0.
 constexpr int kMaxTileRows = 128;
 constexpr int kSelectMaxPairs = 2048;  // launch_select_permute: T * k at most this
+constexpr int kSlicePairs = 4096;      // launch_permute_sliced: pairs per workgroup
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm,
                           int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
                           int32_t* num_tiles, hipStream_t stream);
+// The same over many workgroups (two launches) for large batches: counts is workspace of
+// permute_sliced_workspace(T, k, E) bytes (0: use launch_permute).
+size_t permute_sliced_workspace(int T, int k, int E);
+hipError_t launch_permute_sliced(const int32_t* idx, int T, int k, int E, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv, int32_t* status, int tile_rows,
+                                 int2* tiles, int32_t* num_tiles, int32_t* counts,
+                                 hipStream_t stream);
 // The same after the top-k selection from the router logits (writes idx and w [T][k]).
 hipError_t launch_select_permute(const float* logits, int T, int k, int E, int32_t* idx, float* w,
                                  int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,

@@ -83,6 +83,13 @@ def test_route_and_permute_argument_errors(L):
     assert L.moe_route_topk(p, p, None, 4, 64, 32, 4, None, p, p, None) == mx.MX_ERR_NULL  # logits
     assert L.moe_route_topk(p, p, None, 0, 64, 32, 4, p, p, p, None) == mx.MX_OK  # T = 0
     assert L.moe_permute(p, 4, 2, 8, None, p, p, None, None) == mx.MX_ERR_NULL
+    need = mx.lib().moe_permute_workspace(4096, 4, 32)  # 16 384 pairs: the sliced path
+    assert need > 0 and need % 256 == 0 and mx.lib().moe_permute_workspace(64, 4, 32) == 0
+    assert L.moe_permute_ws(p, 4096, 4, 32, p, p, p, None, None, 0, None) == mx.MX_ERR_WORKSPACE
+    assert L.moe_permute_ws(p, 4096, 4, 32, p, p, p, None, p, need - 1, None) == mx.MX_ERR_WORKSPACE
+    assert L.moe_permute_ws(p, 4096, 4, 32, p, p, p, None, ctypes.c_void_p(0x10000010), need,
+                            None) == mx.MX_ERR_ALIGN
+    assert L.moe_permute_ws(p, 4, 9, 8, p, p, p, None, None, 0, None) == mx.MX_ERR_SHAPE
     assert L.moe_permute(p, 4, 0, 8, p, p, p, None, None) == mx.MX_ERR_SHAPE
 
 

@@ -86,6 +86,40 @@ def test_permute_bit_exact(T, k, E, skew):
     np.testing.assert_array_equal(inv, o_inv)
 
 
+@pytest.mark.parametrize("T,k,E,skew,bad", [(2048, 4, 32, 0, 0), (8192, 4, 32, 1, 0),
+                                            (4096, 4, 128, 0, 0), (10001, 3, 7, 1, 0),
+                                            (3000, 8, 256, 1, 0), (5000, 4, 16, 0, 1)])
+def test_permute_sliced_bit_exact(T, k, E, skew, bad):
+    """moe_permute_ws: large batches go through the per-slice histogram and scatter (two launches,
+    many workgroups); the result must be the oracle's counting sort element for element."""
+    r = np.random.default_rng(70 + T)
+    if skew:
+        p = np.exp(r.normal(0, 1.5, E)); p /= p.sum()
+        idx = np.stack([r.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    else:
+        idx = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    if bad:  # a few indices outside [0, E), in different slices
+        for pos in (5, 4100, 9000, T * k - 1):
+            idx.reshape(-1)[pos] = E + 3 if pos % 2 else -2
+    note("permute sliced P=%d E=%d bad=%d" % (idx.size, E, bad))
+    offs, perm, inv, status = mx.moe_permute(to_dev(idx), E, use_workspace=True)
+    torch.cuda.synchronize()
+    offs, perm, inv, st = offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), int(status.cpu()[0])
+    assert st == bad
+    if not bad:
+        o_offs, o_perm, o_inv = oracle.permute(idx, E)
+        np.testing.assert_array_equal(offs, o_offs)
+        np.testing.assert_array_equal(perm, o_perm)
+        np.testing.assert_array_equal(inv, o_inv)
+    # the one-workgroup path gives the same arrays (including skipped pairs)
+    o1, p1, i1, s1 = _permute(idx, E)
+    assert s1 == st
+    n = int(offs[-1])
+    np.testing.assert_array_equal(offs, o1)
+    np.testing.assert_array_equal(perm[:n], p1[:n])
+    np.testing.assert_array_equal(inv, i1)
+
+
 def test_permute_all_to_one_expert_and_empty_experts():
     idx = np.full((500, 1), 3, np.int32)
     offs, perm, inv, st = _permute(idx, 9)
