@@ -10,11 +10,12 @@
 // 통합") and dedicated MXFP4 kernels instead of a bf16 fallback ("Transformers 4.40 performance
 // upgrades for OpenAI GPT-OSS ...", section "MXFP4 4-Bit Quantization").
 //
-// Operand mapping (v_mfma_f32_16x16x32_bf16). The reduction order inside a product does not
-// matter, so the K axis is assigned to lanes in whole 32-element blocks: in one "super-step" of
-// four MFMAs, lane group g = lane/16 owns block 4j+g of the K tile, and MFMA s uses elements
-// [8s, 8s+8) of it. A lane therefore reads one whole 16-byte packed block (one scale byte) per
-// super-step and 64 contiguous bytes of the bf16 activation row.
+// Operand mapping (v_mfma_f32_16x16x32_bf16, or v_mfma_f32_32x32x16_bf16 for 32 x 32 fragments).
+// The reduction order inside a product does not matter, so the K axis is assigned to lanes in
+// whole 32-element blocks: in one "super-step" of four MFMAs, lane group g owns one block of the
+// K tile (g = lane/16 and block 4j+g for 16 x 16 fragments; g = lane/32 and block 2j+g for
+// 32 x 32), and MFMA s uses elements [8s, 8s+8) of it. A lane therefore reads one whole 16-byte
+// packed block (one scale byte) per super-step and 64 contiguous bytes of the bf16 activation row.
 //
 // LDS layout per stage: A [BM rows][KT*64 B], B [BN rows][KT*16 B], 16-byte chunks XOR-swizzled
 // by row so that the per-lane 16-byte reads of 8 consecutive rows hit distinct bank groups. The
@@ -52,20 +53,23 @@ struct GemmKArgs {
   int out_bf16;
 };
 
-// LDS swizzles. A 16-byte chunk c of LDS row r is stored at slot c ^ swz(r). The per-lane
-// 16-byte reads of one MFMA operand cover 16 consecutive rows at the same chunk; these XOR
-// patterns were measured conflict-free on gfx950 for exactly that access (SQ_LDS_BANK_CONFLICT
-// = 0 for ds_read_b128 over 16 rows x 4 lane groups; e.g. "r & 15" on 256-byte rows costs 2x):
-//   A rows (KT*64 bytes, >= 16 chunks): swz = ((r & 7) << 1) | ((r >> 3) & 1).
-//   B rows (KT*16 bytes): KT = 4 -> ((r >> 2) ^ (r >> 1)) & 3; KT = 8 -> (r ^ (r >> 3)) & 7;
-//   KT = 16 -> the A pattern.
-__device__ __forceinline__ int swz_a(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
-template <int KT>
-__device__ __forceinline__ int swz_b(int row) {
-  static_assert(KT == 4 || KT == 8 || KT == 16, "K tile");
-  if constexpr (KT == 4) return ((row >> 2) ^ (row >> 1)) & 3;
-  else if constexpr (KT == 8) return (row ^ (row >> 3)) & 7;
-  else return swz_a(row);  // 256-byte rows, as the bf16 A rows
+// LDS swizzles, by the number of 16-byte chunks per LDS row (CH). Chunk c of row r is stored at
+// slot c ^ swz(r). The per-lane 16-byte reads of one MFMA operand cover 16 (or 32) consecutive
+// rows at the same chunk; with 256-byte bank rows a chunk's bank group is (r % (16/CH))*CH + slot
+// for CH < 16, so the pattern must give distinct slots to the rows that share r % (16/CH) within
+// any 16 consecutive rows. Measured conflict-free on gfx950 for that access where CH >= 4
+// (SQ_LDS_BANK_CONFLICT = 0 for ds_read_b128 over 16 rows x 4 lane groups; e.g. "r & 15" on
+// 256-byte rows costs 2x):
+//   CH >= 16 (bf16 A rows of 4+ blocks): ((r & 7) << 1) | ((r >> 3) & 1)
+//   CH = 8 (128-byte rows): (r ^ (r >> 3)) & 7     CH = 4: ((r >> 2) ^ (r >> 1)) & 3
+//   CH = 2 (32-byte rows: rows r and r + 8 share a bank group): (r >> 3) & 1
+template <int CH>
+__device__ __forceinline__ int swz_rows(int row) {
+  static_assert(CH == 2 || CH == 4 || CH == 8 || CH >= 16, "LDS row size");
+  if constexpr (CH == 2) return (row >> 3) & 1;
+  else if constexpr (CH == 4) return ((row >> 2) ^ (row >> 1)) & 3;
+  else if constexpr (CH == 8) return (row ^ (row >> 3)) & 7;
+  else return ((row & 7) << 1) | ((row >> 3) & 1);
 }
 
 // Buffer views. Loads go through buffer resources (base address, byte size): each lane keeps a
@@ -185,40 +189,50 @@ __device__ __forceinline__ int weight_row_of(const GemmKArgs& p, int nt, int lro
   return min(nt * BN + lrow, p.N - 1);
 }
 
-// Local tile row of fragment f of wave column wn (lane row ln): gate_up waves take FN/2 gate
-// fragments and the FN/2 up fragments of the same output columns.
-template <int MODE, int BN, int WN, int FN>
+// Local tile row of fragment f (MF columns) of wave column wn (lane row ln): gate_up waves take
+// FN/2 gate fragments and the FN/2 up fragments of the same output columns.
+template <int MODE, int BN, int WN, int FN, int MF>
 __device__ __forceinline__ int frag_row(int wn, int f, int ln) {
   constexpr int BNH = BN / 2, TN = BN / WN;
   if (MODE == MODE_GATE_UP)
-    return ((f < FN / 2) ? wn * (BNH / WN) + f * 16 : BNH + wn * (BNH / WN) + (f - FN / 2) * 16) + ln;
-  return wn * TN + f * 16 + ln;
+    return ((f < FN / 2) ? wn * (BNH / WN) + f * MF : BNH + wn * (BNH / WN) + (f - FN / 2) * MF) + ln;
+  return wn * TN + f * MF + ln;
 }
 
-// Epilogue of a wave's FM x FN fragments (rows r0 + wm*TM + 16i + 4g + q, column lane ln):
-// down -> fp32 at the permuted row (the combine applies the routing weights: the epilogue needs
-// no index or weight loads); linear -> fp32 or bf16. (gate_up stores through LDS, below.)
-template <int MODE, int FM, int FN, int TM, int BN, int WN>
-__device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc)[FM][FN], int r0,
+// Row within an MF x MF accumulator fragment of value v of lane group g (the lane's column is
+// lane % MF): 16 x 16 -> 4g + v (v < 4); 32 x 32 -> 8(v/4) + 4g + v%4 (v < 16).
+template <int MF>
+__device__ __forceinline__ int acc_row(int g, int v) {
+  return MF == 32 ? 8 * (v >> 2) + 4 * g + (v & 3) : 4 * g + v;
+}
+template <int MF>
+using AccT = std::conditional_t<MF == 32, f32x16, f32x4>;
+
+// Epilogue of a wave's FM x FN fragments (rows r0 + wm*TM + MF*i + acc_row(g, v), column lane
+// ln): down -> fp32 at the permuted row (the combine applies the routing weights: the epilogue
+// needs no index or weight loads); linear -> fp32 or bf16. (gate_up stores through LDS, below.)
+template <int MODE, int FM, int FN, int TM, int BN, int WN, int MF>
+__device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&acc)[FM][FN], int r0,
                                            int row_end, int nt, int wm, int wn, int g, int ln) {
   constexpr int TN = BN / WN;
+  constexpr int NV = MF == 32 ? 16 : 4;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = r0 + wm * TM + i * 16 + 4 * g + q;
+    for (int q = 0; q < NV; ++q) {
+      const int r = r0 + wm * TM + i * MF + acc_row<MF>(g, q);
       if (r >= row_end) continue;
       if constexpr (MODE == MODE_DOWN) {
         float* y = reinterpret_cast<float*>(p.out);
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
-          const int col = nt * BN + wn * TN + f * 16 + ln;
+          const int col = nt * BN + wn * TN + f * MF + ln;
           if (col < p.N) y[(int64_t)r * p.N + col] = acc[i][f][q];
         }
       } else {
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
-          const int col = nt * BN + wn * TN + f * 16 + ln;
+          const int col = nt * BN + wn * TN + f * MF + ln;
           if (col >= p.N) continue;
           if (p.out_bf16)
             reinterpret_cast<uint16_t*>(p.out)[(int64_t)r * p.N + col] =
@@ -232,9 +246,10 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc
 }
 
 // Grouped / dense MXFP4 GEMM tile: out[BM rows x BN cols] = A times the weights (decoded).
-//   BM x BN workgroup tile, WM x WN waves, each wave a (BM/WM) x (BN/WN) tile of 16 x 16 MFMA
+//   BM x BN workgroup tile, WM x WN waves, each wave a (BM/WM) x (BN/WN) tile of MF x MF MFMA
 //   fragments; KT 32-element blocks per pipeline stage; STAGES (2 to 4) stages in flight.
-//   AFP4 = false: A is bf16 and the weights are decoded to bf16 for v_mfma_f32_16x16x32_bf16.
+//   AFP4 = false: A is bf16 and the weights are decoded to bf16 for v_mfma_f32_16x16x32_bf16
+//                 (MF = 16) or v_mfma_f32_32x32x16_bf16 (MF = 32).
 //   AFP4 = true:  A is MXFP4 too (packed codes + E8M0 scales, same layout as the weights) and
 //                 each 16 x 16 x 128 slice is one v_mfma_scale_f32_16x16x128_f8f6f4 with both
 //                 operands' block scales, so nothing is decoded.
@@ -243,7 +258,7 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc
 //   SCM_RESIDENT: all K/32 scale bytes of the tile's rows, once per tile. A tile's rows are one
 //     (two for gate_up) contiguous byte ranges, loaded as the aligned dwords that cover them:
 //     few, coalesced requests, which matters where streaming the weights is the bound.
-//   SCM_STAGE: per stage, each row's KT bytes as the SD = KT/4 + 1 aligned dwords that cover
+//   SCM_STAGE: per stage, each row's KT bytes as the SD = ceil(KT/4) + 1 aligned dwords that cover
 //     them (the first byte sits at a fixed shift, as stages advance by KT, a multiple of 4).
 //   SCM_BYTE: per stage, one byte per lane into its own dword (4x the LDS, exact at any size).
 // The dword forms may read past a row's last block (next row, or past K in the last stage):
@@ -251,19 +266,21 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const f32x4 (&acc
 // reads as zero, so weights whose scale array is not a whole number of dwords take SCM_BYTE.
 // Rows of the tile past its expert's last row are loaded as out-of-range (zeros, no traffic).
 template <int BM, int BN, int WM, int WN, int KT, int STAGES, int MODE, int GM, bool AFP4, int SCM,
-          bool TW>
+          bool TW, int MF>
 __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   constexpr int NW = WM * WN;
   constexpr int NT = NW * 64;
   constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / 16, FN = TN / 16;
+  constexpr int FM = TM / MF, FN = TN / MF;
+  constexpr int LG = 64 / MF;  // lane groups: each owns one 32-element K block per super-step
+  constexpr int NV = MF == 32 ? 16 : 4;  // accumulator values per lane and fragment
   constexpr bool SWIGLU = (MODE == MODE_GATE_UP);
   constexpr int BNH = BN / 2;
   constexpr int A_ROW = AFP4 ? KT * 16 : KT * 64, B_ROW = KT * 16;
   constexpr int A_STAGE = BM * A_ROW, B_STAGE = BN * B_ROW;
   using PA = DmaPlan<A_STAGE / 1024, NW>;
   using PB = DmaPlan<B_STAGE / 1024, NW>;
-  constexpr int SD = KT / 4 + 1;                           // scale dwords per row and stage
+  constexpr int SD = (KT + 3) / 4 + 1;                     // scale dwords per row and stage
   // (stage scale dwords padded to a whole number of instructions per wave: no repeated loads)
   constexpr int S_DW = SCM == SCM_STAGE ? ((TW ? KT * BN / 4 : BN * SD) + 64 * NW - 1) / (64 * NW) * (64 * NW)
                                         : SCM == SCM_BYTE ? BN * KT : 64;
@@ -278,15 +295,20 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   using PSA = DmaPlan<AFP4 ? SA_DW / 64 : 1, NW>;
   using PR = DmaPlan<RS_DW / 64, NW>;
   constexpr int IA = PA::I, IB = PB::I, IS = SCM == SCM_RESIDENT ? 0 : PS::I, ISA = AFP4 ? PSA::I : 0;
-  constexpr int SS = KT / 4;                               // super-steps per stage
+  constexpr int SS = KT / LG;                              // super-steps per stage
   constexpr int LPS = IS + ISA + IA + IB;                  // vector-memory ops per wave per stage
   static_assert(A_STAGE % 1024 == 0 && B_STAGE % 1024 == 0, "stage split");
-  static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "wave tile");
+  static_assert(FM * MF * WM == BM && FN * MF * WN == BN, "wave tile");
+  static_assert(MF == 16 || (MF == 32 && !AFP4), "32 x 32 fragments: bf16 activations only");
   static_assert(!SWIGLU || FN % 2 == 0, "gate/up fragment pairs");
-  static_assert(KT % 4 == 0 && (AFP4 || A_ROW >= 256) && STAGES >= 2 && STAGES <= 4, "pipeline");
+  static_assert(KT % LG == 0 && KT % 2 == 0 && STAGES >= 2 && STAGES <= 4, "pipeline");
+  constexpr int ACH = A_ROW / 16, BCH = B_ROW / 16;       // 16-byte chunks per LDS row
   static_assert((STAGES - 1) * LPS < 64, "vmcnt range");
   static_assert(BM <= NT, "one gathered row per thread");
   static_assert(!TW || (SCM != SCM_BYTE && BNH % 16 == 0), "tiled weights: dword scales, row groups");
+  // row-major dword stage scales keep a row's first byte at a fixed shift only if stages advance
+  // by a multiple of 4 blocks
+  static_assert(SCM != SCM_STAGE || TW || KT % 4 == 0, "row-major stage scales: 4-block stages");
 
   // The pipeline stages. The direct loads that fill them are inline asm the compiler does not
   // see, so it neither orders LDS reads after them nor tracks them: the kernel waits itself.
@@ -310,7 +332,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets go in M0
   const int wm = wave / WN, wn = wave % WN;
-  const int ln = lane & 15, g = lane >> 4;
+  const int ln = lane % MF, g = lane / MF;
 
   // ---- weight rows (within the expert) ----
   auto weight_row = [&](int lrow) -> int { return weight_row_of<MODE, BN>(p, nt, lrow); };
@@ -333,7 +355,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   for (int q = 0; q < IB; ++q) {
     const int off = PB::instr(wave, q) * 1024 + lane * 16;
     const int lrow = off / B_ROW;
-    const int chunk = ((off % B_ROW) >> 4) ^ swz_b<KT>(lrow);
+    const int chunk = ((off % B_ROW) >> 4) ^ swz_rows<BCH>(lrow);
     bblk[q] = chunk;
     if constexpr (TW) {  // 16-row group gr/16, block chunk: 256 bytes, row gr%16 at 16 * (gr%16)
       const uint32_t gr = (uint32_t)weight_row_u(lrow);
@@ -381,7 +403,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   int brow[FN], bsh[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
-    brow[f] = frag_row<MODE, BN, WN, FN>(wn, f, ln);
+    brow[f] = frag_row<MODE, BN, WN, FN, MF>(wn, f, ln);
     // LDS byte of the row's block 0 (of the stage, or of K for resident scales)
     if constexpr (TW) {
       bsh[f] = brow[f];
@@ -464,11 +486,11 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     const int off = PA::instr(wave, q) * 1024 + lane * 16;
     const int lrow = off / A_ROW;
     if constexpr (AFP4) {
-      const int chunk = ((off % A_ROW) >> 4) ^ swz_b<KT>(lrow);
+      const int chunk = ((off % A_ROW) >> 4) ^ swz_rows<ACH>(lrow);
       ablk[q] = chunk;
       voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K >> 1) + chunk * 16;
     } else {
-      const int chunk = ((off % A_ROW) >> 4) ^ swz_a(lrow);
+      const int chunk = ((off % A_ROW) >> 4) ^ swz_rows<ACH>(lrow);
       ablk[q] = chunk >> 2;
       voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K * 2) + chunk * 16;
     }
@@ -485,7 +507,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   int ash[AFP4 ? FM : 1];  // FP4 A: byte of block 0 of each fragment row's scales
 #pragma unroll
   for (int i = 0; i < (AFP4 ? FM : 0); ++i) {
-    const int r = wm * TM + i * 16 + ln;
+    const int r = wm * TM + i * MF + ln;
     ash[i] = r * SD * 4 + (int)(((uint32_t)sArow[r] * (uint32_t)nb) & 3u);
   }
   auto issue_a = [&](Stage& sg, int kt) {
@@ -509,15 +531,19 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   };
   for (int q = 0; q < STAGES - 1 && q < ntk; ++q) issue_a(stg[q], q);
 
-  f32x4 acc[FM][FN];
+  AccT<MF> acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) acc[i][j][v] = 0.f;
 
-  // One stage of MFMAs.
+  // One stage of MFMAs. A super-step covers LG K blocks, lane group g owning block LG*j + g.
   //   bf16 A: per super-step, read the wave's A fragments and packed B blocks; decode B fragment
-  //   f+1 (two codes per cvt, other register set) while the 4 x FM MFMAs of fragment f run.
+  //   f+1 (two codes per cvt, other register set) while the 4 x FM MFMAs of fragment f run
+  //   (16 x 16 x 32, or 32 x 32 x 16 when MF = 32: MFMA s takes elements [8s, 8s+8) of the
+  //   lane's block either way).
   //   FP4 A: per super-step and fragment pair, one scaled MFMA on the raw blocks and scale bytes.
   auto compute = [&](const Stage& sg, int kt) {
     const uint8_t* As = sg.A;
@@ -528,24 +554,24 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     const bool partial = (kt + 1) * KT > nb;  // blocks past K: zero codes, scale read as 1.0
 #pragma unroll
     for (int j = 0; j < SS; ++j) {
-      const bool past = partial && kt * KT + 4 * j + g >= nb;
+      const bool past = partial && kt * KT + LG * j + g >= nb;
       u32x4 w[FN];
       uint32_t scb[FN];
 #pragma unroll
       for (int f = 0; f < FN; ++f) {
         const int r = brow[f];
-        w[f] = lds_read_b128(Bsm + r * B_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
+        w[f] = lds_read_b128(Bsm + r * B_ROW + (((LG * j + g) ^ swz_rows<BCH>(r)) << 4));
         // (tiled weights: blocks past K hold zero codes and zero scales, 0 * 2^-127 = 0)
-        scb[f] = (!TW && past) ? 127u : (uint32_t)Scb[bsh[f] + (4 * j + g) * SBS];
+        scb[f] = (!TW && past) ? 127u : (uint32_t)Scb[bsh[f] + (LG * j + g) * SBS];
       }
       if constexpr (AFP4) {
         u32x4 a[FM];
         uint32_t sca[FM];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 16 + ln;
-          a[i] = lds_read_b128(As + r * A_ROW + (((4 * j + g) ^ swz_b<KT>(r)) << 4));
-          sca[i] = past ? 127u : (uint32_t)Sab[ash[i] + 4 * j + g];
+          const int r = wm * TM + i * MF + ln;
+          a[i] = lds_read_b128(As + r * A_ROW + (((LG * j + g) ^ swz_rows<ACH>(r)) << 4));
+          sca[i] = past ? 127u : (uint32_t)Sab[ash[i] + LG * j + g];
         }
 #pragma unroll
         for (int f = 0; f < FN; ++f)
@@ -556,28 +582,49 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
         bf16x8 a[FM][4];
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
-          const int r = wm * TM + i * 16 + ln;
+          const int r = wm * TM + i * MF + ln;
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             a[i][s] = u32x4_as_bf16x8(
-                lds_read_b128(As + r * A_ROW + ((((4 * j + g) * 4 + s) ^ swz_a(r)) << 4)));
+                lds_read_b128(As + r * A_ROW + ((((LG * j + g) * 4 + s) ^ swz_rows<ACH>(r)) << 4)));
         }
         float sc[FN];
 #pragma unroll
         for (int f = 0; f < FN; ++f) sc[f] = e8m0_scale(scb[f]);
-        bf16x8 b[2][4];
+        if constexpr (MF == 32) {
+          // 32 x 32 fragments are few (FM x FN = 4 for a 64 x 64 wave tile) and a 32x32x16 MFMA
+          // has about twice the latency of the 16x16x32 form: go round all accumulators per
+          // slice s (each MFMA then has the other FM*FN - 1 between it and its predecessor) and
+          // decode slice s+1 of every fragment while slice s's MFMAs run.
+          bf16x8 b[FN][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
+          for (int f = 0; f < FN; ++f) b[f][0] = fp4x8_to_bf16x8(w[f][0], sc[f]);
 #pragma unroll
-        for (int f = 0; f < FN; ++f) {
-          if (f + 1 < FN) {
+          for (int s = 0; s < 4; ++s) {
+            if (s + 1 < 4) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) b[(f + 1) & 1][s] = fp4x8_to_bf16x8(w[f + 1][s], sc[f + 1]);
+              for (int f = 0; f < FN; ++f) b[f][s + 1] = fp4x8_to_bf16x8(w[f][s + 1], sc[f]);
+            }
+#pragma unroll
+            for (int f = 0; f < FN; ++f)
+#pragma unroll
+              for (int i = 0; i < FM; ++i) acc[i][f] = mfma32x32x16(a[i][s], b[f][s], acc[i][f]);
           }
+        } else {
+          bf16x8 b[2][4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
+          for (int s = 0; s < 4; ++s) b[0][s] = fp4x8_to_bf16x8(w[0][s], sc[0]);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
+          for (int f = 0; f < FN; ++f) {
+            if (f + 1 < FN) {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) b[(f + 1) & 1][s] = fp4x8_to_bf16x8(w[f + 1][s], sc[f + 1]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+              for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
+          }
         }
       }
     }
@@ -629,12 +676,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NV; ++q)
 #pragma unroll
         for (int f = 0; f < FN / 2; ++f) {
           const float gt = acc[i][f][q], up = acc[i][FN / 2 + f][q];
           const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
-          sh[(wm * TM + i * 16 + 4 * g + q) * LDH + wn * (BNH / WN) + f * 16 + ln] =
+          sh[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDH + wn * (BNH / WN) + f * MF + ln] =
               (uint16_t)f32_to_bf16_bits(hv);
         }
     barrier_lds();
@@ -656,10 +703,10 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NV; ++q)
 #pragma unroll
         for (int f = 0; f < FN; ++f)
-          sy[(wm * TM + i * 16 + 4 * g + q) * LDY + wn * TN + f * 16 + ln] = acc[i][f][q];
+          sy[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDY + wn * TN + f * MF + ln] = acc[i][f][q];
     barrier_lds();
     float* y = reinterpret_cast<float*>(p.out);
     for (int c = tid; c < BM * CPR; c += NT) {
@@ -670,22 +717,22 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
             *reinterpret_cast<const float4*>(sy + lr * LDY + cc * 4);
     }
   } else {
-    store_tile<MODE, FM, FN, TM, BN, WN>(p, acc, r0, row_end, nt, wm, wn, g, ln);
+    store_tile<MODE, FM, FN, TM, BN, WN, MF>(p, acc, r0, row_end, nt, wm, wn, g, ln);
   }
 }
 
 // One kernel name per role, so profiles show which product a launch is.
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM, bool TW>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM, bool TW, int MF>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_gate_up_swiglu_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4, SCM, TW>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_GATE_UP, GM, AFP4, SCM, TW, MF>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM, bool TW>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM, bool TW, int MF>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void moe_down_weighted_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4, SCM, TW>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_DOWN, GM, AFP4, SCM, TW, MF>(p);
 }
-template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM>
+template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool AFP4, int SCM, int MF>
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_kernel(GemmKArgs p) {
-  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM, false>(p);
+  gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM, false, MF>(p);
 }
 // out[t][n] = sum_{j < k} w[t][j] * Y[inv[t*k + j]][n] in slot order (each product rounded to
 // fp32, then summed); pairs with inv < 0 (skipped routing indices) contribute nothing. Eight
@@ -726,11 +773,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // ---- tile configurations ----
-// Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles, four waves of 64 x 64, a
-// 2-stage pipeline of 4-block stages, two workgroups per CU so that one's barrier waits and tile
-// prologue overlap the other's MFMAs. Measured on the 20B prefill shapes: 128 x 256 (eight
-// waves, 2 or 3 stages) about 10% slower and 128 x 384 about 3% slower, both one workgroup per
-// CU whose eight waves stall at the same barriers.
+// Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles, four waves of 64 x 64 in
+// 32 x 32 fragments, 2-block (64-element) stages, 2 stages, four workgroups per CU. Measured on
+// the 20B prefill shape (T = 8192, tiled weights): the mainloop alone (no loads) runs at about
+// 70% of the bf16 peak and the loads alone take longer than that, so what pays is hiding load
+// latency with more resident workgroups, not more MFMA throughput. Small stages buy the
+// residency: 17 KB per stage lets four workgroups share a CU's LDS (0.97 -> 0.88 ms for gate_up
+// against 4-block stages of 16 x 16 fragments at two per CU; three per CU with 3 stages 0.91 ms;
+// 2-block stages need the 32 x 32 form, whose two lane groups split a stage's two blocks). The
+// 16 x 16 form with 4-block stages at two per CU, 128 x 256 tiles of eight waves and GM 2 or 8
+// measured slower.
 // Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, the tile's
 // weight scales resident, 4-block stages x 3, three workgroups per CU. Weight streaming
 // dominates and is bound by the loads in flight per CU: more resident workgroups beat deeper or
@@ -740,22 +792,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 // OCC: workgroups per CU the register allocation must leave room for (the second launch bound
 // is in waves per SIMD).
 // SCM: how the weight scales reach LDS (resident per tile where weight streaming is the bound).
-struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2, SCM = SCM_STAGE; };
-struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 4, ST = 2, GM = 4, OCC = 2, SCM = SCM_STAGE; };
-struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT; };
-struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT; };
+// MF: MFMA fragment size, 32 (v_mfma_f32_32x32x16_bf16) or 16; FP4 activations always take 16.
+struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 2, ST = 2, GM = 4, OCC = 4, SCM = SCM_STAGE, MF = 32; };
+struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 2, ST = 2, GM = 4, OCC = 4, SCM = SCM_STAGE, MF = 32; };
+struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT, MF = 16; };
+struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT, MF = 16; };
 // Activation variant, prefill-shaped: FP4 activations take a quarter of the LDS and need no
 // decode instructions, so wide tiles with fewer bytes per MFMA pay: 128 x 512 (gate_up, eight
 // waves of 64 x 128) and 128 x 384 (down: 2880 columns split into 7.5 rather than 5.6 tiles),
 // 3 stages. Measured on the 20B prefill shapes against 64 x 256 (about 15% slower), 128 x 256,
 // 128 x 384 with 2 or 4 stages and 8-block stages (spills).
-struct CfgPreGU4 { static constexpr int BM = 128, BN = 512, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE; };
-struct CfgPreDn4 { static constexpr int BM = 128, BN = 384, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE; };
+struct CfgPreGU4 { static constexpr int BM = 128, BN = 512, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
+struct CfgPreDn4 { static constexpr int BM = 128, BN = 384, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
 // Few pairs (a handful of experts touched): the down GEMM (2880 columns: 23 tiles of 128 per
 // expert) takes 64-column tiles, twice the workgroups to stream the few experts' weights
 // (120B-shaped decode, T = 1: 15.9 -> 14.1 us; gate_up, which has twice the columns, measured no
 // better with them).
-struct CfgTinyDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 4, SCM = SCM_RESIDENT; };
+struct CfgTinyDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 4, SCM = SCM_RESIDENT, MF = 16; };
 constexpr int kPrefillRows = 64, kPrefillRows4 = 128;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
 static_assert(CfgPreGU4::BM == kPrefillRows4 && CfgPreDn4::BM == kPrefillRows4, "one tile list");
@@ -771,12 +824,13 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
   constexpr int GN = 32 / C::GM;
   const int64_t supers = (int64_t)((m_tiles + C::GM - 1) / C::GM) * ((n_tiles + GN - 1) / GN);
   const dim3 grid((unsigned)(8 * 32 * ((supers + 7) / 8))), block(C::WM * C::WN * 64);
+  constexpr int MF = AFP4 ? 16 : C::MF;
   if constexpr (MODE == MODE_GATE_UP)
-    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, TW>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, TW, MF>), grid, block, 0, stream, a);
   else if constexpr (MODE == MODE_DOWN)
-    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, TW>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((moe_down_weighted_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, TW, MF>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((linear_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, MF>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -789,8 +843,11 @@ hipError_t launch_linear_tiles(const GemmKArgs& g, int M, int N, hipStream_t str
   if (M > 64) {
     using C = std::conditional_t<AFP4, CfgPreGU4, CfgPreGU>;
     const int mt = (M + C::BM - 1) / C::BM;
-    return dw ? launch_gemm<C, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
-              : launch_gemm<C, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
+    if constexpr (C::KT % 4 != 0)  // row-major stage scales need 4-block stages
+      return launch_gemm<C, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
+    else
+      return dw ? launch_gemm<C, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
+                : launch_gemm<C, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
   }
   const int mt = (M + CfgDecDn::BM - 1) / CfgDecDn::BM;
   if (dw && nb <= kResidentNb) return launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_RESIDENT>(g, mt, N, stream);
@@ -857,9 +914,12 @@ int moe_max_tiles(int T, int k, int E, int tile_rows) {
 }
 
 namespace {
+// Row-major weights with stages of other than a multiple of 4 blocks read stage scales bytewise.
+template <class C, bool TW>
+constexpr int stage_scm() { return (C::SCM == SCM_STAGE && !TW && C::KT % 4 != 0) ? SCM_BYTE : C::SCM; }
 template <class C, int MODE, bool AFP4, bool TW>
 hipError_t launch_moe_gemm(const GemmKArgs& g, int m_tiles, int n_cols, hipStream_t stream) {
-  return launch_gemm<C, MODE, AFP4, C::SCM, TW>(g, m_tiles, n_cols, stream);
+  return launch_gemm<C, MODE, AFP4, stage_scm<C, TW>(), TW>(g, m_tiles, n_cols, stream);
 }
 template <bool TW>
 hipError_t gate_up_tw(GemmKArgs g, const MoeGemmArgs& m, hipStream_t stream) {
