@@ -27,7 +27,10 @@ constexpr int kSpreadBelow = 512;
 
 // SELECT: the workgroup covers all experts of its tokens (n_groups * 16 >= E); it keeps the
 // logits tile in LDS and its waves (one per token) also make the top-k selection.
-template <bool SELECT>
+// BATCH: 32-element steps whose loads go out together (one memory round trip per batch): 8 where
+// 16 splits leave each wave about 6 steps, 12 where fewer splits leave it 12 or more (20B-shaped
+// router, T = 8192: 40 -> 34 us; 12 with 16 splits only adds masked re-reads, 15 -> 18 us).
+template <bool SELECT, int BATCH>
 __global__ __launch_bounds__(1024) void route_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ br,
     int T, int H, int E, int n_groups, int n_splits, float* __restrict__ logits, int k,
@@ -50,10 +53,9 @@ __global__ __launch_bounds__(1024) void route_logits_kernel(
   const uint16_t* xa = x + (int64_t)tok * H + g * 8;
   const uint16_t* wb = wr + (int64_t)ex * H + g * 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // batches of 8 steps (what fits in the registers of 16 waves), branch-free: all loads of a
-  // batch go out before its MFMAs; steps past the split's end re-read its last step and are
-  // zeroed, so they add nothing
-  constexpr int kBatch = 8;
+  // batches of BATCH steps, branch-free: all loads of a batch go out before its MFMAs; steps past
+  // the split's end re-read its last step and are zeroed, so they add nothing
+  constexpr int kBatch = BATCH;
   for (int st = s0; st < s1; st += kBatch) {
     u32x4 a[kBatch], b[kBatch];
 #pragma unroll
@@ -123,7 +125,7 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   if (T == 0) return hipSuccess;
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
   const int splits = min(16, H / 32);
-  hipLaunchKernelGGL(route_logits_kernel<false>, dim3(tiles, groups), dim3(64 * splits), 0, stream,
+  hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups), dim3(64 * splits), 0, stream,
                      x, wr, br, T, H, E, 1, splits, logits, 0, nullptr, nullptr);
   return hipGetLastError();
 }
@@ -137,12 +139,17 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
   const int G = (tiles * groups <= kSpreadBelow) ? 1 : groups;
   const int splits = min(16 / G, H / 32);
   if (G == groups) {  // one workgroup covers all experts of its tokens: select in the same kernel
-    hipLaunchKernelGGL(route_logits_kernel<true>, dim3(tiles, 1), dim3(64 * G * splits), 0, stream,
-                       x, wr, br, T, H, E, G, splits, logits, k, idx, w);
+    if (splits >= 16)
+      hipLaunchKernelGGL((route_logits_kernel<true, 8>), dim3(tiles, 1), dim3(64 * G * splits), 0, stream,
+                         x, wr, br, T, H, E, G, splits, logits, k, idx, w);
+    else
+      hipLaunchKernelGGL((route_logits_kernel<true, 12>), dim3(tiles, 1), dim3(64 * G * splits), 0, stream,
+                         x, wr, br, T, H, E, G, splits, logits, k, idx, w);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(route_logits_kernel<false>, dim3(tiles, groups / G), dim3(64 * G * splits), 0,
-                     stream, x, wr, br, T, H, E, G, splits, logits, k, idx, w);
+  // (G is 1 here: one expert group per workgroup)
+  hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups), dim3(64 * splits), 0,
+                     stream, x, wr, br, T, H, E, 1, splits, logits, k, idx, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k,
