@@ -323,6 +323,9 @@ def bench_linear(args, name, cfg):
     n_w = max(1, math.ceil(2 * CACHE_BYTES / wbytes))
     wsets = [(p, sc)] + [(p.clone(), sc.clone()) for _ in range(n_w - 1)]
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = mx.mxfp4_linear_workspace(M, K, N, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws_ptr = ws.data_ptr() if ws_bytes else None
     L = mx.lib()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -330,7 +333,7 @@ def bench_linear(args, name, cfg):
     def step(i):
         pp, ss = wsets[i % n_w]
         st = L.mxfp4_linear(x.data_ptr(), M, K, pp.data_ptr(), ss.data_ptr(), N, out.data_ptr(),
-                            mx.MX_BF16, 0, None, 0, sh)
+                            mx.MX_BF16, 0, ws_ptr, ws_bytes, sh)
         if st != 0:
             raise mx.MXError(st, mx.last_error())
 

@@ -188,8 +188,10 @@ mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void
  * matrix product the MoE MLP's grouped GEMMs are made of; [EN] "MXFP4 4-Bit Quantization").
  *   x [M][K] bf16; packed [N][K/2], scales [N][K/32]; y [M][N] fp32 or bf16 (y_dtype).
  *   flags: 0 or MX_ACT_MXFP4 (x is MXFP4-quantized along K first; needs the workspace).
- *   ws: mxfp4_linear_workspace(M, K, N, flags) bytes, 256-byte aligned, owned by the caller
- *   (may be 0 and ws NULL when flags == 0); it holds the quantized x.
+ *   ws: mxfp4_linear_workspace(M, K, N, flags) bytes, 256-byte aligned, owned by the caller,
+ *   contents need not be initialized (ws may be NULL when that size is 0); it holds the
+ *   quantized x (MX_ACT_MXFP4) and, for decode-sized M (<= 64), the fp32 partial sums of the
+ *   workgroups that split K (summed in a fixed order: results do not depend on timing).
  *   K % 32 == 0, K <= MX_MAX_K; x, packed, y 16-byte aligned.
  * ---------------------------------------------------------------------------------------------- */
 size_t mxfp4_linear_workspace(int32_t M, int32_t K, int32_t N, uint32_t flags);

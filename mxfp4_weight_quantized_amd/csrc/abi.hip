@@ -402,10 +402,20 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   return ok();
 }
 
+// Linear workspace: [quantized x, its scales] (MX_ACT_MXFP4) then [fp32 partial sums of the K
+// splits] (decode-sized M).
+static size_t linear_xq_bytes(int32_t M, int32_t K, uint32_t flags) {
+  return (flags & MX_ACT_MXFP4) ? align256((size_t)M * K / 2) + align256((size_t)M * K / 32) : 0;
+}
+static size_t linear_part_bytes(int32_t M, int32_t K, int32_t N) {
+  if (M <= 0 || K < 32 || N <= 0) return 0;
+  const int S = mx::linear_k_splits(M, K, N);
+  return S > 1 ? align256((size_t)S * M * N * 4) : 0;
+}
+
 MX_API size_t mxfp4_linear_workspace(int32_t M, int32_t K, int32_t N, uint32_t flags) {
   if (M < 0 || K < 0 || N < 0) return 0;
-  if (flags & MX_ACT_MXFP4) return align256((size_t)M * K / 2) + align256((size_t)M * K / 32);
-  return 0;
+  return linear_xq_bytes(M, K, flags) + linear_part_bytes(M, K, N);
 }
 
 MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uint8_t* packed,
@@ -419,12 +429,16 @@ MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uin
   if (M == 0 || N == 0) return ok();
   if (!x || !packed || !scales || !y) return fail(MX_ERR_NULL, "x, packed, scales and y are required");
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 16) || !aligned(y, 16)) return fail(MX_ERR_ALIGN, "x, packed, scales and y must be 16-byte aligned");
-  if (flags & MX_ACT_MXFP4) {
-    if (ws == nullptr || ws_bytes < mxfp4_linear_workspace(M, K, N, flags)) return fail(MX_ERR_WORKSPACE, "workspace too small");
+  const size_t need = mxfp4_linear_workspace(M, K, N, flags);
+  if (need > 0) {
+    if (ws == nullptr || ws_bytes < need) return fail(MX_ERR_WORKSPACE, "workspace too small (%zu bytes needed)", need);
     if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
   mx_status st = check_device();
   if (st != MX_OK) return st;
+  float* partials = linear_part_bytes(M, K, N) > 0
+                        ? reinterpret_cast<float*>(static_cast<char*>(ws) + linear_xq_bytes(M, K, flags))
+                        : nullptr;
   if (flags & MX_ACT_MXFP4) {
     uint8_t* xq = static_cast<uint8_t*>(ws);
     uint8_t* xqs = xq + align256((size_t)M * K / 2);
@@ -435,11 +449,13 @@ MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uin
     }
     if (e != hipSuccess) return hip_fail(e, "x quantize launch");
     ProfScope ps(PK_LINEAR, (hipStream_t)stream);
-    e = mx::launch_linear_mxact(xq, xqs, M, K, packed, scales, N, y, y_dtype == MX_BF16, (hipStream_t)stream);
+    e = mx::launch_linear_mxact(xq, xqs, M, K, packed, scales, N, y, y_dtype == MX_BF16, partials,
+                                (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "linear launch");
   }
   ProfScope ps(PK_LINEAR, (hipStream_t)stream);
-  hipError_t e = mx::launch_linear(x, M, K, packed, scales, N, y, y_dtype == MX_BF16, (hipStream_t)stream);
+  hipError_t e = mx::launch_linear(x, M, K, packed, scales, N, y, y_dtype == MX_BF16, partials,
+                                   (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "linear launch");
 }
 

@@ -51,6 +51,9 @@ struct GemmKArgs {
   int F;                      // gate_up: up rows start at F
   void* out;
   int out_bf16;
+  int gn;                     // column tiles per XCD super-tile (set by the launcher)
+  int k_splits;               // linear only: K range split over blockIdx.z (<= 1: none); out
+  int64_t part_stride;        //   then takes fp32 partial sums, split z at z * part_stride
 };
 
 // LDS swizzles, by the number of 16-byte chunks per LDS row (CH). Chunk c of row r is stored at
@@ -155,7 +158,7 @@ struct DmaPlan {
 template <int BM, int GM>
 __device__ __forceinline__ bool pick_tile(const GemmKArgs& p, int& e, int& r0, int& row_end,
                                           int& nt) {
-  constexpr int GN = 32 / GM;
+  const int GN = p.gn;
   const bool grouped = p.tiles != nullptr;
   const int num_mt = grouped ? *p.num_tiles : (p.M + BM - 1) / BM;
   const int sm_count = (num_mt + GM - 1) / GM, sn_count = (p.n_tiles + GN - 1) / GN;
@@ -230,6 +233,7 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&
           if (col < p.N) y[(int64_t)r * p.N + col] = acc[i][f][q];
         }
       } else {
+        const int64_t zoff = p.k_splits > 1 ? (int64_t)blockIdx.z * p.part_stride : 0;
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           const int col = nt * BN + wn * TN + f * MF + ln;
@@ -238,7 +242,7 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&
             reinterpret_cast<uint16_t*>(p.out)[(int64_t)r * p.N + col] =
                 (uint16_t)f32_to_bf16_bits(acc[i][f][q]);
           else
-            reinterpret_cast<float*>(p.out)[(int64_t)r * p.N + col] = acc[i][f][q];
+            reinterpret_cast<float*>(p.out)[zoff + (int64_t)r * p.N + col] = acc[i][f][q];
         }
       }
     }
@@ -450,7 +454,15 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
                  &sg.B[PB::instr(wave, q) * 1024]);
     }
   };
-  const int ntk = (nb + KT - 1) / KT;
+  // K stages of this workgroup: all of them, or (split linear) split blockIdx.z's share
+  int kt0 = 0, ntk = (nb + KT - 1) / KT;
+  if constexpr (MODE == MODE_LINEAR) {
+    if (p.k_splits > 1) {
+      const int all = ntk, z = blockIdx.z;
+      kt0 = z * all / p.k_splits;
+      ntk = (z + 1) * all / p.k_splits - kt0;
+    }
+  }
   if constexpr (SCM == SCM_RESIDENT) {  // first of all loads: every stage wait covers it
 #pragma unroll
     for (int q = 0; q < PR::I; ++q) {
@@ -469,7 +481,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
       dma_b32(rS, (d >= 0 && vo < end) ? vo : kOutOfRange, 0, &sRes[PR::instr(wave, q) * 64]);
     }
   }
-  for (int q = 0; q < STAGES - 1 && q < ntk; ++q) issue_w(stg[q], q);
+  for (int q = 0; q < STAGES - 1 && q < ntk; ++q) issue_w(stg[q], kt0 + q);
   if (p.a_gather != nullptr) {  // consumed only now, after the weight loads went out
     int gathered = gv[0];
 #pragma unroll
@@ -529,7 +541,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
                  0, &sg.A[PA::instr(wave, q) * 1024]);
     }
   };
-  for (int q = 0; q < STAGES - 1 && q < ntk; ++q) issue_a(stg[q], q);
+  for (int q = 0; q < STAGES - 1 && q < ntk; ++q) issue_a(stg[q], kt0 + q);
 
   AccT<MF> acc[FM][FN];
 #pragma unroll
@@ -656,10 +668,10 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     barrier_lds();
     if (kt + STAGES - 1 < ntk) {
       Stage& sn = stg[st == 0 ? STAGES - 1 : st - 1];
-      issue_w(sn, kt + STAGES - 1);
-      issue_a(sn, kt + STAGES - 1);
+      issue_w(sn, kt0 + kt + STAGES - 1);
+      issue_a(sn, kt0 + kt + STAGES - 1);
     }
-    compute(stg[st], kt);
+    compute(stg[st], kt0 + kt);
     st = st == STAGES - 1 ? 0 : st + 1;
   }
 
@@ -772,6 +784,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// Split linear: out[i] = sum over z of part[z * n + i], in split order, as fp32 or bf16.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int S,
+                                                           int64_t n, void* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int z = 1; z < S; ++z) s += part[(int64_t)z * n + i];
+  if (BF16_OUT) reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(s);
+  else reinterpret_cast<float*>(out)[i] = s;
+}
+
 // ---- tile configurations ----
 // Prefill-shaped (many rows per expert): 64 x 256 workgroup tiles, four waves of 64 x 64 in
 // 32 x 32 fragments, 2-block (64-element) stages, 2 stages, four workgroups per CU. Measured on
@@ -820,10 +844,18 @@ hipError_t launch_gemm(GemmKArgs a, int m_tiles, int n_cols, hipStream_t stream)
                                              : (n_cols + C::BN - 1) / C::BN;
   if (m_tiles <= 0 || n_tiles <= 0) return hipSuccess;
   a.n_tiles = n_tiles;
-  // grid: 8 XCDs x (super-tiles per XCD) x (tiles per super-tile), from the row-tile bound
-  constexpr int GN = 32 / C::GM;
-  const int64_t supers = (int64_t)((m_tiles + C::GM - 1) / C::GM) * ((n_tiles + GN - 1) / GN);
-  const dim3 grid((unsigned)(8 * 32 * ((supers + 7) / 8))), block(C::WM * C::WN * 64);
+  // grid: 8 XCDs x (super-tiles per XCD) x (tiles per super-tile), from the row-tile bound.
+  // Super-tiles of 32 tiles (activation and weight tiles shared in an XCD's L2; for decode tiles,
+  // neighbouring column tiles of one expert, adjacent in memory, streamed by one XCD). Where that
+  // gives fewer super-tiles than XCDs (a dense linear of one row tile: 45 column tiles had run
+  // on 2 of the 8 XCDs) the groups narrow until every XCD gets one.
+  const int m_sup = (m_tiles + C::GM - 1) / C::GM;
+  int GN = 32 / C::GM;
+  if ((int64_t)m_sup * ((n_tiles + GN - 1) / GN) < 8) GN = std::max(1, n_tiles / ((8 + m_sup - 1) / m_sup));
+  a.gn = GN;
+  const int64_t supers = (int64_t)m_sup * ((n_tiles + GN - 1) / GN);
+  const unsigned zs = (MODE == MODE_LINEAR && a.k_splits > 1) ? (unsigned)a.k_splits : 1u;
+  const dim3 grid((unsigned)(8 * C::GM * GN * ((supers + 7) / 8)), 1, zs), block(C::WM * C::WN * 64);
   constexpr int MF = AFP4 ? 16 : C::MF;
   if constexpr (MODE == MODE_GATE_UP)
     hipLaunchKernelGGL((moe_gate_up_swiglu_kernel<C::BM, C::BN, C::WM, C::WN, C::KT, C::ST, C::GM, C::OCC, AFP4, SCM, TW, MF>), grid, block, 0, stream, a);
@@ -850,12 +882,39 @@ hipError_t launch_linear_tiles(const GemmKArgs& g, int M, int N, hipStream_t str
                 : launch_gemm<C, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
   }
   const int mt = (M + CfgDecDn::BM - 1) / CfgDecDn::BM;
-  if (dw && nb <= kResidentNb) return launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_RESIDENT>(g, mt, N, stream);
+  // (split K: each split needs only its stages' scales)
+  if (dw && nb <= kResidentNb && g.k_splits <= 1)
+    return launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_RESIDENT>(g, mt, N, stream);
   return dw ? launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
             : launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
 }
 
 bool use_prefill_tiles(int T, int k, int E) { return (int64_t)T * k >= 64LL * E; }
+
+// Split linear: output tiles in fp32 partial sums, then their sum in split order into y.
+template <bool AFP4>
+hipError_t launch_linear_split(GemmKArgs g, int M, int N, void* y, bool y_bf16, float* partials,
+                               hipStream_t stream) {
+  const int S = linear_k_splits(M, g.K, N);
+  if (S > 1) {
+    g.out = partials;
+    g.out_bf16 = 0;
+    g.k_splits = S;
+    g.part_stride = (int64_t)M * N;
+  } else {
+    g.out = y;
+    g.out_bf16 = y_bf16 ? 1 : 0;
+  }
+  hipError_t e = launch_linear_tiles<AFP4>(g, M, N, stream);
+  if (e != hipSuccess || S <= 1) return e;
+  const int64_t n = (int64_t)M * N;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (y_bf16)
+    hipLaunchKernelGGL(split_reduce_kernel<true>, dim3(grid), dim3(256), 0, stream, partials, S, n, y);
+  else
+    hipLaunchKernelGGL(split_reduce_kernel<false>, dim3(grid), dim3(256), 0, stream, partials, S, n, y);
+  return hipGetLastError();
+}
 // at most min(T*k, E) experts touched: with 128-column tiles fewer than two workgroups per CU
 bool use_tiny_tiles(int T, int k, int E, int N) {
   return (int64_t)std::min(T * k, E) * ((N + 127) / 128) < 512;
@@ -971,8 +1030,20 @@ hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Decode-sized dense linears (M <= 64) have few output tiles (45 for N = 5760): each tile's K is
+// split over several workgroups, enough for about three per CU while every split keeps at least
+// 3 pipeline stages of 4 blocks.
+int linear_k_splits(int M, int K, int N) {
+  if (M > 64) return 1;
+  const int64_t tiles = (int64_t)((M + 15) / 16) * ((N + 127) / 128);
+  const int stages = (K / 32 + 3) / 4;
+  const int64_t want = (768 + tiles - 1) / tiles;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(stages / 3, want));
+}
+
 hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
-                         const uint8_t* scales, int N, void* y, bool y_bf16, hipStream_t stream) {
+                         const uint8_t* scales, int N, void* y, bool y_bf16, float* partials,
+                         hipStream_t stream) {
   GemmKArgs g{};
   g.A = x;
   g.a_rows = M;
@@ -985,14 +1056,12 @@ hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
   g.M = M;
   g.rows_total = M;
   g.F = N;
-  g.out = y;
-  g.out_bf16 = y_bf16 ? 1 : 0;
-  return launch_linear_tiles<false>(g, M, N, stream);
+  return launch_linear_split<false>(g, M, N, y, y_bf16, partials, stream);
 }
 
 hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int K,
                                const uint8_t* packed, const uint8_t* scales, int N, void* y,
-                               bool y_bf16, hipStream_t stream) {
+                               bool y_bf16, float* partials, hipStream_t stream) {
   GemmKArgs g{};
   g.A = reinterpret_cast<const uint16_t*>(xq);
   g.Asc = xqs;
@@ -1006,9 +1075,7 @@ hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int
   g.M = M;
   g.rows_total = M;
   g.F = N;
-  g.out = y;
-  g.out_bf16 = y_bf16 ? 1 : 0;
-  return launch_linear_tiles<true>(g, M, N, stream);
+  return launch_linear_split<true>(g, M, N, y, y_bf16, partials, stream);
 }
 
 hipError_t gemm_init() { return hipSuccess; }

@@ -76,12 +76,17 @@ hipError_t launch_moe_gate_up(const MoeGemmArgs& a, hipStream_t stream);
 hipError_t launch_moe_down(const MoeGemmArgs& a, hipStream_t stream);
 hipError_t launch_moe_combine(const MoeGemmArgs& a, hipStream_t stream);
 
+// Dense linear. Decode-sized M splits K over several workgroups (linear_k_splits > 1): the
+// splits' fp32 partial sums go to `partials` (linear_k_splits * M * N floats), then one more
+// launch sums them in split order into y; partials may be null when linear_k_splits is 1.
+int linear_k_splits(int M, int K, int N);
 hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
-                         const uint8_t* scales, int N, void* y, bool y_bf16, hipStream_t stream);
+                         const uint8_t* scales, int N, void* y, bool y_bf16, float* partials,
+                         hipStream_t stream);
 // Activation variant: x already MXFP4 (xq [M][K/2], xqs [M][K/32]).
 hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int K,
                                const uint8_t* packed, const uint8_t* scales, int N, void* y,
-                               bool y_bf16, hipStream_t stream);
+                               bool y_bf16, float* partials, hipStream_t stream);
 
 // Kernel attributes that must be set once per process before the first launch.
 hipError_t gemm_init();

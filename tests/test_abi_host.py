@@ -150,6 +150,15 @@ def test_linear_argument_errors(L):
     assert mx.mxfp4_linear_workspace(4, 64, 8, mx.MX_ACT_MXFP4) > 0
     assert L.mxfp4_linear(p, 4, 64, p, p, 8, p, mx.MX_F32, mx.MX_ACT_MXFP4, None, 0,
                           None) == mx.MX_ERR_WORKSPACE
+    # decode-sized M splits K: the partial sums need a workspace even for bf16 activations
+    need = mx.mxfp4_linear_workspace(1, 2880, 5760, 0)
+    assert need >= 2 * 1 * 5760 * 4 and need % 256 == 0
+    assert mx.mxfp4_linear_workspace(1, 2880, 5760, mx.MX_ACT_MXFP4) > need
+    assert mx.mxfp4_linear_workspace(128, 2880, 5760, 0) == 0  # prefill-sized: no split
+    assert L.mxfp4_linear(p, 1, 2880, p, p, 5760, p, mx.MX_BF16, 0, None, 0,
+                          None) == mx.MX_ERR_WORKSPACE
+    assert L.mxfp4_linear(p, 1, 2880, p, p, 5760, p, mx.MX_BF16, 0, p, need - 1,
+                          None) == mx.MX_ERR_WORKSPACE
 
 
 def test_binding_rejects_cpu_tensors():

@@ -45,7 +45,10 @@ def test_linear_decode_sweep_bf16(M):
 @pytest.mark.parametrize("M,K,N", [(1, 32, 16), (17, 96, 200), (5, 64, 48), (100, 2880, 300),
                                    (130, 320, 130), (3, 8192, 64), (257, 2880, 96),
                                    # scale arrays of N*K/32 bytes that are not whole dwords
-                                   (3, 32, 17), (100, 96, 33), (70, 160, 7)])
+                                   (3, 32, 17), (100, 96, 33), (70, 160, 7),
+                                   # K split over workgroups (decode-sized M): bytewise scales
+                                   # with a ragged N, and ragged M over three row tiles
+                                   (3, 2880, 17), (33, 2880, 200)])
 def test_linear_ragged(M, K, N):
     y, ref = _linear_case(M, K, N, 7 + M, torch.float32)
     check_tolerance(to_f64(y), ref, "linear %dx%dx%d" % (M, K, N))
