@@ -829,10 +829,11 @@ struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4
 struct CfgPreGU4 { static constexpr int BM = 128, BN = 512, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
 struct CfgPreDn4 { static constexpr int BM = 128, BN = 384, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
 // Few pairs (a handful of experts touched): the down GEMM (2880 columns: 23 tiles of 128 per
-// expert) takes 64-column tiles, twice the workgroups to stream the few experts' weights
-// (120B-shaped decode, T = 1: 15.9 -> 14.1 us; gate_up, which has twice the columns, measured no
-// better with them).
-struct CfgTinyDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 4, SCM = SCM_RESIDENT, MF = 16; };
+// expert) takes 64-column tiles, twice the workgroups to stream the few experts' weights, with
+// deep stages (8 blocks x 4): with fewer tiles than CUs each workgroup's own stream is the bound
+// (120B-shaped decode, T = 1: 15.9 -> 14.1 us for the 64-column tiles, -> 12.2 us with the deep
+// stages; gate_up, which has twice the columns, measured no better with either).
+struct CfgTinyDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 8, ST = 4, GM = 1, OCC = 2, SCM = SCM_RESIDENT, MF = 16; };
 constexpr int kPrefillRows = 64, kPrefillRows4 = 128;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
 static_assert(CfgPreGU4::BM == kPrefillRows4 && CfgPreDn4::BM == kPrefillRows4, "one tile list");
