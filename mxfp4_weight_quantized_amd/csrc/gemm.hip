@@ -828,12 +828,13 @@ struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4
 // 128 x 384 with 2 or 4 stages and 8-block stages (spills).
 struct CfgPreGU4 { static constexpr int BM = 128, BN = 512, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
 struct CfgPreDn4 { static constexpr int BM = 128, BN = 384, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
-// Few pairs (a handful of experts touched): the down GEMM (2880 columns: 23 tiles of 128 per
-// expert) takes 64-column tiles, twice the workgroups to stream the few experts' weights, with
-// deep stages (8 blocks x 4): with fewer tiles than CUs each workgroup's own stream is the bound
-// (120B-shaped decode, T = 1: 15.9 -> 14.1 us for the 64-column tiles, -> 12.2 us with the deep
-// stages; gate_up, which has twice the columns, measured no better with either).
+// Few pairs (a handful of experts touched): with fewer tiles than CUs each workgroup's own weight
+// stream is the bound, so these tiles keep more stages in flight. The down GEMM (2880 columns: 23
+// tiles of 128 per expert) also takes 64-column tiles, twice the workgroups. 120B-shaped decode,
+// T = 1: down 15.9 -> 14.1 us for the 64-column tiles, -> 12.2 us with 8-block x 4 stages;
+// gate_up 16.8 -> 16.1 us with 4 stages (64-column or 8-block gate_up tiles measured slower).
 struct CfgTinyDn { static constexpr int BM = 16, BN = 64, WM = 1, WN = 4, KT = 8, ST = 4, GM = 1, OCC = 2, SCM = SCM_RESIDENT, MF = 16; };
+struct CfgTinyGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 4, GM = 1, OCC = 2, SCM = SCM_RESIDENT, MF = 16; };
 constexpr int kPrefillRows = 64, kPrefillRows4 = 128;
 static_assert(CfgPreGU::BM == kPrefillRows && CfgPreDn::BM == kPrefillRows, "one tile list");
 static_assert(CfgPreGU4::BM == kPrefillRows4 && CfgPreDn4::BM == kPrefillRows4, "one tile list");
@@ -991,6 +992,8 @@ hipError_t gate_up_tw(GemmKArgs g, const MoeGemmArgs& m, hipStream_t stream) {
     return launch_moe_gemm<CfgDecGU, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);
   }
   if (pre) return launch_moe_gemm<CfgPreGU, MODE_GATE_UP, false, TW>(g, m.max_tiles, m.F, stream);
+  if (use_tiny_tiles(m.T, m.k, m.E, 2 * m.F))
+    return launch_moe_gemm<CfgTinyGU, MODE_GATE_UP, false, TW>(g, m.max_tiles, m.F, stream);
   return launch_moe_gemm<CfgDecGU, MODE_GATE_UP, false, TW>(g, m.max_tiles, m.F, stream);
 }
 template <bool TW>
