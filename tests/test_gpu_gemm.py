@@ -128,6 +128,37 @@ def test_moe_bad_routing_index_is_flagged():
     check_tolerance(to_f64(out)[good], ref, "moe rows without the bad index")
 
 
+def test_moe_empty_batch():
+    """T = 0: nothing to route or compute; the call succeeds and the output is empty."""
+    H, F, E, k, seed = 64, 64, 4, 2, 73
+    wr, _ = inputs.router(seed, E, H, 0.0)
+    x = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    note("moe empty batch")
+    out = mx.mxfp4_moe_mlp(x, *moe_weights_dev(seed, E, H, F), k, wr=to_dev(wr),
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, H)
+
+
+@pytest.mark.parametrize("T", [16, 64])
+def test_moe_max_experts_and_topk(T):
+    """E = MX_MAX_EXPERTS (256) and k = MX_MAX_TOPK (8), internal routing: four experts per lane
+    in the selection, all 256 groups of the permutation (T = 16: selection inside the
+    permutation launch; T = 64: its own launch)."""
+    H, F, E, k, seed = 128, 64, 256, 8, 75
+    x = inputs.activations(seed, T, H)
+    wr, br = inputs.router(seed, E, H, bias_std=0.5)
+    wts = moe_weights(seed, E, H, F)
+    note("moe max experts T=%d E=%d k=%d" % (T, E, k))
+    out, (lg, idx, w) = _run_moe(x, moe_weights_dev(seed, E, H, F), k, torch.float32, wr=wr, br=br)
+    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    oidx, ow = oracle.topk_softmax(lg, k)
+    np.testing.assert_array_equal(idx, oidx)
+    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
+    ref = oracle.moe_mlp(x, idx, w, *wts, E=E)
+    check_tolerance(to_f64(out), ref, "moe E=256 k=8 T=%d" % T)
+
+
 # ----------------------------------------------------------------------------- full-size layers
 def _full_moe(shape, n_sample, out_dtype=torch.float32):
     s = shape

@@ -91,6 +91,28 @@ def test_moe_tiled_equals_row_major_20b_prefill(flags):
     assert torch.equal(a, b)
 
 
+# H = F = MX_MAX_MOE_DIM (3072): decode tiles hold exactly 96 blocks of resident scales per row;
+# prefill tiles end K with a full stage. Internal routing, row-major and tiled weights.
+@pytest.mark.parametrize("T,E,k,tiled", [(9, 4, 2, False), (9, 4, 2, True), (200, 2, 1, True)])
+def test_moe_max_dims(T, E, k, tiled):
+    H = F = 3072
+    seed = 76 + T
+    x = inputs.activations(seed, T, H)
+    wr, br = inputs.router(seed, E, H, 0.5)
+    wts = moe_weights(seed, E, H, F)
+    wd = moe_weights_dev(seed, E, H, F)
+    note("moe max dims T=%d H=F=%d E=%d k=%d tiled=%d" % (T, H, E, k, tiled))
+    out, (lg, idx, w) = mx.mxfp4_moe_mlp(
+        to_dev(x), *(_tiled(wd) if tiled else wd), k, wr=to_dev(wr), br=to_dev(br),
+        out_dtype=torch.float32, flags=TILED if tiled else 0, return_routing=True)
+    torch.cuda.synchronize()
+    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    oidx, ow = oracle.topk_softmax(lg, k)
+    np.testing.assert_array_equal(idx, oidx)
+    ref = oracle.moe_mlp(x, idx, w, *wts, E=E)
+    check_tolerance(to_f64(out), ref, "moe H=F=3072 T=%d" % T)
+
+
 def _full_tiled(shape, n_sample):
     s = shape
     x = inputs.activations(s.seed, s.T, s.H)
