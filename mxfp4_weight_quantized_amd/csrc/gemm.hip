@@ -809,10 +809,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 // measured slower.
 // Decode-shaped (few rows per expert): 16-row tiles, four waves side by side in N, the tile's
 // weight scales resident, 4-block stages x 3, three workgroups per CU. Weight streaming
-// dominates and is bound by the loads in flight per CU: more resident workgroups beat deeper or
-// wider stages (measured on the 20B decode shapes, tiled weights rotated through copies larger
-// than the last-level cache: 8-block x 2 stages, 4 stages, 64-column down tiles and per-stage
-// scales all slower).
+// dominates: a copy of the kernel without its MFMA work and activation loads runs within 5% of
+// it (measured on the 20B decode shapes, tiled weights rotated through copies larger than the
+// last-level cache: three workgroups per CU beat two; 8-block x 2 stages, 4 stages, four
+// workgroups per CU, 256-column tiles, 64-column down tiles and per-stage scales measured no
+// better).
 // OCC: workgroups per CU the register allocation must leave room for (the second launch bound
 // is in waves per SIMD).
 // SCM: how the weight scales reach LDS (resident per tile where weight streaming is the bound).
