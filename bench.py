@@ -287,6 +287,17 @@ def bench_moe(args, name, shape, flags):
     return result
 
 
+def host_cpu() -> str:
+    """The host CPU's model name (Linux), for the baseline's description."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline_moe(args, s, x_np, wr_np, br_np, host_w, mx_act=False):
     """The oracle (router + top-k + MoE MLP) on the first tokens of the same batch, in chunks,
     until about args.cpu_seconds of wall time have passed."""
@@ -306,8 +317,9 @@ def cpu_baseline_moe(args, s, x_np, wr_np, br_np, host_w, mx_act=False):
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "first %d of the %d tokens: router, top-%d softmax and MoE MLP%s in the fp64 "
-                      "C oracle, %.1f s wall" % (done, s.T, s.k,
-                                                 " (activation variant)" if mx_act else "", el)}
+                      "C oracle, %.1f s wall, %d threads on %s" % (
+                          done, s.T, s.k, " (activation variant)" if mx_act else "", el,
+                          oracle.num_threads(), host_cpu())}
 
 
 def bench_linear(args, name, cfg):
@@ -381,7 +393,8 @@ def bench_linear(args, name, cfg):
         el = time.perf_counter() - t0c
         result["cpu_baseline"] = {"value": round(reps * M / el, 3), "unit": "tokens/s",
                                   "cores": oracle.num_threads(), "kind": "oracle",
-                                  "sample": "%d full calls (%d tokens each), %.1f s wall" % (reps, M, el)}
+                                  "sample": "%d full calls (%d tokens each), %.1f s wall, %d threads on %s"
+                                            % (reps, M, el, oracle.num_threads(), host_cpu())}
     return result
 
 
