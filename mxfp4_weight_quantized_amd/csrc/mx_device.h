@@ -3,6 +3,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace mx {
 
@@ -121,14 +122,33 @@ __device__ __forceinline__ int select_topk_wave(LogitOf logit_of, int lane, int 
         bv = cv[q];
         bi = ci[q];
       }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
+    // wave-wide best: DPP exchanges inside each 16-lane row (partners lane^1, lane^2, then the
+    // mirrored lane in the half row and in the row), then the four rows' bests combined
+    // uniformly from lanes 0, 16, 32 and 48
+    auto take = [&](float ov, int oi) {
       if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
         bv = ov;
         bi = oi;
       }
+    };
+    auto dpp_step = [&](auto ctrl) {
+      constexpr int C = decltype(ctrl)::value;
+      const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), C, 0xf, 0xf, false));
+      const int oi = __builtin_amdgcn_update_dpp(0, bi, C, 0xf, 0xf, false);
+      take(ov, oi);
+    };
+    dpp_step(std::integral_constant<int, 0xb1>{});   // quad_perm [1,0,3,2]: lane ^ 1
+    dpp_step(std::integral_constant<int, 0x4e>{});   // quad_perm [2,3,0,1]: lane ^ 2
+    dpp_step(std::integral_constant<int, 0x141>{});  // row_half_mirror: 7 - lane in 8
+    dpp_step(std::integral_constant<int, 0x140>{});  // row_mirror: 15 - lane in 16
+#pragma unroll
+    for (int row = 1; row < 4; ++row)
+      take(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * row)),
+           __builtin_amdgcn_readlane(bi, 16 * row));
+    {  // row 0 last, so that every lane ends with the same (uniform) result
+      const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
+      const int i0 = __builtin_amdgcn_readlane(bi, 0);
+      take(v0, i0);
     }
     sel_v[j] = bv;
     sel_i[j] = bi;
