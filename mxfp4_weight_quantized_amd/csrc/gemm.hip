@@ -971,8 +971,9 @@ int moe_tile_rows(int T, int k, int E, bool mx_act) {
   return use_prefill_tiles(T, k, E) ? (mx_act ? kPrefillRows4 : kPrefillRows) : 16;
 }
 
+// Each touched expert (at most min(E, T*k) of them) adds at most one partial row tile.
 int moe_max_tiles(int T, int k, int E, int tile_rows) {
-  return (int)(((int64_t)T * k + tile_rows - 1) / tile_rows) + E;
+  return (int)(((int64_t)T * k + tile_rows - 1) / tile_rows + std::min<int64_t>(E, (int64_t)T * k));
 }
 
 namespace {
