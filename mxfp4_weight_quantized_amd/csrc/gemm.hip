@@ -991,6 +991,8 @@ hipError_t gate_up_tw(GemmKArgs g, const MoeGemmArgs& m, hipStream_t stream) {
     g.A = reinterpret_cast<const uint16_t*>(m.xq);  // packed codes, addressed in bytes
     g.Asc = m.xqs;
     if (pre) return launch_moe_gemm<CfgPreGU4, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);
+    if (use_tiny_tiles(m.T, m.k, m.E, 2 * m.F))
+      return launch_moe_gemm<CfgTinyGU, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);
     return launch_moe_gemm<CfgDecGU, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);
   }
   if (pre) return launch_moe_gemm<CfgPreGU, MODE_GATE_UP, false, TW>(g, m.max_tiles, m.F, stream);
@@ -1005,6 +1007,8 @@ hipError_t down_tw(GemmKArgs d, const MoeGemmArgs& m, hipStream_t stream) {
     d.A = reinterpret_cast<const uint16_t*>(m.hq);
     d.Asc = m.hqs;
     if (pre) return launch_moe_gemm<CfgPreDn4, MODE_DOWN, true, TW>(d, m.max_tiles, m.H, stream);
+    if (use_tiny_tiles(m.T, m.k, m.E, m.H))
+      return launch_moe_gemm<CfgTinyDn, MODE_DOWN, true, TW>(d, m.max_tiles, m.H, stream);
     return launch_moe_gemm<CfgDecDn, MODE_DOWN, true, TW>(d, m.max_tiles, m.H, stream);
   }
   if (pre) return launch_moe_gemm<CfgPreDn, MODE_DOWN, false, TW>(d, m.max_tiles, m.H, stream);

@@ -18,6 +18,7 @@ from parity_util import (check_tolerance, moe_weights, moe_weights_dev, note, to
 pytestmark = pytest.mark.gpu
 
 TILED = mx.MX_WEIGHTS_TILED
+FRAGILE_C = 4.0  # assumed fp32 error of g and u: 4 * 2^-24 * sqrt(H * sum of squared terms)
 
 
 def _np_tile(packed, scales):
@@ -113,23 +114,29 @@ def test_moe_max_dims(T, E, k, tiled):
     check_tolerance(to_f64(out), ref, "moe H=F=3072 T=%d" % T)
 
 
-# Few pairs and a long K (the few-tile GEMM configurations over all their stages): tiled equals
-# row-major bit for bit, and both match the oracle.
+# Few pairs and a long K (the few-tile GEMM configurations over all their stages), for the bf16
+# path and the activation variant: tiled equals row-major bit for bit, and both match the oracle.
 @pytest.mark.parametrize("T,H,F,E,k", [(2, 2880, 2880, 8, 2), (3, 2880, 1440, 16, 4)])
-def test_moe_few_pairs_long_k(T, H, F, E, k):
+@pytest.mark.parametrize("flags", [0, mx.MX_ACT_MXFP4])
+def test_moe_few_pairs_long_k(T, H, F, E, k, flags):
     seed = 90 + T
     x = inputs.activations(seed, T, H)
     wts = moe_weights(seed, E, H, F)
     wd = moe_weights_dev(seed, E, H, F)
     idx, w = _routing(T, E, k, seed)
     idx_d, w_d = to_dev(idx), to_dev(w)
-    note("moe few pairs T=%d H=%d F=%d E=%d k=%d" % (T, H, F, E, k))
-    a = mx.mxfp4_moe_mlp(to_dev(x), *wd, k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32)
+    note("moe few pairs T=%d H=%d F=%d E=%d k=%d flags=%d" % (T, H, F, E, k, flags))
+    a = mx.mxfp4_moe_mlp(to_dev(x), *wd, k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32,
+                         flags=flags)
     b = mx.mxfp4_moe_mlp(to_dev(x), *_tiled(wd), k, topk_idx=idx_d, topk_w=w_d,
-                         out_dtype=torch.float32, flags=TILED)
+                         out_dtype=torch.float32, flags=flags | TILED)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
-    check_tolerance(to_f64(b), oracle.moe_mlp(x, idx, w, *wts, E=E), "moe few pairs T=%d" % T)
+    if flags & mx.MX_ACT_MXFP4:
+        ref, _, slack = oracle.moe_mlp(x, idx, w, *wts, E=E, mx_act=True, fragile_c=FRAGILE_C)
+        check_tolerance(to_f64(b), ref, "moe mx-act few pairs T=%d" % T, slack=slack)
+    else:
+        check_tolerance(to_f64(b), oracle.moe_mlp(x, idx, w, *wts, E=E), "moe few pairs T=%d" % T)
 
 
 def _full_tiled(shape, n_sample):
