@@ -180,7 +180,10 @@ size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc);
  *   Limits: H, F multiples of 32 and <= MX_MAX_MOE_DIM; E, k as for moe_route_topk; all weight, x and
  *   out pointers 16-byte aligned. Routing indices outside [0, E) (caller routing) are skipped and
  *   flagged in the workspace status word (read it with mx_workspace_status); their tokens'
- *   outputs then lack those experts. Concurrent calls must use distinct workspaces. */
+ *   outputs then lack those experts. Concurrent calls must use distinct workspaces.
+ *   Internal routing is moe_route_topk's up to the fp32 summation order of the logits (small
+ *   batches split H over more workgroups, partial sums added in a fixed order, so results do not
+ *   depend on timing); the top-k is exact given the logits it reports. */
 mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------

@@ -242,7 +242,7 @@ MX_API mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const flo
   st = check_device();
   if (st != MX_OK) return st;
   ProfScope ps(PK_ROUTE, (hipStream_t)stream);
-  hipError_t e = mx::launch_route_topk(x, wr, br, T, H, E, k, logits, topk_idx, topk_w, (hipStream_t)stream);
+  hipError_t e = mx::launch_route_topk(x, wr, br, T, H, E, k, logits, topk_idx, topk_w, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "route launch");
 }
 
@@ -317,11 +317,14 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
     int32_t* oi = d.topk_idx_out ? d.topk_idx_out : reinterpret_cast<int32_t*>(w + L.idx);
     float* ow = d.topk_w_out ? d.topk_w_out : reinterpret_cast<float*>(w + L.w);
     select_in_permute = mx::route_logits_defers_select(d.T, d.E, d.k);
+    // the router's partial sums borrow the down projection's output rows (written later)
+    const size_t part_bytes = (size_t)mx::route_partial_splits(d.T, d.H, d.E) * d.T * d.E * 4;
+    float* rpart = part_bytes <= (size_t)d.T * d.k * d.H * 4 ? reinterpret_cast<float*>(w + L.y) : nullptr;
     {
       ProfScope ps(PK_ROUTE, s);
       e = select_in_permute
               ? mx::launch_route_logits(d.x, d.wr, d.br, d.T, d.H, d.E, logits, s)
-              : mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, s);
+              : mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, rpart, s);
     }
     if (e != hipSuccess) return hip_fail(e, "route launch");
     sel_logits = logits;

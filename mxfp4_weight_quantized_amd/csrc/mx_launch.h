@@ -17,9 +17,12 @@ hipError_t launch_tile_weights(const uint8_t* packed, const uint8_t* scales, int
                                int K, uint8_t* packed_t, uint8_t* scales_t, hipStream_t stream);
 
 // route.hip
+// partials (may be null): fp32 scratch of route_partial_splits(T, H, E) * T * E floats; with it
+// small batches split H over more workgroups.
 hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
-                             int E, int k, float* logits, int32_t* idx, float* w,
+                             int E, int k, float* logits, int32_t* idx, float* w, float* partials,
                              hipStream_t stream);
+int route_partial_splits(int T, int H, int E);
 // Router logits only, when the selection can be left to launch_select_permute (small batches
 // whose logits kernel does not select itself); returns false (nothing launched) otherwise.
 bool route_logits_defers_select(int T, int E, int k);

@@ -10,7 +10,7 @@ import torch
 import oracle
 from mxfp4_weight_quantized_amd import inputs
 import mxfp4_weight_quantized_amd as mx
-from parity_util import DEV, note, to_dev
+from parity_util import DEV, moe_weights_dev, note, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,29 @@ def test_route_topk_parity(T, H, E, k, bias):
     for t in np.nonzero(diff)[0]:
         s = np.sort(ref[t])[::-1]
         assert np.min(np.abs(np.diff(s[:k + 1]))) < 1e-4, "routing differs beyond a near-tie"
+
+
+# Routing inside mxfp4_moe_mlp: small batches split H over 2 or 4 workgroups per tile, whose
+# partial sums the selection adds up in split order (T=64/E=32 and T=9/E=4: four splits,
+# T=256/E=128: two, E=40: a ragged expert group). Same bar as the router alone.
+@pytest.mark.parametrize("T,H,E,k,bias", [(64, 2880, 32, 4, 0.0), (64, 2880, 40, 8, 0.5),
+                                          (9, 3072, 4, 2, 0.5), (256, 2880, 128, 4, 1.0)])
+def test_route_inside_moe_call(T, H, E, k, bias):
+    seed, F = 35 + T, 64
+    x = inputs.activations(seed, T, H)
+    wr, br = inputs.router(seed, E, H, bias)
+    note("route in moe call T=%d H=%d E=%d k=%d" % (T, H, E, k))
+    _, (lg, idx, w) = mx.mxfp4_moe_mlp(to_dev(x), *moe_weights_dev(seed, E, H, F), k,
+                                       wr=to_dev(wr), br=to_dev(br) if bias else None,
+                                       out_dtype=torch.float32, return_routing=True)
+    torch.cuda.synchronize()
+    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    ref = oracle.router_logits(x, wr, br if bias else None)
+    assert np.all(np.abs(lg - ref) <= 1e-5 * (np.abs(ref) + 1) + 2e-6 * np.abs(ref).max()), \
+        float(np.abs(lg - ref).max())
+    oidx, ow = oracle.topk_softmax(lg, k)
+    np.testing.assert_array_equal(idx, oidx)
+    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
 
 
 def test_route_ties_go_to_lower_index():
