@@ -557,7 +557,11 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   //   (16 x 16 x 32, or 32 x 32 x 16 when MF = 32: MFMA s takes elements [8s, 8s+8) of the
   //   lane's block either way).
   //   FP4 A: per super-step and fragment pair, one scaled MFMA on the raw blocks and scale bytes.
+  // A wave whose output columns all lie past N (in the last column tile) skips its fragment reads
+  // and MFMAs; it still loads its share of every stage and meets every barrier.
+  const bool wave_live = (SWIGLU ? nt * BNH + wn * (BNH / WN) : nt * BN + wn * TN) < p.N;
   auto compute = [&](const Stage& sg, int kt) {
+    if (!wave_live) return;
     const uint8_t* As = sg.A;
     const uint8_t* Bsm = sg.B;
     const uint8_t* Scb = SCM == SCM_RESIDENT ? reinterpret_cast<const uint8_t*>(sRes) + kt * KT * SBS
