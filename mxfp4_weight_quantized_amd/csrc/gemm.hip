@@ -557,10 +557,16 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
   //   (16 x 16 x 32, or 32 x 32 x 16 when MF = 32: MFMA s takes elements [8s, 8s+8) of the
   //   lane's block either way).
   //   FP4 A: per super-step and fragment pair, one scaled MFMA on the raw blocks and scale bytes.
-  // A wave whose output columns all lie past N (in the last column tile) skips its fragment reads
-  // and MFMAs; it still loads its share of every stage and meets every barrier.
-  const bool wave_live = (SWIGLU ? nt * BNH + wn * (BNH / WN) : nt * BN + wn * TN) < p.N;
-  auto compute = [&](const Stage& sg, int kt) {
+  // A wave whose output columns all lie past N (in the last column tile), or whose rows all lie
+  // past the tile's last valid row, skips its fragment reads and MFMAs; it still loads its share
+  // of every stage and meets every barrier. Where the valid rows fit in the first half of the
+  // wave's row fragments (an expert's last, mostly empty row tile), the main loop runs a copy
+  // that computes only that half (the other accumulators stay zero; their rows are dropped).
+  const int wave_rows = n_valid - wm * TM;
+  const bool wave_live = (SWIGLU ? nt * BNH + wn * (BNH / WN) : nt * BN + wn * TN) < p.N && wave_rows > 0;
+  constexpr int FMH = (FM % 2 == 0) ? FM / 2 : FM;
+  auto compute = [&](const Stage& sg, int kt, auto fl) {
+    constexpr int FL = decltype(fl)::value;
     if (!wave_live) return;
     const uint8_t* As = sg.A;
     const uint8_t* Bsm = sg.B;
@@ -581,10 +587,10 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
         scb[f] = (!TW && past) ? 127u : (uint32_t)Scb[bsh[f] + (LG * j + g) * SBS];
       }
       if constexpr (AFP4) {
-        u32x4 a[FM];
-        uint32_t sca[FM];
+        u32x4 a[FL];
+        uint32_t sca[FL];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int i = 0; i < FL; ++i) {
           const int r = wm * TM + i * MF + ln;
           a[i] = lds_read_b128(As + r * A_ROW + (((LG * j + g) ^ swz_rows<ACH>(r)) << 4));
           sca[i] = past ? 127u : (uint32_t)Sab[ash[i] + LG * j + g];
@@ -592,12 +598,12 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
         for (int f = 0; f < FN; ++f)
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FL; ++i)
             acc[i][f] = mfma_fp4_16x16x128(a[i], w[f], sca[i], scb[f], acc[i][f]);
       } else {
-        bf16x8 a[FM][4];
+        bf16x8 a[FL][4];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+        for (int i = 0; i < FL; ++i) {
           const int r = wm * TM + i * MF + ln;
 #pragma unroll
           for (int s = 0; s < 4; ++s)
@@ -624,7 +630,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
             for (int f = 0; f < FN; ++f)
 #pragma unroll
-              for (int i = 0; i < FM; ++i) acc[i][f] = mfma32x32x16(a[i][s], b[f][s], acc[i][f]);
+              for (int i = 0; i < FL; ++i) acc[i][f] = mfma32x32x16(a[i][s], b[f][s], acc[i][f]);
           }
         } else {
           bf16x8 b[2][4];
@@ -639,7 +645,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-              for (int i = 0; i < FM; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
+              for (int i = 0; i < FL; ++i) acc[i][f] = mfma16x16x32(a[i][s], b[f & 1][s], acc[i][f]);
           }
         }
       }
@@ -666,18 +672,22 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     else if (STAGES >= 3 && n >= LA) wait_vmcnt<(STAGES >= 3 ? LA : 0)>();
     else wait_vmcnt<0>();
   };
-  int st = 0;
-  for (int kt = 0; kt < ntk; ++kt) {
-    wait_stage(kt);
-    barrier_lds();
-    if (kt + STAGES - 1 < ntk) {
-      Stage& sn = stg[st == 0 ? STAGES - 1 : st - 1];
-      issue_w(sn, kt0 + kt + STAGES - 1);
-      issue_a(sn, kt0 + kt + STAGES - 1);
+  auto main_loop = [&](auto fl) {
+    int st = 0;
+    for (int kt = 0; kt < ntk; ++kt) {
+      wait_stage(kt);
+      barrier_lds();
+      if (kt + STAGES - 1 < ntk) {
+        Stage& sn = stg[st == 0 ? STAGES - 1 : st - 1];
+        issue_w(sn, kt0 + kt + STAGES - 1);
+        issue_a(sn, kt0 + kt + STAGES - 1);
+      }
+      compute(stg[st], kt0 + kt, fl);
+      st = st == STAGES - 1 ? 0 : st + 1;
     }
-    compute(stg[st], kt0 + kt);
-    st = st == STAGES - 1 ? 0 : st + 1;
-  }
+  };
+  if (FMH < FM && wave_rows <= FMH * MF) main_loop(std::integral_constant<int, FMH>{});
+  else main_loop(std::integral_constant<int, FM>{});
 
   if constexpr (MODE == MODE_GATE_UP) {
     // h goes out through LDS: SwiGLU into a BM x BN/2 bf16 tile (rows padded by 16 bytes: the
