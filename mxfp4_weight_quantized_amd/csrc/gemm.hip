@@ -776,7 +776,8 @@ __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_
 }
 // out[t][n] = sum_{j < k} w[t][j] * Y[inv[t*k + j]][n] in slot order (each product rounded to
 // fp32, then summed); pairs with inv < 0 (skipped routing indices) contribute nothing. Eight
-// columns per thread (two 16-byte loads per row in flight).
+// columns per thread (two 16-byte loads per row in flight). Each Y element is read once: the
+// loads carry the non-temporal hint (20B-shaped prefill, T = 8192: 82 -> 79 us).
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       const int32_t* __restrict__ inv,
@@ -792,12 +793,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int r = inv[(int64_t)t * k + j];
     if (r < 0) continue;
     const float wj = w[(int64_t)t * k + j];
-    const float4 v0 = *reinterpret_cast<const float4*>(Y + (int64_t)r * H + c);
-    const float4 v1 = *reinterpret_cast<const float4*>(Y + (int64_t)r * H + c + 4);
-    s[0] += __fmul_rn(v0.x, wj); s[1] += __fmul_rn(v0.y, wj);
-    s[2] += __fmul_rn(v0.z, wj); s[3] += __fmul_rn(v0.w, wj);
-    s[4] += __fmul_rn(v1.x, wj); s[5] += __fmul_rn(v1.y, wj);
-    s[6] += __fmul_rn(v1.z, wj); s[7] += __fmul_rn(v1.w, wj);
+    const f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r * H + c));
+    const f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r * H + c + 4));
+    s[0] += __fmul_rn(v0[0], wj); s[1] += __fmul_rn(v0[1], wj);
+    s[2] += __fmul_rn(v0[2], wj); s[3] += __fmul_rn(v0[3], wj);
+    s[4] += __fmul_rn(v1[0], wj); s[5] += __fmul_rn(v1[1], wj);
+    s[6] += __fmul_rn(v1[2], wj); s[7] += __fmul_rn(v1[3], wj);
   }
   if (BF16_OUT) {
     uint32_t q[4];
