@@ -25,8 +25,9 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked host. bf16 tensors are passed as uint16_t bit
  *     patterns. The caller owns every buffer; the library never allocates or frees memory and
- *     never synchronizes (mx_workspace_status is the one exception). Work is enqueued on `stream`
- *     (a hipStream_t; NULL = the default stream) and outputs are valid once it completes.
+ *     never synchronizes (the diagnostics mx_get_device_error, mx_workspace_status and
+ *     mx_profile_read are the exceptions). Work is enqueued on `stream` (a hipStream_t; NULL =
+ *     the default stream) and outputs are valid once it completes.
  *   - Inputs and outputs must not alias.
  *   - Argument errors are found on the host before anything is launched and return a status
  *     (never a C++ exception); mx_last_error() then describes it. A failed launch returns
@@ -93,7 +94,11 @@ mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t
 /* ------------------------------------------------------------------------------------------------
  * mxfp4_tile_weights -- rearrange G packed matrices [R][K] into the layout in which the grouped
  * GEMMs of mxfp4_moe_mlp (flag MX_WEIGHTS_TILED) read every weight stage as whole cache lines.
- * Weights are static, so this runs once, when they are loaded. A pure permutation of bytes:
+ * The pages put the MXFP4 conversion at model load, through the quantizer and its integration
+ * hooks ([EN] "MXFP4 4-Bit Quantization" > "Native Support in transformers"), and have the
+ * quantized matmul read the packed weights as they are stored ([GGUF] "ggml Metal 커널 통합");
+ * this is that load-time step for these kernels: weights are static, so it runs once, and it is
+ * a pure permutation of bytes (every weight stays packed, nothing is decoded):
  *   packed [G][R][K/2], scales [G][R][K/32] in (the layout above);
  *   packed_t [G][R/16][K/32][16][16] out: the 16 code bytes of block b of rows 16q..16q+15 as
  *     one 256-byte run, row r at byte 16*(r % 16);
@@ -109,9 +114,10 @@ mx_status mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales, int64
  * moe_route_topk -- router logits, top-k expert selection and softmax over the k selected
  * ([GGUF] "ggml Metal 커널 통합": top-k expert selection for MoE; the router itself is a reading).
  *   x [T][H] bf16, wr [E][H] bf16, br [E] fp32 or NULL (no bias).
- *   logits [T][E] fp32 out (required: the selection pass reads it back); topk_idx [T][k] int32
- *   out, in rank order
- *   (logit descending, lower expert index first on equal logits); topk_w [T][k] fp32 out.
+ *   logits [T][E] fp32 out, or NULL (not stored: every workgroup then covers all experts of its
+ *   16 tokens and selects from on-chip memory, which leaves small batches on fewer CUs);
+ *   topk_idx [T][k] int32 out, in rank order (logit descending, lower expert index first on
+ *   equal logits); topk_w [T][k] fp32 out.
  *   Limits: 1 <= k <= min(E, MX_MAX_TOPK), 1 <= E <= MX_MAX_EXPERTS, H % 32 == 0 (MX_ERR_SHAPE);
  *   x and wr 16-byte aligned (MX_ERR_ALIGN). Logits are fp32 sums of bf16 products; the top-k
  *   is exact given those logits.
@@ -128,22 +134,19 @@ mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const float* br,
  *   offsets [E+1] int32 out: expert e owns permuted rows [offsets[e], offsets[e+1]).
  *   perm [T*k] int32 out: perm[row] = t*k + j of the pair at permuted row `row`.
  *   inv [T*k] int32 out: inv[t*k + j] = its permuted row.
- *   status: one int32 out (may be NULL): 0, or 1 if some index lay outside [0, E); such pairs
- *   are left out of perm and their inv entry is -1.
+ *   ws: device workspace of moe_permute_workspace(T, k, E) bytes, 256-byte aligned, owned by the
+ *   caller (contents need not be initialized). Large batches are then permuted by many
+ *   workgroups (a histogram of every 4096-pair slice, then each slice placed from all slice
+ *   histograms). ws may be NULL (ws_bytes ignored): one workgroup then does the whole
+ *   permutation, with the same results element for element. A non-NULL ws smaller than the
+ *   query is MX_ERR_WORKSPACE. The query is 0 for small batches.
+ *   Indices outside [0, E) are left out of perm, their inv entry is -1, and the device error
+ *   word gets MX_DEVERR_ROUTING (mx_get_device_error).
  *   Deterministic (no ordering by atomics). Limits as for moe_route_topk; T*k < 2^31.
  * ---------------------------------------------------------------------------------------------- */
-mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* offsets,
-                      int32_t* perm, int32_t* inv, int32_t* status, void* stream);
-
-/* moe_permute_ws -- moe_permute with a caller-owned device workspace, which lets a large batch
- * be permuted by many workgroups (a histogram of every 4096-pair slice, then each slice placed
- * from all slice histograms; the same stable counting sort, so the same results element for
- * element). ws: at least moe_permute_workspace(T, k, E) bytes, 256-byte aligned (may be NULL
- * when that is 0: small batches take the one-workgroup path). */
 size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E);
-mx_status moe_permute_ws(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
-                         int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status, void* ws,
-                         size_t ws_bytes, void* stream);
+mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t* offsets,
+                      int32_t* perm, int32_t* inv, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * mxfp4_moe_mlp -- the whole MoE MLP: route -> permute -> gate_up grouped GEMM with fused SwiGLU
@@ -180,7 +183,8 @@ size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc);
  *   Limits: H, F multiples of 32 and <= MX_MAX_MOE_DIM; E, k as for moe_route_topk; all weight, x and
  *   out pointers 16-byte aligned. Routing indices outside [0, E) (caller routing) are skipped and
  *   flagged in the workspace status word (read it with mx_workspace_status); their tokens'
- *   outputs then lack those experts. Concurrent calls must use distinct workspaces.
+ *   outputs then lack those experts (the device error word gets MX_DEVERR_ROUTING too).
+ *   Concurrent calls must use distinct workspaces.
  *   Internal routing is moe_route_topk's up to the fp32 summation order of the logits (small
  *   batches split H over more workgroups, partial sums added in a fixed order, so results do not
  *   depend on timing); the top-k is exact given the logits it reports. */
@@ -207,8 +211,16 @@ mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uint8_t* p
  * ---------------------------------------------------------------------------------------------- */
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* mx_last_error(void);
+/* Errors the kernels found in the data (not in the arguments), as bits of the device error word
+ * the library keeps for each device (the current one is read): */
+#define MX_DEVERR_ROUTING 0x1  /* a routing index outside [0, E) was skipped (moe_permute,
+                                  mxfp4_moe_mlp with caller routing) */
+/* Synchronizes `stream`, copies the current device's error word to *code_host (host pointer; 0 =
+ * none) and clears it. Calls on other streams of the device share the word. For tests and
+ * debugging: it synchronizes. */
+mx_status mx_get_device_error(void* stream, int32_t* code_host);
 /* Synchronizes `stream`, then copies the status word of an mxfp4_moe_mlp workspace to *status
- * (host pointer): 0 = fine, 1 = routing index outside [0, E) seen. */
+ * (host pointer): 0 = fine, 1 = routing index outside [0, E) seen by that call. */
 mx_status mx_workspace_status(const void* ws, void* stream, int32_t* status);
 /* Library version string. */
 const char* mx_version(void);

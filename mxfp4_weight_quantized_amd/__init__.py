@@ -22,6 +22,7 @@ MX_ERR_WORKSPACE, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 5, 6, 7
 MX_F32, MX_BF16 = 0, 1
 MX_ACT_MXFP4 = 0x1
 MX_WEIGHTS_TILED = 0x2
+MX_DEVERR_ROUTING = 0x1
 STATUS_NAMES = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
                 4: "MX_ERR_DTYPE", 5: "MX_ERR_WORKSPACE", 6: "MX_ERR_UNSUPPORTED", 7: "MX_ERR_HIP"}
 
@@ -66,14 +67,14 @@ SIGNATURES = {
     "mxfp4_dequantize": (_INT, [_VP, _VP, _I64, _I64, _VP, _INT, _VP]),
     "mxfp4_tile_weights": (_INT, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP]),
     "moe_route_topk": (_INT, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
-    "moe_permute": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
     "moe_permute_workspace": (_SZ, [_I32, _I32, _I32]),
-    "moe_permute_ws": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "moe_permute": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxfp4_moe_mlp_workspace": (_SZ, [ctypes.POINTER(MoeDesc)]),
     "mxfp4_moe_mlp": (_INT, [ctypes.POINTER(MoeDesc), _VP, _SZ, _VP]),
     "mxfp4_linear_workspace": (_SZ, [_I32, _I32, _I32, _U32]),
     "mxfp4_linear": (_INT, [_VP, _I32, _I32, _VP, _VP, _I32, _VP, _INT, _U32, _VP, _SZ, _VP]),
     "mx_last_error": (ctypes.c_char_p, []),
+    "mx_get_device_error": (_INT, [_VP, ctypes.POINTER(ctypes.c_int32)]),
     "mx_workspace_status": (_INT, [_VP, _VP, ctypes.POINTER(ctypes.c_int32)]),
     "mx_version": (ctypes.c_char_p, []),
     "mx_profile_enable": (_INT, [_INT]),
@@ -169,37 +170,41 @@ def mxfp4_tile_weights(packed: torch.Tensor, scales: torch.Tensor, stream=None):
 
 def moe_route_topk(x: torch.Tensor, wr: torch.Tensor, br: torch.Tensor | None, k: int,
                    want_logits: bool = True, stream=None):
-    """x [T, H] bf16, wr [E, H] bf16, br [E] fp32 or None -> (logits, topk_idx, topk_w)."""
+    """x [T, H] bf16, wr [E, H] bf16, br [E] fp32 or None -> (logits or None, topk_idx, topk_w).
+    want_logits=False passes logits = NULL (the library then selects without storing them)."""
     T, H = x.shape
     E = wr.shape[0]
     dev = x.device
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     _check(lib().moe_route_topk(_ptr(x), _ptr(wr), _ptr(br), T, H, E, k, _ptr(logits), _ptr(idx),
                                 _ptr(w), _stream(stream)))
-    return (logits if want_logits else None), idx, w
+    return logits, idx, w
 
 
-def moe_permute(topk_idx: torch.Tensor, E: int, stream=None, use_workspace: bool = False):
-    """topk_idx [T, k] int32 -> (offsets [E+1], perm [T*k], inv [T*k], status [1]).
-    use_workspace: go through moe_permute_ws (many workgroups for large batches)."""
+def moe_permute(topk_idx: torch.Tensor, E: int, stream=None, use_workspace: bool = True):
+    """topk_idx [T, k] int32 -> (offsets [E+1], perm [T*k], inv [T*k]).
+    use_workspace: pass moe_permute_workspace bytes (many workgroups for large batches); else
+    ws = NULL (one workgroup). Out-of-range indices are reported by get_device_error()."""
     T, k = topk_idx.shape
     dev = topk_idx.device
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    if use_workspace:
-        nbytes = int(lib().moe_permute_workspace(T, k, E))
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
-        _check(lib().moe_permute_ws(_ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(perm), _ptr(inv),
-                                    _ptr(status), _ptr(ws) if nbytes else None, nbytes,
-                                    _stream(stream)))
-    else:
-        _check(lib().moe_permute(_ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(perm), _ptr(inv),
-                                 _ptr(status), _stream(stream)))
-    return offsets, perm, inv, status
+    nbytes = int(lib().moe_permute_workspace(T, k, E)) if use_workspace else 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    _check(lib().moe_permute(_ptr(topk_idx), T, k, E, _ptr(offsets), _ptr(perm), _ptr(inv),
+                             _ptr(ws), nbytes, _stream(stream)))
+    return offsets, perm, inv
+
+
+def get_device_error(stream=None) -> int:
+    """mx_get_device_error: synchronizes the stream, returns and clears the device error word of
+    the current device (0 = none; MX_DEVERR_ROUTING = a routing index was out of range)."""
+    v = ctypes.c_int32(0)
+    _check(lib().mx_get_device_error(_stream(stream), ctypes.byref(v)))
+    return int(v.value)
 
 
 def make_moe_desc(x, gu_packed, gu_scales, dn_packed, dn_scales, k, out, wr=None, br=None,

@@ -38,8 +38,6 @@ mx_status hip_fail(hipError_t e, const char* what) {
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
-std::once_flag g_init_once;
-hipError_t g_init_err = hipSuccess;
 
 // gfx950 check for the current device (cached per device).
 mx_status check_device() {
@@ -56,8 +54,6 @@ mx_status check_device() {
     g_arch_ok[dev].store(v, std::memory_order_release);
   }
   if (v != 1) return fail(MX_ERR_UNSUPPORTED, "this library runs on gfx950 (MI355X) devices only");
-  std::call_once(g_init_once, [] { g_init_err = mx::gemm_init(); });
-  if (g_init_err != hipSuccess) return hip_fail(g_init_err, "kernel setup");
   return MX_OK;
 }
 
@@ -236,8 +232,8 @@ MX_API mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const flo
   if (st != MX_OK) return st;
   if (H % 32) return fail(MX_ERR_SHAPE, "H=%d must be a multiple of 32", H);
   if (T == 0) return ok();
-  if (!x || !wr || !logits || !topk_idx || !topk_w)
-    return fail(MX_ERR_NULL, "x, wr, logits, topk_idx and topk_w are required");
+  if (!x || !wr || !topk_idx || !topk_w)
+    return fail(MX_ERR_NULL, "x, wr, topk_idx and topk_w are required");
   if (!aligned(x, 16) || !aligned(wr, 16)) return fail(MX_ERR_ALIGN, "x and wr must be 16-byte aligned");
   st = check_device();
   if (st != MX_OK) return st;
@@ -246,42 +242,29 @@ MX_API mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const flo
   return e == hipSuccess ? ok() : hip_fail(e, "route launch");
 }
 
-MX_API mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
-                             int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
-                             void* stream) {
-  mx_status st = check_routing_shape(T, 32, E, k);
-  if (st != MX_OK) return st;
-  if (!offsets) return fail(MX_ERR_NULL, "offsets is required");
-  if (T > 0 && (!topk_idx || !perm || !inv)) return fail(MX_ERR_NULL, "topk_idx, perm and inv are required");
-  st = check_device();
-  if (st != MX_OK) return st;
-  ProfScope ps(PK_PERMUTE, (hipStream_t)stream);
-  hipError_t e = mx::launch_permute(topk_idx, T, k, E, offsets, perm, inv, status, 0, nullptr, nullptr, (hipStream_t)stream);
-  return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
-}
-
 MX_API size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E) {
   if (check_routing_shape(T, 32, E, k) != MX_OK) return 0;
   return align256(mx::permute_sliced_workspace(T, k, E));
 }
 
-MX_API mx_status moe_permute_ws(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
-                                int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
-                                void* ws, size_t ws_bytes, void* stream) {
+MX_API mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                             int32_t* offsets, int32_t* perm, int32_t* inv, void* ws,
+                             size_t ws_bytes, void* stream) {
   mx_status st = check_routing_shape(T, 32, E, k);
   if (st != MX_OK) return st;
   if (!offsets) return fail(MX_ERR_NULL, "offsets is required");
   if (T > 0 && (!topk_idx || !perm || !inv)) return fail(MX_ERR_NULL, "topk_idx, perm and inv are required");
   const size_t need = align256(mx::permute_sliced_workspace(T, k, E));  // as moe_permute_workspace
-  if (need > 0 && (ws == nullptr || ws_bytes < need)) return fail(MX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
-  if (need > 0 && !aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const bool sliced = need > 0 && ws != nullptr;  // ws NULL: one workgroup does it all
+  if (sliced && ws_bytes < need) return fail(MX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (sliced && !aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
   st = check_device();
   if (st != MX_OK) return st;
   ProfScope ps(PK_PERMUTE, (hipStream_t)stream);
-  hipError_t e = need > 0
-      ? mx::launch_permute_sliced(topk_idx, T, k, E, offsets, perm, inv, status, 0, nullptr, nullptr,
-                                  static_cast<int32_t*>(ws), (hipStream_t)stream)
-      : mx::launch_permute(topk_idx, T, k, E, offsets, perm, inv, status, 0, nullptr, nullptr,
+  hipError_t e = sliced
+      ? mx::launch_permute_sliced(topk_idx, T, k, E, offsets, perm, inv, nullptr, 0, nullptr,
+                                  nullptr, static_cast<int32_t*>(ws), (hipStream_t)stream)
+      : mx::launch_permute(topk_idx, T, k, E, offsets, perm, inv, nullptr, 0, nullptr, nullptr,
                            (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "permute launch");
 }
@@ -463,6 +446,18 @@ MX_API mx_status mxfp4_linear(const uint16_t* x, int32_t M, int32_t K, const uin
 }
 
 MX_API const char* mx_last_error(void) { return g_err; }
+
+MX_API mx_status mx_get_device_error(void* stream, int32_t* code_host) {
+  if (!code_host) return fail(MX_ERR_NULL, "code_host is required");
+  mx_status st = check_device();
+  if (st != MX_OK) return st;
+  int32_t* word = mx::device_error_word();
+  if (word == nullptr) return fail(MX_ERR_HIP, "device error word lookup failed");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess) e = hipMemcpy(code_host, word, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(word, 0, sizeof(int32_t));
+  return e == hipSuccess ? ok() : hip_fail(e, "device error read");
+}
 
 MX_API mx_status mx_workspace_status(const void* ws, void* stream, int32_t* status) {
   if (!ws || !status) return fail(MX_ERR_NULL, "ws and status are required");

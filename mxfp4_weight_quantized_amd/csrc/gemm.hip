@@ -1117,6 +1117,4 @@ hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int
   return launch_linear_split<true>(g, M, N, y, y_bf16, partials, stream);
 }
 
-hipError_t gemm_init() { return hipSuccess; }
-
 }  // namespace mx

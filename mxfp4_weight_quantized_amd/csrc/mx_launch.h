@@ -18,7 +18,8 @@ hipError_t launch_tile_weights(const uint8_t* packed, const uint8_t* scales, int
 
 // route.hip
 // partials (may be null): fp32 scratch of route_partial_splits(T, H, E) * T * E floats; with it
-// small batches split H over more workgroups.
+// small batches split H over more workgroups. logits may be null (not stored): then every
+// workgroup covers all experts of its tokens and makes the selection itself.
 hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
                              int E, int k, float* logits, int32_t* idx, float* w, float* partials,
                              hipStream_t stream);
@@ -28,6 +29,12 @@ int route_partial_splits(int T, int H, int E);
 bool route_logits_defers_select(int T, int E, int k);
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
                                int H, int E, float* logits, hipStream_t stream);
+
+// Device error word, one per device, owned by the library: kernels OR error codes into it, and
+// mx_get_device_error reads and clears it. device_error_word() is its device address on the
+// current device (looked up once per device; nullptr if the lookup failed).
+constexpr int32_t kDevErrRouting = 1;  // a routing index outside [0, E) was skipped
+int32_t* device_error_word();
 
 // permute.hip: tiles/num_tiles may be NULL (tile_rows ignored then). With a tile list, perm must
 // hold P + tile_rows entries: the padding (and rows past the last valid pair) are set to pair 0.
@@ -90,8 +97,5 @@ hipError_t launch_linear(const uint16_t* x, int M, int K, const uint8_t* packed,
 hipError_t launch_linear_mxact(const uint8_t* xq, const uint8_t* xqs, int M, int K,
                                const uint8_t* packed, const uint8_t* scales, int N, void* y,
                                bool y_bf16, float* partials, hipStream_t stream);
-
-// Kernel attributes that must be set once per process before the first launch.
-hipError_t gemm_init();
 
 }  // namespace mx

@@ -20,7 +20,28 @@
 #include "mx_device.h"
 #include "mx_launch.h"
 
+#include <atomic>
+
 namespace mx {
+
+// The library's device error word (one copy per device; see device_error_word).
+__device__ int32_t g_device_error;
+
+int32_t* device_error_word() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int32_t*> addr[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  int32_t* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(g_device_error)) != hipSuccess) return nullptr;
+    p = static_cast<int32_t*>(a);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 namespace {
 
 constexpr int kWaves = 16;
@@ -49,7 +70,8 @@ __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx
                                                        int E, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ perm,
                                                        int32_t* __restrict__ inv,
-                                                       int32_t* __restrict__ status, int tile_rows,
+                                                       int32_t* __restrict__ status,
+                                                       int32_t* __restrict__ dev_err, int tile_rows,
                                                        int2* __restrict__ tiles,
                                                        int32_t* __restrict__ num_tiles,
                                                        const float* __restrict__ logits, int k,
@@ -122,6 +144,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx
   if (threadIdx.x == 0) {
     if (tile_rows > 0) *num_tiles = tbase[E];
     if (status != nullptr) *status = bad;
+    if (bad && dev_err != nullptr) atomicOr(dev_err, kDevErrRouting);
   }
   // With a tile list, perm carries tile_rows entries of padding past P: rows past the last valid
   // one (and the padding) hold pair 0, so a tile may read its whole row range of perm.
@@ -180,8 +203,8 @@ __global__ __launch_bounds__(256) void slice_hist_kernel(const int32_t* __restri
 __global__ __launch_bounds__(1024) void slice_scatter_kernel(
     const int32_t* __restrict__ idx, int P, int E, const int32_t* __restrict__ counts, int n_slices,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ status, int tile_rows, int2* __restrict__ tiles,
-    int32_t* __restrict__ num_tiles) {
+    int32_t* __restrict__ status, int32_t* __restrict__ dev_err, int tile_rows,
+    int2* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
   __shared__ int cnt[kWaves][kMaxE];
   __shared__ int tot[kMaxE + 1];
   __shared__ int pre[kMaxE];
@@ -229,11 +252,10 @@ __global__ __launch_bounds__(1024) void slice_scatter_kernel(
       }
     if (threadIdx.x == 0) {
       if (tile_rows > 0) *num_tiles = tbase[E];
-      if (status != nullptr) {
-        int bad = 0;
-        for (int w = 0; w < n_slices; ++w) bad |= counts[(int64_t)w * (E + 1) + E] != 0;
-        *status = bad;
-      }
+      int bad = 0;
+      for (int w = 0; w < n_slices; ++w) bad |= counts[(int64_t)w * (E + 1) + E] != 0;
+      if (status != nullptr) *status = bad;
+      if (bad && dev_err != nullptr) atomicOr(dev_err, kDevErrRouting);
     }
     if (tile_rows > 0)
       for (int i = tot[E] + threadIdx.x; i < P + tile_rows; i += blockDim.x) perm[i] = 0;
@@ -296,7 +318,8 @@ hipError_t launch_permute_sliced(const int32_t* idx, int T, int k, int E, int32_
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(slice_scatter_kernel, dim3(n_slices), dim3(64 * kWaves), 0, stream, idx, P, E,
-                     counts, n_slices, offsets, perm, inv, status, tile_rows, tiles, num_tiles);
+                     counts, n_slices, offsets, perm, inv, status, device_error_word(), tile_rows,
+                     tiles, num_tiles);
   return hipGetLastError();
 }
 
@@ -306,8 +329,8 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
   const int P = T * k;
   if (tiles == nullptr || num_tiles == nullptr) tile_rows = 0;
   hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(64 * kWaves), 0, stream,
-                     const_cast<int32_t*>(idx), P, E, offsets, perm, inv, status, tile_rows, tiles,
-                     num_tiles, nullptr, k, nullptr);
+                     const_cast<int32_t*>(idx), P, E, offsets, perm, inv, status,
+                     device_error_word(), tile_rows, tiles, num_tiles, nullptr, k, nullptr);
   return hipGetLastError();
 }
 
@@ -318,7 +341,8 @@ hipError_t launch_select_permute(const float* logits, int T, int k, int E, int32
   const int P = T * k;
   if (tiles == nullptr || num_tiles == nullptr) tile_rows = 0;
   hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(64 * kWaves), 0, stream, idx, P, E,
-                     offsets, perm, inv, status, tile_rows, tiles, num_tiles, logits, k, w);
+                     offsets, perm, inv, status, device_error_word(), tile_rows, tiles, num_tiles,
+                     logits, k, w);
   return hipGetLastError();
 }
 

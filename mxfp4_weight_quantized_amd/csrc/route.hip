@@ -102,7 +102,7 @@ __global__ __launch_bounds__(1024) void route_logits_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 4 * g + i;
-        if (t < T) logits[(int64_t)t * E + e] = acc[i] + bias;
+        if (t < T && logits != nullptr) logits[(int64_t)t * E + e] = acc[i] + bias;
         if constexpr (SELECT) tile[4 * g + i][e] = acc[i] + bias;
       }
     }
@@ -177,8 +177,9 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
                              hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
-  // G groups per workgroup, H split so that G x splits fills up to 16 waves
-  const int G = (tiles * groups <= kSpreadBelow) ? 1 : groups;
+  // G groups per workgroup, H split so that G x splits fills up to 16 waves. Without a logits
+  // buffer every workgroup covers all experts of its tokens and selects from LDS.
+  const int G = (tiles * groups <= kSpreadBelow && logits != nullptr) ? 1 : groups;
   const int splits = min(16 / G, H / 32);
   if (G == groups) {  // one workgroup covers all experts of its tokens: select in the same kernel
     if (splits >= 16)

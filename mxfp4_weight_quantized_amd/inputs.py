@@ -81,21 +81,26 @@ def expert_weights(seed: int, E: int, H: int, F: int, quantize, threads: int = 8
     """Draw all experts' weights and pack them with ``quantize`` (fp32 [R, K] -> (packed, scales)).
 
     Returns (gu_packed [E, 2F, H/2], gu_scales [E, 2F, H/32], dn_packed [E, H, F/2],
-    dn_scales [E, H, F/32]) as numpy uint8 arrays. Experts are drawn and packed one at a time so
-    the fp32 copies never all coexist."""
+    dn_scales [E, H, F/32]) as numpy uint8 arrays. The random draws run on ``threads`` worker
+    threads, at most ``threads`` experts ahead, so the fp32 copies never all coexist;
+    ``quantize`` is called on the calling thread only (it may run its own thread team)."""
     gu_p = np.empty((E, 2 * F, H // 2), np.uint8)
     gu_s = np.empty((E, 2 * F, H // 32), np.uint8)
     dn_p = np.empty((E, H, F // 2), np.uint8)
     dn_s = np.empty((E, H, F // 32), np.uint8)
 
-    def one(e):
-        p, s = quantize(gate_up_f32(seed, e, F, H))
-        gu_p[e], gu_s[e] = p, s
-        p, s = quantize(down_f32(seed, e, H, F))
-        dn_p[e], dn_s[e] = p, s
+    def draw(e):
+        return gate_up_f32(seed, e, F, H), down_f32(seed, e, H, F)
 
     with ThreadPoolExecutor(max(1, threads)) as ex:
-        list(ex.map(one, range(E)))
+        pending = [ex.submit(draw, e) for e in range(min(E, max(1, threads)))]
+        for e in range(E):
+            wgu, wdn = pending[e].result()
+            pending[e] = None
+            if len(pending) < E:  # keep `threads` draws in flight
+                pending.append(ex.submit(draw, len(pending)))
+            gu_p[e], gu_s[e] = quantize(wgu)
+            dn_p[e], dn_s[e] = quantize(wdn)
     return gu_p, gu_s, dn_p, dn_s
 
 

@@ -25,7 +25,7 @@ _LIB_OVERRIDE = os.environ.get("MXO_ORACLE_LIB")
 _lock = threading.Lock()
 _lib = None
 
-GCC_FLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+GCC_FLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-pthread", "-fPIC",
              "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
 
@@ -63,6 +63,7 @@ def lib():
         sig = {
             "mxo_e2m1_value": (f64, [ctypes.c_uint]),
             "mxo_e8m0_value": (f64, [ctypes.c_uint]),
+            "mxo_weight_operand": (f64, [ctypes.c_uint, ctypes.c_uint, c_int]),
             "mxo_bf16_from_double": (u16, [f64]),
             "mxo_double_from_bf16": (f64, [u16]),
             "mxo_quantize_f32": (None, [_P(f32), i64, i64, _P(u8), _P(u8)]),
@@ -111,6 +112,12 @@ def e2m1_value(code: int) -> float:
 def e8m0_value(b: int) -> float:
     """mxo_e8m0_value: 2^(b-127), NaN for 255."""
     return lib().mxo_e8m0_value(int(b))
+
+
+def weight_operand(code: int, b: int, mx_act: bool = False) -> float:
+    """mxo_weight_operand: value of weight element (code, scale byte b) in the matrix products
+    (the bf16 operand for bf16 activations, the exact value for the activation variant)."""
+    return lib().mxo_weight_operand(int(code), int(b), int(bool(mx_act)))
 
 
 def bf16_from_double(d: float) -> int:

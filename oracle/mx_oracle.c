@@ -13,6 +13,7 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#include <pthread.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -67,26 +68,55 @@ double mxo_double_from_bf16(uint16_t b) {
 
 static double g_e2m1[16];
 static double g_e8m0[256];
-static int g_tables_ready = 0;
+/* Value a weight element takes in the matrix products, by (scale byte, code):
+ *  - g_dq_exact: code * 2^(b-127) exactly (fp64 holds every such value; byte 255 gives NaN).
+ *    The activation variant multiplies MXFP4 by MXFP4 as they are, so its weights are these.
+ *  - g_dq_bf16: the same value as the bf16 operand of a bf16 matrix product, rounded to nearest
+ *    even. Reading of the open point: the pages describe the de-quantized model as the bf16 one
+ *    [EN "Memory Savings"; "Native Support in transformers"], so the weight entering a bf16
+ *    product is the bf16 value of code * 2^(b-127). It is the exact value for every byte and
+ *    code except where the value lies past bf16's largest finite number (bytes 253 and 254 with
+ *    the larger codes), which becomes +-Inf; subnormal values are kept. */
+static double g_dq_exact[256][16];
+static double g_dq_bf16[256][16];
+static pthread_once_t g_tables_once = PTHREAD_ONCE_INIT;
 
 /* Decode tables, filled from the two definitions above (not typed in). */
-static void ensure_tables(void) {
-  if (g_tables_ready) return;
-#pragma omp critical(mxo_tables)
-  {
-    if (!g_tables_ready) {
-      for (unsigned c = 0; c < 16; ++c) g_e2m1[c] = mxo_e2m1_value(c);
-      for (unsigned b = 0; b < 256; ++b) g_e8m0[b] = mxo_e8m0_value(b);
-      g_tables_ready = 1;
+static void build_tables(void) {
+  for (unsigned c = 0; c < 16; ++c) g_e2m1[c] = mxo_e2m1_value(c);
+  for (unsigned b = 0; b < 256; ++b) g_e8m0[b] = mxo_e8m0_value(b);
+  for (unsigned b = 0; b < 256; ++b)
+    for (unsigned c = 0; c < 16; ++c) {
+      g_dq_exact[b][c] = g_e2m1[c] * g_e8m0[b];
+      g_dq_bf16[b][c] = mxo_double_from_bf16(mxo_bf16_from_double(g_dq_exact[b][c]));
     }
-  }
 }
 
-/* Value of element k of a packed row: element 2j is the low nibble of byte j. */
-static inline double decode_elem(const uint8_t* prow, const uint8_t* srow, int64_t k) {
+/* Once per process, whatever thread gets here first (calls may come from several threads). */
+static void ensure_tables(void) { pthread_once(&g_tables_once, build_tables); }
+
+/* Code of element k of a packed row: element 2j is the low nibble of byte j. */
+static inline unsigned elem_code(const uint8_t* prow, int64_t k) {
   uint8_t byte = prow[k >> 1];
-  unsigned code = (k & 1) ? (byte >> 4) : (byte & 0xfu);
-  return g_e2m1[code] * g_e8m0[srow[k >> 5]];
+  return (k & 1) ? (byte >> 4) : (byte & 0xfu);
+}
+
+/* Exact value of element k of a packed row. */
+static inline double decode_elem(const uint8_t* prow, const uint8_t* srow, int64_t k) {
+  return g_dq_exact[srow[k >> 5]][elem_code(prow, k)];
+}
+
+/* Value of weight element k in a matrix product: the bf16 operand (bf16_operand != 0: bf16
+ * activations on bf16 matrix cores), else the exact value (the activation variant). */
+static inline double weight_elem(const uint8_t* prow, const uint8_t* srow, int64_t k,
+                                 int bf16_operand) {
+  const unsigned b = srow[k >> 5], c = elem_code(prow, k);
+  return bf16_operand ? g_dq_bf16[b][c] : g_dq_exact[b][c];
+}
+
+double mxo_weight_operand(unsigned code, unsigned b, int mx_act) {
+  ensure_tables();
+  return mx_act ? g_dq_exact[b & 255u][code & 15u] : g_dq_bf16[b & 255u][code & 15u];
 }
 
 /* ---------------------------------------------------------------------------------------------
@@ -293,7 +323,7 @@ void mxo_linear(const uint16_t* x, int M, int K, const uint8_t* packed, const ui
       const uint8_t* prow = packed + (int64_t)n * (K / 2);
       const uint8_t* srow = scales + (int64_t)n * (K / 32);
       double acc = 0.0;
-      for (int kk = 0; kk < K; ++kk) acc += xr[kk] * decode_elem(prow, srow, kk);
+      for (int kk = 0; kk < K; ++kk) acc += xr[kk] * weight_elem(prow, srow, kk, !mx_act);
       y[(int64_t)m * N + n] = acc;
     }
     free(xr);
@@ -380,7 +410,7 @@ int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t
         const uint8_t* srow = gu_scales + ((int64_t)e * 2 * F + n) * gu_srow;
         double acc = 0.0, sq = 0.0;
         for (int kk = 0; kk < H; ++kk) {
-          const double term = xr[kk] * decode_elem(prow, srow, kk);
+          const double term = xr[kk] * weight_elem(prow, srow, kk, !mx_act);
           acc += term;
           if (fragility) sq += term * term;
         }
@@ -444,7 +474,7 @@ int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t
         const uint8_t* prow = dn_packed + ((int64_t)e * H + m) * dn_row;
         const uint8_t* srow = dn_scales + ((int64_t)e * H + m) * dn_srow;
         double acc = 0.0;
-        for (int f = 0; f < F; ++f) acc += h[f] * decode_elem(prow, srow, f);
+        for (int f = 0; f < F; ++f) acc += h[f] * weight_elem(prow, srow, f, !mx_act);
         o[m] += wt * acc;
       }
     }

@@ -40,6 +40,10 @@ double mxo_double_from_bf16(uint16_t b);
  * packed: rows*K/2 bytes, element 2j in the low nibble of byte j; scales: rows*K/32 bytes. */
 void mxo_quantize_f32(const float* src, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales);
 void mxo_quantize_bf16(const uint16_t* src, int64_t rows, int64_t K, uint8_t* packed, uint8_t* scales);
+/* Value weight element (code, scale byte b) takes in the matrix products: mx_act == 0, the bf16
+ * operand of a bf16 product (code * 2^(b-127) rounded to nearest even bf16: exact except past
+ * bf16's range, which gives +-Inf); mx_act != 0, the exact value. Byte 255 gives NaN. */
+double mxo_weight_operand(unsigned code, unsigned b, int mx_act);
 /* Exact dequantization to fp64. */
 void mxo_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t rows, int64_t K, double* dst);
 
@@ -52,7 +56,8 @@ void mxo_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, fl
  * Returns 0, or -1 if an index lies outside [0, E). */
 int mxo_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm, int32_t* inv);
 
-/* Dense weight-only linear y[m][n] = sum_k x[m][k] * W^[n][k] in fp64.
+/* Dense weight-only linear y[m][n] = sum_k x[m][k] * W^[n][k] in fp64, W^ the weight operand
+ * above (bf16 for mx_act == 0, exact for mx_act != 0).
  * mx_act != 0: the rows of x are first quantized and dequantized along K (activation variant). */
 void mxo_linear(const uint16_t* x, int M, int K, const uint8_t* packed, const uint8_t* scales, int N,
                 int mx_act, double* y);

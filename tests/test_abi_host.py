@@ -26,16 +26,62 @@ def L():
         pytest.fail("HIP library not built: %s" % e)
 
 
+# The boundary the hot path is specified with: every call, with its parameter list (C types as
+# the header spells them, names dropped). mxfp4_linear takes a caller-owned workspace as well
+# (the library never allocates; it holds the quantized activations and the split-K partials).
+CONTRACT = {
+    "mxfp4_quantize": ["const void*", "mx_dtype", "int64_t", "int64_t", "uint8_t*", "uint8_t*",
+                       "void*"],
+    "mxfp4_dequantize": ["const uint8_t*", "const uint8_t*", "int64_t", "int64_t", "void*",
+                         "mx_dtype", "void*"],
+    "moe_route_topk": ["const uint16_t*", "const uint16_t*", "const float*", "int32_t", "int32_t",
+                       "int32_t", "int32_t", "float*", "int32_t*", "float*", "void*"],
+    "moe_permute_workspace": ["int32_t", "int32_t", "int32_t"],
+    "moe_permute": ["const int32_t*", "int32_t", "int32_t", "int32_t", "int32_t*", "int32_t*",
+                    "int32_t*", "void*", "size_t", "void*"],
+    "mxfp4_moe_mlp_workspace": ["const mx_moe_desc*"],
+    "mxfp4_moe_mlp": ["const mx_moe_desc*", "void*", "size_t", "void*"],
+    "mxfp4_linear": ["const uint16_t*", "int32_t", "int32_t", "const uint8_t*", "const uint8_t*",
+                     "int32_t", "void*", "mx_dtype", "uint32_t", "void*", "size_t", "void*"],
+    "mx_last_error": [],
+    "mx_get_device_error": ["void*", "int32_t*"],
+}
+# mx_moe_desc fields in order
+DESC_FIELDS = ["struct_size", "T", "H", "F", "E", "k", "flags", "out_dtype", "x", "wr", "br",
+               "topk_idx_in", "topk_w_in", "gu_packed", "gu_scales", "dn_packed", "dn_scales",
+               "out", "topk_idx_out", "topk_w_out", "logits_out"]
+
+
+def _prototypes():
+    """name -> parameter types of every function the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(mx.HEADER_PATH).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"\b(?:mx_status|size_t|const char\*|int32_t)\s+([a-z_][a-z0-9_]*)\s*"
+                         r"\(([^)]*)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        types = [re.sub(r"\s*\b[a-zA-Z_][a-zA-Z0-9_]*$", "", p).replace(" *", "*").strip()
+                 for p in params]
+        protos[m.group(1)] = types
+    return protos
+
+
+def test_header_declares_the_contract():
+    protos = _prototypes()
+    for name, types in CONTRACT.items():
+        assert name in protos, "header does not declare %s" % name
+        assert protos[name] == types, (name, protos[name], types)
+    fields = [f for f, _ in mx.MoeDesc._fields_]
+    assert fields == DESC_FIELDS
+
+
 def test_exports_every_declared_entry_point(L):
     names = _declared_functions()
-    for required in ("mxfp4_quantize", "mxfp4_dequantize", "moe_route_topk", "moe_permute",
-                     "mxfp4_moe_mlp", "mxfp4_moe_mlp_workspace", "mxfp4_linear",
-                     "mxfp4_linear_workspace", "mx_last_error", "mx_workspace_status",
-                     "mx_version"):
-        assert required in names
+    assert set(CONTRACT) <= set(names)
     for n in names:
         assert hasattr(L, n), "library does not export %s" % n
     assert set(names) == set(mx.SIGNATURES), "binding signatures out of sync with the header"
+    for n, types in _prototypes().items():  # binding arity matches the header
+        assert len(mx.SIGNATURES[n][1]) == len(types), n
 
 
 def test_version_and_error_string(L):
@@ -80,17 +126,18 @@ def test_route_and_permute_argument_errors(L):
     assert L.moe_route_topk(p, p, None, 4, 64, 32, 9, p, p, p, None) == mx.MX_ERR_SHAPE  # k > 8
     assert L.moe_route_topk(p, p, None, 4, 48, 32, 4, p, p, p, None) == mx.MX_ERR_SHAPE  # H % 32
     assert L.moe_route_topk(p, None, None, 4, 64, 32, 4, p, p, p, None) == mx.MX_ERR_NULL
-    assert L.moe_route_topk(p, p, None, 4, 64, 32, 4, None, p, p, None) == mx.MX_ERR_NULL  # logits
+    assert L.moe_route_topk(p, p, None, 4, 64, 32, 4, None, None, p, None) == mx.MX_ERR_NULL  # idx
     assert L.moe_route_topk(p, p, None, 0, 64, 32, 4, p, p, p, None) == mx.MX_OK  # T = 0
-    assert L.moe_permute(p, 4, 2, 8, None, p, p, None, None) == mx.MX_ERR_NULL
+    assert L.moe_route_topk(p, p, None, 0, 64, 32, 4, None, p, p, None) == mx.MX_OK  # no logits
+    assert L.moe_permute(p, 4, 2, 8, None, p, p, None, 0, None) == mx.MX_ERR_NULL
     need = mx.lib().moe_permute_workspace(4096, 4, 32)  # 16 384 pairs: the sliced path
     assert need > 0 and need % 256 == 0 and mx.lib().moe_permute_workspace(64, 4, 32) == 0
-    assert L.moe_permute_ws(p, 4096, 4, 32, p, p, p, None, None, 0, None) == mx.MX_ERR_WORKSPACE
-    assert L.moe_permute_ws(p, 4096, 4, 32, p, p, p, None, p, need - 1, None) == mx.MX_ERR_WORKSPACE
-    assert L.moe_permute_ws(p, 4096, 4, 32, p, p, p, None, ctypes.c_void_p(0x10000010), need,
-                            None) == mx.MX_ERR_ALIGN
-    assert L.moe_permute_ws(p, 4, 9, 8, p, p, p, None, None, 0, None) == mx.MX_ERR_SHAPE
-    assert L.moe_permute(p, 4, 0, 8, p, p, p, None, None) == mx.MX_ERR_SHAPE
+    assert L.moe_permute(p, 4096, 4, 32, p, p, p, p, need - 1, None) == mx.MX_ERR_WORKSPACE
+    assert L.moe_permute(p, 4096, 4, 32, p, p, p, ctypes.c_void_p(0x10000010), need,
+                         None) == mx.MX_ERR_ALIGN
+    assert L.moe_permute(p, 4, 9, 8, p, p, p, None, 0, None) == mx.MX_ERR_SHAPE
+    assert L.moe_permute(p, 4, 0, 8, p, p, p, None, 0, None) == mx.MX_ERR_SHAPE
+    assert L.mx_get_device_error(None, None) == mx.MX_ERR_NULL
 
 
 def _desc(T=4, H=64, F=64, E=8, k=2, **kw):

@@ -2,7 +2,7 @@
 
 Shapes span several tiles with ragged tails (rows per expert, N not a multiple of the tile, K not
 a multiple of the K tile), the decode- and prefill-shaped tile configurations, and the full-size
-layers (sampled tokens where the oracle would take too long)."""
+layers, every token of them against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -10,8 +10,8 @@ import torch
 import oracle
 from mxfp4_weight_quantized_amd import inputs
 import mxfp4_weight_quantized_amd as mx
-from parity_util import (DEV, bf16_host_bits, check_bf16_output, check_tolerance, moe_weights,
-                         moe_weights_dev, note, to_dev, to_f64)
+from parity_util import (DEV, bf16_host_bits, check_bf16_output, check_full_layer,
+                         check_tolerance, moe_weights, moe_weights_dev, note, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -118,11 +118,13 @@ def test_moe_bad_routing_index_is_flagged():
     gp, gs, dp, ds = moe_weights_dev(seed, E, H, F)
     out = torch.empty((T, H), dtype=torch.float32, device=DEV)
     xd, idxd, wd = to_dev(x), to_dev(idx), to_dev(w)  # held until the call has completed
+    assert mx.get_device_error() == 0
     d = mx.make_moe_desc(xd, gp, gs, dp, ds, k, out, topk_idx=idxd, topk_w=wd)
     ws = torch.empty(mx.mxfp4_moe_mlp_workspace(d), dtype=torch.uint8, device=DEV)
     mx._check(mx.lib().mxfp4_moe_mlp(mx.ctypes.byref(d), ws.data_ptr(), ws.numel(),
                                      mx._stream(None)))
     assert mx.workspace_status(ws) == 1
+    assert mx.get_device_error() == mx.MX_DEVERR_ROUTING
     good = [0, 1, 3]
     ref = oracle.moe_mlp(x[good], idx[good], w[good], *moe_weights(seed, E, H, F), E=E)
     check_tolerance(to_f64(out)[good], ref, "moe rows without the bad index")
@@ -160,45 +162,12 @@ def test_moe_max_experts_and_topk(T):
 
 
 # ----------------------------------------------------------------------------- full-size layers
-def _full_moe(shape, n_sample, out_dtype=torch.float32):
-    s = shape
-    x = inputs.activations(s.seed, s.T, s.H)
-    wr, br = inputs.router(s.seed, s.E, s.H, s.bias_std)
-    wts = moe_weights(s.seed, s.E, s.H, s.F)
-    note("moe full %s" % s.name)
-    out, (lg, idx, w) = _run_moe(x, moe_weights_dev(s.seed, s.E, s.H, s.F), s.k, out_dtype,
-                                 wr=wr, br=br if s.bias_std else None)
-    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
-    oidx, ow = oracle.topk_softmax(lg, s.k)
-    np.testing.assert_array_equal(idx, oidx)
-    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
-    # sampled tokens: spread over the batch plus tokens routed to the busiest expert
-    r = np.random.default_rng(s.seed)
-    busiest = np.bincount(idx.reshape(-1), minlength=s.E).argmax()
-    on_busiest = np.nonzero((idx == busiest).any(axis=1))[0]
-    toks = np.unique(np.concatenate([r.choice(s.T, size=min(s.T, n_sample), replace=False),
-                                     on_busiest[:4], [0, s.T - 1]])).astype(np.int32)
-    ref = oracle.moe_mlp(x, idx, w, *wts, E=s.E, tokens=toks)
-    got = to_f64(out)[toks] if out_dtype == torch.float32 else bf16_host_bits(out)[toks]
-    return got, ref
+FULL_SHAPES = [inputs.MOE_20B_DECODE, inputs.MOE_20B_PREFILL, *inputs.MOE_120B.values()]
 
 
-def test_moe_20b_decode_T64_full():
-    got, ref = _full_moe(inputs.MOE_20B_DECODE, 64)
-    check_tolerance(got, ref, "20b decode")
-
-
-def test_moe_20b_decode_T64_bf16():
-    got, ref = _full_moe(inputs.MOE_20B_DECODE, 16, torch.bfloat16)
-    check_bf16_output(got, ref, "20b decode bf16")
-
-
-def test_moe_20b_prefill_T8192_sampled():
-    got, ref = _full_moe(inputs.MOE_20B_PREFILL, 24)
-    check_tolerance(got, ref, "20b prefill")
-
-
-@pytest.mark.parametrize("T", [1, 256, 4096])
-def test_moe_120b_sampled(T):
-    got, ref = _full_moe(inputs.MOE_120B[T], 12)
-    check_tolerance(got, ref, "120b T=%d" % T)
+@pytest.mark.parametrize("shape", FULL_SHAPES, ids=[s.name for s in FULL_SHAPES])
+def test_moe_full_layer_row_major(shape):
+    """Every token of the 20B-shaped (T = 64; T = 8192 with the skewed router) and 120B-shaped
+    (T = 1, 256, 4096) layers, internal routing, fp32 and bf16 outputs, against one oracle run
+    under the oracle's own routing."""
+    check_full_layer(shape, flags=0, tiled=False)

@@ -12,13 +12,12 @@ import torch
 import oracle
 from mxfp4_weight_quantized_amd import inputs
 import mxfp4_weight_quantized_amd as mx
-from parity_util import (DEV, bf16_host_bits, check_bf16_output, check_tolerance, moe_weights,
-                         moe_weights_dev, note, to_dev, to_f64)
+from parity_util import (DEV, FRAGILE_C, bf16_host_bits, check_bf16_output, check_full_layer,
+                         check_tolerance, moe_weights, moe_weights_dev, note, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
 
 MX = mx.MX_ACT_MXFP4
-FRAGILE_C = 4.0  # assumed fp32 error of g and u: 4 * 2^-24 * sqrt(H * sum of squared terms)
 
 
 # ------------------------------------------------------------------------------------ linear
@@ -100,45 +99,13 @@ def test_moe_mxact_is_deterministic():
     assert torch.equal(a, b)
 
 
-def _full(shape, n_sample, out_dtype=torch.float32):
-    s = shape
-    x = inputs.activations(s.seed, s.T, s.H)
-    wr, br = inputs.router(s.seed, s.E, s.H, s.bias_std)
-    wts = moe_weights(s.seed, s.E, s.H, s.F)
-    note("moe mx-act full %s" % s.name)
-    out, (lg, idx, w) = _run(x, moe_weights_dev(s.seed, s.E, s.H, s.F), s.k, out_dtype, wr=wr,
-                             br=br if s.bias_std else None)
-    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
-    oidx, ow = oracle.topk_softmax(lg, s.k)
-    np.testing.assert_array_equal(idx, oidx)
-    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
-    r = np.random.default_rng(s.seed + 1000)
-    busiest = np.bincount(idx.reshape(-1), minlength=s.E).argmax()
-    on_busiest = np.nonzero((idx == busiest).any(axis=1))[0]
-    toks = np.unique(np.concatenate([r.choice(s.T, size=min(s.T, n_sample), replace=False),
-                                     on_busiest[:4], [0, s.T - 1]])).astype(np.int32)
-    ref, _, slack = oracle.moe_mlp(x, idx, w, *wts, E=s.E, tokens=toks, mx_act=True,
-                                   fragile_c=FRAGILE_C)
-    got = to_f64(out)[toks] if out_dtype == torch.float32 else bf16_host_bits(out)[toks]
-    return got, ref, slack
+FULL_SHAPES = [inputs.MOE_20B_DECODE, inputs.MOE_20B_PREFILL, *inputs.MOE_120B.values()]
 
 
-def test_moe_mxact_20b_decode_T64():
-    got, ref, slack = _full(inputs.MOE_20B_DECODE, 64)
-    check_tolerance(got, ref, "20b decode mx-act", slack=slack)
-
-
-def test_moe_mxact_20b_decode_T64_bf16():
-    got, ref, slack = _full(inputs.MOE_20B_DECODE, 16, torch.bfloat16)
-    check_bf16_output(got, ref, "20b decode mx-act bf16", slack=slack)
-
-
-def test_moe_mxact_20b_prefill_T8192_sampled():
-    got, ref, slack = _full(inputs.MOE_20B_PREFILL, 24)
-    check_tolerance(got, ref, "20b prefill mx-act", slack=slack)
-
-
-@pytest.mark.parametrize("T", [1, 256, 4096])
-def test_moe_mxact_120b_sampled(T):
-    got, ref, slack = _full(inputs.MOE_120B[T], 12)
-    check_tolerance(got, ref, "120b mx-act T=%d" % T, slack=slack)
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("shape", FULL_SHAPES, ids=[s.name for s in FULL_SHAPES])
+def test_moe_mxact_full_layer(shape, tiled):
+    """Every token of the full-size layers with activations quantized on the fly, fp32 and bf16
+    outputs, against one oracle run of the activation variant (with its fragile-decision
+    slack)."""
+    check_full_layer(shape, flags=MX, tiled=tiled)

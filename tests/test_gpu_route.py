@@ -45,11 +45,14 @@ def test_route_topk_parity(T, H, E, k, bias):
         assert np.min(np.abs(np.diff(s[:k + 1]))) < 1e-4, "routing differs beyond a near-tie"
 
 
-# Routing inside mxfp4_moe_mlp: small batches split H over 2 or 4 workgroups per tile, whose
-# partial sums the selection adds up in split order (T=64/E=32 and T=9/E=4: four splits,
-# T=256/E=128: two, E=40: a ragged expert group). Same bar as the router alone.
+# Routing inside mxfp4_moe_mlp: small batches with more than one expert group split H over 2 or
+# 4 workgroups per tile, whose partial sums the selection adds up in split order (T=64/E=32 and
+# T=17/E=20: four splits, the latter with a ragged token tile and expert group; T=256/E=128:
+# two; E=40: a ragged expert group). T=9/E=4 is one expert group: the logits kernel selects
+# itself, no split. Same bar as the router alone.
 @pytest.mark.parametrize("T,H,E,k,bias", [(64, 2880, 32, 4, 0.0), (64, 2880, 40, 8, 0.5),
-                                          (9, 3072, 4, 2, 0.5), (256, 2880, 128, 4, 1.0)])
+                                          (9, 3072, 4, 2, 0.5), (256, 2880, 128, 4, 1.0),
+                                          (17, 2880, 20, 4, 0.5)])
 def test_route_inside_moe_call(T, H, E, k, bias):
     seed, F = 35 + T, 64
     x = inputs.activations(seed, T, H)
@@ -84,11 +87,14 @@ def test_route_ties_go_to_lower_index():
     assert np.all(idx0.cpu().numpy() == np.arange(k)) and np.all(w0.cpu().numpy() == 0.25)
 
 
-def _permute(idx, E):
-    note("permute P=%d E=%d" % (idx.size, E))
-    offs, perm, inv, status = mx.moe_permute(to_dev(idx), E)
-    torch.cuda.synchronize()
-    return offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), int(status.cpu()[0])
+def _permute(idx, E, use_workspace=False):
+    """moe_permute (ws = NULL: one workgroup; else the sliced form for large batches); the
+    fourth value is the device error word after the call (cleared before it)."""
+    note("permute P=%d E=%d ws=%d" % (idx.size, E, use_workspace))
+    assert mx.get_device_error() == 0
+    offs, perm, inv = mx.moe_permute(to_dev(idx), E, use_workspace=use_workspace)
+    st = mx.get_device_error()
+    return offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), st
 
 
 @pytest.mark.parametrize("T,k,E,skew", [(1, 1, 1, 0), (1, 4, 128, 0), (3, 2, 8, 0),
@@ -113,8 +119,9 @@ def test_permute_bit_exact(T, k, E, skew):
                                             (4096, 4, 128, 0, 0), (10001, 3, 7, 1, 0),
                                             (3000, 8, 256, 1, 0), (5000, 4, 16, 0, 1)])
 def test_permute_sliced_bit_exact(T, k, E, skew, bad):
-    """moe_permute_ws: large batches go through the per-slice histogram and scatter (two launches,
-    many workgroups); the result must be the oracle's counting sort element for element."""
+    """moe_permute with its workspace: large batches go through the per-slice histogram and
+    scatter (two launches, many workgroups); the result must be the oracle's counting sort
+    element for element, and equal the one-workgroup form (ws = NULL)."""
     r = np.random.default_rng(70 + T)
     if skew:
         p = np.exp(r.normal(0, 1.5, E)); p /= p.sum()
@@ -124,11 +131,8 @@ def test_permute_sliced_bit_exact(T, k, E, skew, bad):
     if bad:  # a few indices outside [0, E), in different slices
         for pos in (5, 4100, 9000, T * k - 1):
             idx.reshape(-1)[pos] = E + 3 if pos % 2 else -2
-    note("permute sliced P=%d E=%d bad=%d" % (idx.size, E, bad))
-    offs, perm, inv, status = mx.moe_permute(to_dev(idx), E, use_workspace=True)
-    torch.cuda.synchronize()
-    offs, perm, inv, st = offs.cpu().numpy(), perm.cpu().numpy(), inv.cpu().numpy(), int(status.cpu()[0])
-    assert st == bad
+    offs, perm, inv, st = _permute(idx, E, use_workspace=True)
+    assert st == (mx.MX_DEVERR_ROUTING if bad else 0)
     if not bad:
         o_offs, o_perm, o_inv = oracle.permute(idx, E)
         np.testing.assert_array_equal(offs, o_offs)
@@ -155,8 +159,35 @@ def test_permute_all_to_one_expert_and_empty_experts():
 def test_permute_flags_out_of_range_indices():
     idx = np.array([[0, 1], [5, 2], [-1, 0]], np.int32)
     offs, perm, inv, st = _permute(idx, 4)
-    assert st == 1
+    assert st == mx.MX_DEVERR_ROUTING
+    assert mx.get_device_error() == 0  # reading clears the word
     assert inv[2] == -1 and inv[4] == -1
     valid = np.array([0, 1, 3, 5])  # pairs with an index inside [0, 4)
     assert offs[-1] == 4 and sorted(perm[:4].tolist()) == valid.tolist()
     np.testing.assert_array_equal(perm[:4], [0, 5, 1, 3])  # experts 0,0,1,2 in pair order
+
+
+@pytest.mark.parametrize("T,H,E,k,bias", [(1, 2880, 128, 4, 0.0), (64, 2880, 32, 4, 0.5),
+                                          (37, 256, 40, 8, 0.5), (300, 96, 256, 8, 1.0)])
+def test_route_topk_without_logits(T, H, E, k, bias):
+    """logits = NULL: the workgroups cover all experts of their tokens and select from on-chip
+    memory (another split of H than with a logits buffer, so the fp32 sums may differ in the
+    last bits): indices equal the oracle's top-k except where two oracle logits are within fp32
+    noise, and the weights match the oracle's softmax."""
+    seed = 90 + T
+    x = inputs.activations(seed, T, H)
+    wr, br = inputs.router(seed, E, H, bias)
+    br = br if bias else None
+    note("route without logits T=%d H=%d E=%d k=%d" % (T, H, E, k))
+    lg, idx, w = mx.moe_route_topk(to_dev(x), to_dev(wr), None if br is None else to_dev(br), k,
+                                   want_logits=False)
+    torch.cuda.synchronize()
+    assert lg is None
+    idx, w = idx.cpu().numpy(), w.cpu().numpy()
+    ref = oracle.router_logits(x, wr, br)
+    oidx, ow = oracle.topk_softmax(ref, k)
+    same = np.all(idx == oidx, axis=1)
+    for t in np.nonzero(~same)[0]:
+        s = np.sort(ref[t])[::-1]
+        assert np.min(np.abs(np.diff(s[:k + 1]))) < 1e-4, "routing differs beyond a near-tie"
+    np.testing.assert_allclose(w[same], ow[same], rtol=2e-5, atol=1e-6)

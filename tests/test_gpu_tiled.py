@@ -13,12 +13,12 @@ import torch
 import oracle
 from mxfp4_weight_quantized_amd import inputs
 import mxfp4_weight_quantized_amd as mx
-from parity_util import (check_tolerance, moe_weights, moe_weights_dev, note, to_dev, to_f64)
+from parity_util import (FRAGILE_C, check_full_layer, check_tolerance, layer_weights_dev,
+                         moe_weights, moe_weights_dev, note, tiled_dev, to_dev, to_f64)
 
 pytestmark = pytest.mark.gpu
 
 TILED = mx.MX_WEIGHTS_TILED
-FRAGILE_C = 4.0  # assumed fp32 error of g and u: 4 * 2^-24 * sqrt(H * sum of squared terms)
 
 
 def _np_tile(packed, scales):
@@ -45,11 +45,6 @@ def test_tile_weights_is_the_documented_permutation(G, R, K):
     np.testing.assert_array_equal(st.cpu().numpy(), est)
 
 
-def _tiled(wdev):
-    gp, gs, dp, ds = wdev
-    return (*mx.mxfp4_tile_weights(gp, gs), *mx.mxfp4_tile_weights(dp, ds))
-
-
 def _routing(T, E, k, seed):
     r = np.random.default_rng(seed)
     idx = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -72,7 +67,7 @@ def test_moe_tiled_equals_row_major(T, H, F, E, k, flags):
     note("moe tiled vs row-major T=%d H=%d F=%d E=%d k=%d flags=%d" % (T, H, F, E, k, flags))
     a = mx.mxfp4_moe_mlp(x, *wd, k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32,
                          flags=flags)
-    b = mx.mxfp4_moe_mlp(x, *_tiled(wd), k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32,
+    b = mx.mxfp4_moe_mlp(x, *tiled_dev(wd), k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32,
                          flags=flags | TILED)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
@@ -83,11 +78,11 @@ def test_moe_tiled_equals_row_major_20b_prefill(flags):
     s = inputs.MOE_20B_PREFILL
     x = to_dev(inputs.activations(s.seed, s.T, s.H))
     wr, br = inputs.router(s.seed, s.E, s.H, s.bias_std)
-    wd = moe_weights_dev(s.seed, s.E, s.H, s.F)
+    wd = layer_weights_dev(s.seed, s.E, s.H, s.F)
     note("moe tiled vs row-major %s flags=%d" % (s.name, flags))
     kw = dict(wr=to_dev(wr), br=to_dev(br) if s.bias_std else None, out_dtype=torch.bfloat16)
     a = mx.mxfp4_moe_mlp(x, *wd, s.k, flags=flags, **kw)
-    b = mx.mxfp4_moe_mlp(x, *_tiled(wd), s.k, flags=flags | TILED, **kw)
+    b = mx.mxfp4_moe_mlp(x, *tiled_dev(wd), s.k, flags=flags | TILED, **kw)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
@@ -104,7 +99,7 @@ def test_moe_max_dims(T, E, k, tiled):
     wd = moe_weights_dev(seed, E, H, F)
     note("moe max dims T=%d H=F=%d E=%d k=%d tiled=%d" % (T, H, E, k, tiled))
     out, (lg, idx, w) = mx.mxfp4_moe_mlp(
-        to_dev(x), *(_tiled(wd) if tiled else wd), k, wr=to_dev(wr), br=to_dev(br),
+        to_dev(x), *(tiled_dev(wd) if tiled else wd), k, wr=to_dev(wr), br=to_dev(br),
         out_dtype=torch.float32, flags=TILED if tiled else 0, return_routing=True)
     torch.cuda.synchronize()
     lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
@@ -128,7 +123,7 @@ def test_moe_few_pairs_long_k(T, H, F, E, k, flags):
     note("moe few pairs T=%d H=%d F=%d E=%d k=%d flags=%d" % (T, H, F, E, k, flags))
     a = mx.mxfp4_moe_mlp(to_dev(x), *wd, k, topk_idx=idx_d, topk_w=w_d, out_dtype=torch.float32,
                          flags=flags)
-    b = mx.mxfp4_moe_mlp(to_dev(x), *_tiled(wd), k, topk_idx=idx_d, topk_w=w_d,
+    b = mx.mxfp4_moe_mlp(to_dev(x), *tiled_dev(wd), k, topk_idx=idx_d, topk_w=w_d,
                          out_dtype=torch.float32, flags=flags | TILED)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
@@ -139,40 +134,11 @@ def test_moe_few_pairs_long_k(T, H, F, E, k, flags):
         check_tolerance(to_f64(b), oracle.moe_mlp(x, idx, w, *wts, E=E), "moe few pairs T=%d" % T)
 
 
-def _full_tiled(shape, n_sample):
-    s = shape
-    x = inputs.activations(s.seed, s.T, s.H)
-    wr, br = inputs.router(s.seed, s.E, s.H, s.bias_std)
-    wts = moe_weights(s.seed, s.E, s.H, s.F)
-    note("moe tiled full %s" % s.name)
-    out, (lg, idx, w) = mx.mxfp4_moe_mlp(
-        to_dev(x), *_tiled(moe_weights_dev(s.seed, s.E, s.H, s.F)), s.k, wr=to_dev(wr),
-        br=to_dev(br) if s.bias_std else None, out_dtype=torch.float32, flags=TILED,
-        return_routing=True)
-    torch.cuda.synchronize()
-    lg, idx, w = lg.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
-    oidx, ow = oracle.topk_softmax(lg, s.k)
-    np.testing.assert_array_equal(idx, oidx)
-    np.testing.assert_allclose(w, ow, rtol=2e-6, atol=1e-7)
-    r = np.random.default_rng(s.seed + 7)
-    busiest = np.bincount(idx.reshape(-1), minlength=s.E).argmax()
-    on_busiest = np.nonzero((idx == busiest).any(axis=1))[0]
-    toks = np.unique(np.concatenate([r.choice(s.T, size=min(s.T, n_sample), replace=False),
-                                     on_busiest[:4], [0, s.T - 1]])).astype(np.int32)
-    ref = oracle.moe_mlp(x, idx, w, *wts, E=s.E, tokens=toks)
-    return to_f64(out)[toks], ref
+FULL_SHAPES = [inputs.MOE_20B_DECODE, inputs.MOE_20B_PREFILL, *inputs.MOE_120B.values()]
 
 
-def test_moe_tiled_20b_prefill_T8192_sampled():
-    got, ref = _full_tiled(inputs.MOE_20B_PREFILL, 24)
-    check_tolerance(got, ref, "20b prefill tiled")
-
-
-def test_moe_tiled_20b_decode_T64_full():
-    got, ref = _full_tiled(inputs.MOE_20B_DECODE, 64)
-    check_tolerance(got, ref, "20b decode tiled")
-
-
-def test_moe_tiled_120b_T4096_sampled():
-    got, ref = _full_tiled(inputs.MOE_120B[4096], 12)
-    check_tolerance(got, ref, "120b T=4096 tiled")
+@pytest.mark.parametrize("shape", FULL_SHAPES, ids=[s.name for s in FULL_SHAPES])
+def test_moe_full_layer_tiled(shape):
+    """The benchmarked weight layout: every token of the full-size layers against the oracle,
+    fp32 and bf16 outputs."""
+    check_full_layer(shape, flags=0, tiled=True)

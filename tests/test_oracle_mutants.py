@@ -14,7 +14,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "mx_oracle.c")
 PIN_TESTS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
              os.path.join(ROOT, "tests", "test_oracle_path.py"),
-             os.path.join(ROOT, "tests", "test_oracle_fragile.py")]
+             os.path.join(ROOT, "tests", "test_oracle_fragile.py"),
+             os.path.join(ROOT, "tests", "test_oracle_operand.py")]
 
 # (name, exact text in mx_oracle.c, replacement)
 MUTANTS = [
@@ -44,6 +45,17 @@ MUTANTS = [
      "prow = dn_packed + ((int64_t)e * F + m) * dn_row"),
     ("mx-act-h-skipped", "activation_row(hb, F, mx_act, h);", "activation_row(hb, F, 0, h);"),
     ("bf16-truncates", "nearbyint(a / quantum)", "floor(a / quantum)"),
+    # the weight operand of the products (bf16 operand on the bf16 path, exact on the FP4 path)
+    ("bf16-operand-skipped", "return bf16_operand ? g_dq_bf16[b][c] : g_dq_exact[b][c];",
+     "return g_dq_exact[b][c];"),
+    ("bf16-operand-in-fp4-linear", "acc += xr[kk] * weight_elem(prow, srow, kk, !mx_act);",
+     "acc += xr[kk] * weight_elem(prow, srow, kk, 1);"),
+    ("gate-up-exact-operand", "const double term = xr[kk] * weight_elem(prow, srow, kk, !mx_act);",
+     "const double term = xr[kk] * decode_elem(prow, srow, kk);"),
+    ("down-exact-operand", "acc += h[f] * weight_elem(prow, srow, f, !mx_act);",
+     "acc += h[f] * decode_elem(prow, srow, f);"),
+    ("tables-subnormal-flush", "g_dq_bf16[b][c] = mxo_double_from_bf16(mxo_bf16_from_double(g_dq_exact[b][c]));",
+     "g_dq_bf16[b][c] = fabs(g_dq_exact[b][c]) < 0x1p-126 ? 0.0 : mxo_double_from_bf16(mxo_bf16_from_double(g_dq_exact[b][c]));"),
     # the fragile-decision aid of the activation variant
     ("fragile-slack-unweighted", "sl[m] += wt * d;", "sl[m] += d;"),
     ("fragile-alt-two-steps", "if (up != neg) return (uint16_t)(b + 1);",

@@ -171,7 +171,10 @@ def test_moe_single_expert_is_dense_swiglu_mlp(golden_dir):
     np.testing.assert_allclose(hgot, href, rtol=2 ** -7, atol=1e-30)
     ref_from_h = hgot @ _decode_np(dn_p[0], dn_s[0], tab).T
     np.testing.assert_allclose(out, ref_from_h, rtol=1e-11, atol=1e-14)
-    np.testing.assert_allclose(out, ref, rtol=5e-3 * 0 + 2e-2, atol=1e-3)
+    # secondary, loose check of the whole chain against numpy (the exact pin is the line above):
+    # numpy's h is rounded to bf16 through fp32, so a few h elements may sit one bf16 ulp
+    # (2^-8 relative) away from the oracle's, and each such flip moves the outputs a little
+    np.testing.assert_allclose(out, ref, rtol=2e-2, atol=1e-3)
 
 
 def test_moe_all_experts_weighted_sum(golden_dir):
