@@ -37,9 +37,9 @@ def test_linear_single_layer_4x256x512():
 def test_linear_decode_sweep_bf16(M):
     """K = 2880, N = 5760, bf16 out, seed 1."""
     y, ref = _linear_case(M, 2880, 5760, 1, torch.bfloat16)
-    check_bf16_output(bf16_host_bits(y), ref, "linear M=%d" % M)
     y32, _ = _linear_case(M, 2880, 5760, 1, torch.float32)
     check_tolerance(to_f64(y32), ref, "linear M=%d fp32" % M)
+    check_bf16_output(bf16_host_bits(y), ref, "linear M=%d" % M, got_f32=to_f64(y32))
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 32, 16), (17, 96, 200), (5, 64, 48), (100, 2880, 300),

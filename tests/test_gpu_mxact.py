@@ -46,7 +46,7 @@ def test_linear_mxact_decode_sweep(M):
     y, ref = _linear_case(M, 2880, 5760, 1, torch.float32)
     check_tolerance(to_f64(y), ref, "linear mx-act M=%d" % M)
     yb, _ = _linear_case(M, 2880, 5760, 1, torch.bfloat16)
-    check_bf16_output(bf16_host_bits(yb), ref, "linear mx-act M=%d bf16" % M)
+    check_bf16_output(bf16_host_bits(yb), ref, "linear mx-act M=%d bf16" % M, got_f32=to_f64(y))
 
 
 @pytest.mark.parametrize("M,K,N", [(17, 96, 200), (5, 64, 48), (100, 2880, 300), (130, 320, 130),
