@@ -191,6 +191,23 @@ size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc);
 mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * mxfp4_moe_mlp_noalloc -- mxfp4_moe_mlp for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels, with the workspace taken from an array the library holds on each device
+ * (MX_NOALLOC_SCRATCH_BYTES per device, kept until the process ends). The call allocates
+ * nothing; the caller still owns desc's inputs and outputs.
+ *   Problems whose workspace (mxfp4_moe_mlp_workspace(desc)) exceeds MX_NOALLOC_SCRATCH_BYTES
+ *   return MX_ERR_WORKSPACE before anything is launched (32 MiB covers decode batches of up to
+ *   about 1300 token-expert pairs at H = F = 2880).
+ *   Every call on a device shares that device's array, which keeps the last call's contents
+ *   (no call needs it cleared): calls that overlap on one device -- on different streams, or from
+ *   different threads -- race and must be serialized by the caller. Other errors as for
+ *   mxfp4_moe_mlp; mx_workspace_status does not apply (read mx_get_device_error instead).
+ * ---------------------------------------------------------------------------------------------- */
+#define MX_NOALLOC_SCRATCH_BYTES (32u << 20)
+mx_status mxfp4_moe_mlp_noalloc(const mx_moe_desc* desc, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * mxfp4_linear -- dense weight-only linear y = x W^T with W packed MXFP4 [N][K] (the single
  * matrix product the MoE MLP's grouped GEMMs are made of; [EN] "MXFP4 4-Bit Quantization").
  *   x [M][K] bf16; packed [N][K/2], scales [N][K/32]; y [M][N] fp32 or bf16 (y_dtype).

@@ -23,6 +23,7 @@ MX_F32, MX_BF16 = 0, 1
 MX_ACT_MXFP4 = 0x1
 MX_WEIGHTS_TILED = 0x2
 MX_DEVERR_ROUTING = 0x1
+MX_NOALLOC_SCRATCH_BYTES = 32 << 20
 STATUS_NAMES = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
                 4: "MX_ERR_DTYPE", 5: "MX_ERR_WORKSPACE", 6: "MX_ERR_UNSUPPORTED", 7: "MX_ERR_HIP"}
 
@@ -71,6 +72,7 @@ SIGNATURES = {
     "moe_permute": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "mxfp4_moe_mlp_workspace": (_SZ, [ctypes.POINTER(MoeDesc)]),
     "mxfp4_moe_mlp": (_INT, [ctypes.POINTER(MoeDesc), _VP, _SZ, _VP]),
+    "mxfp4_moe_mlp_noalloc": (_INT, [ctypes.POINTER(MoeDesc), _VP]),
     "mxfp4_linear_workspace": (_SZ, [_I32, _I32, _I32, _U32]),
     "mxfp4_linear": (_INT, [_VP, _I32, _I32, _VP, _VP, _I32, _VP, _INT, _U32, _VP, _SZ, _VP]),
     "mx_last_error": (ctypes.c_char_p, []),
@@ -261,6 +263,13 @@ def mxfp4_moe_mlp(x, gu_packed, gu_scales, dn_packed, dn_scales, k, wr=None, br=
     if return_routing:
         return out, routing
     return out
+
+
+def mxfp4_moe_mlp_noalloc(desc: MoeDesc, stream=None):
+    """mxfp4_moe_mlp_noalloc on a descriptor built by make_moe_desc (its tensors, the output
+    included, are the caller's): the workspace is the library's own device array, so neither
+    this wrapper nor the library allocates anything."""
+    _check(lib().mxfp4_moe_mlp_noalloc(ctypes.byref(desc), _stream(stream)))
 
 
 def mxfp4_linear_workspace(M: int, K: int, N: int, flags: int = 0) -> int:

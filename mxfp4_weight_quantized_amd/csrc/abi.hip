@@ -275,6 +275,12 @@ MX_API size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc) {
   return moe_layout(*desc).total;
 }
 
+namespace {
+// The launch sequence of mxfp4_moe_mlp on a checked descriptor, its layout and a workspace of at
+// least L.total bytes (256-byte aligned).
+mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStream_t s);
+}  // namespace
+
 MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void* stream) {
   mx_status st = check_moe_desc(desc);
   if (st != MX_OK) return st;
@@ -285,12 +291,60 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   if (!aligned(ws, 256)) return fail(MX_ERR_ALIGN, "workspace must be 256-byte aligned");
   st = check_device();
   if (st != MX_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  char* w = static_cast<char*>(ws);
+  return moe_mlp_run(d, L, static_cast<char*>(ws), (hipStream_t)stream);
+}
+
+// ---- the allocation-free variant: the workspace is the library's own device array ----
+// One array per device (each GPU the library runs on holds its own copy at its own address, until
+// the process ends). Host code never passes `scratch` itself -- on the host that name is only a
+// stand-in -- but the device address hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[MX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::atomic<char*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr and an error message on failure).
+char* scratch_on_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  char* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || a == nullptr) {
+      hip_fail(e, "scratch lookup");
+      return nullptr;
+    }
+    p = static_cast<char*>(a);
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+}  // namespace
+
+MX_API mx_status mxfp4_moe_mlp_noalloc(const mx_moe_desc* desc, void* stream) {
+  mx_status st = check_moe_desc(desc);
+  if (st != MX_OK) return st;
+  const mx_moe_desc& d = *desc;
+  if (d.T == 0) return ok();
+  const MoeLayout L = moe_layout(d);
+  if (L.total > (size_t)MX_NOALLOC_SCRATCH_BYTES)
+    return fail(MX_ERR_WORKSPACE, "this problem needs %zu bytes of workspace; the allocation-free "
+                "entry point holds %zu (use mxfp4_moe_mlp with a caller workspace)",
+                L.total, (size_t)MX_NOALLOC_SCRATCH_BYTES);
+  st = check_device();
+  if (st != MX_OK) return st;
+  char* w = scratch_on_device();
+  if (w == nullptr) return MX_ERR_HIP;
+  return moe_mlp_run(d, L, w, (hipStream_t)stream);
+}
+
+namespace {
+mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStream_t s) {
+  hipError_t e;
   int32_t* status = reinterpret_cast<int32_t*>(w + L.status);
   const int32_t* idx;
   const float* tw;
-  hipError_t e;
   // small batches: the router launch computes the logits only and the permutation launch makes
   // the top-k selection first (one launch fewer)
   bool select_in_permute = false;
@@ -387,6 +441,7 @@ MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_byte
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ok();
 }
+}  // namespace
 
 // Linear workspace: [quantized x, its scales] (MX_ACT_MXFP4) then [fp32 partial sums of the K
 // splits] (decode-sized M).

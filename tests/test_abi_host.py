@@ -183,6 +183,15 @@ def test_moe_workspace_query_and_errors(L):
     assert L.mxfp4_moe_mlp(ctypes.byref(small), _fake(), need - 1, None) == mx.MX_ERR_WORKSPACE
     assert L.mxfp4_moe_mlp(ctypes.byref(small), None, need, None) == mx.MX_ERR_WORKSPACE
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(T=0)), None, 0, None) == mx.MX_OK
+    # the allocation-free entry point: same checks, and problems beyond its array are rejected
+    # on the host before anything runs
+    big = _desc(T=8192, H=2880, F=2880, E=32, k=4)
+    assert mx.mxfp4_moe_mlp_workspace(big) > mx.MX_NOALLOC_SCRATCH_BYTES
+    assert L.mxfp4_moe_mlp_noalloc(ctypes.byref(big), None) == mx.MX_ERR_WORKSPACE
+    assert "allocation-free" in mx.last_error()
+    assert L.mxfp4_moe_mlp_noalloc(ctypes.byref(_desc(k=9)), None) == mx.MX_ERR_SHAPE
+    assert L.mxfp4_moe_mlp_noalloc(None, None) == mx.MX_ERR_NULL
+    assert L.mxfp4_moe_mlp_noalloc(ctypes.byref(_desc(T=0)), None) == mx.MX_OK
 
 
 def test_linear_argument_errors(L):
