@@ -111,8 +111,8 @@ def kernel_work(name, T, H, F, E, k, touched, P, out_bytes, mxact):
     """Algorithmic (flops, bytes) of one launch of a kernel kind."""
     wb = 17.0 / 32.0                 # packed bytes per weight (nibble + 1/32 scale byte)
     abytes = 17.0 / 32.0 if mxact else 2.0   # activation bytes per element read by a GEMM
-    if name == "moe_gate_up_swiglu":
-        return 2.0 * P * H * 2 * F, touched * 2 * F * H * wb + T * H * abytes + P * F * 2
+    if name == "moe_gate_up_swiglu":   # h out: bf16, or MXFP4 (quantized in the epilogue)
+        return 2.0 * P * H * 2 * F, touched * 2 * F * H * wb + T * H * abytes + P * F * abytes
     if name == "moe_down_weighted":
         return 2.0 * P * F * H, touched * H * F * wb + P * F * abytes + P * H * 4
     if name == "moe_combine":
@@ -121,8 +121,8 @@ def kernel_work(name, T, H, F, E, k, touched, P, out_bytes, mxact):
         return 2.0 * T * E * H, T * H * 2 + E * H * 2 + T * E * 4 + T * k * 8
     if name == "permute":
         return 0.0, T * k * 4 * 4 + (E + 1) * 4
-    if name == "quantize":   # activation variant: x along H and h along F, two launches
-        return 0.0, (T * H + P * F) * (2 + wb) / 2
+    if name == "quantize":   # activation variant: x along H (h is quantized by gate_up)
+        return 0.0, T * H * (2 + wb)
     return 0.0, 0.0
 
 

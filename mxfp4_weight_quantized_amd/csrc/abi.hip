@@ -136,7 +136,8 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
   L.tiles = take((size_t)L.max_tiles * 8);
   L.pcounts_bytes = mx::permute_sliced_workspace(d.T, d.k, d.E);  // 0: one-workgroup permutation
   L.pcounts = take(L.pcounts_bytes);
-  L.h = take(P * (size_t)d.F * 2);
+  // bf16 h (the activation variant quantizes h in the gate_up epilogue and keeps only hq, hqs)
+  L.h = (d.flags & MX_ACT_MXFP4) ? 0 : take(P * (size_t)d.F * 2);
   L.y = take(P * (size_t)d.H * 4);
   if (d.flags & MX_ACT_MXFP4) {
     L.xq = take(T * (size_t)d.H / 2);
@@ -414,7 +415,7 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   g.topk_w = tw;
   g.gu_packed = d.gu_packed; g.gu_scales = d.gu_scales;
   g.dn_packed = d.dn_packed; g.dn_scales = d.dn_scales;
-  g.h = reinterpret_cast<uint16_t*>(w + L.h);
+  g.h = mx_act ? nullptr : reinterpret_cast<uint16_t*>(w + L.h);
   g.y = reinterpret_cast<float*>(w + L.y);
   g.out = d.out;
   g.out_bf16 = d.out_dtype == MX_BF16;
@@ -423,12 +424,6 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
     e = mx::launch_moe_gate_up(g, s);
   }
   if (e != hipSuccess) return hip_fail(e, "gate_up launch");
-  if (mx_act) {
-    // the bf16 SwiGLU output h, quantized along F
-    ProfScope ps(PK_QUANTIZE, s);
-    e = mx::launch_quantize(g.h, true, (int64_t)d.T * d.k * (d.F / 32), g.hq, g.hqs, s);
-    if (e != hipSuccess) return hip_fail(e, "h quantize launch");
-  }
   {
     ProfScope ps(PK_DOWN, s);
     e = mx::launch_moe_down(g, s);

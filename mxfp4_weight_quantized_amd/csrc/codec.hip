@@ -11,98 +11,48 @@
 // |x|'s bit pattern with the bit patterns of the seven E2M1 decision points times 2^s, and
 // decoding assembles sign, exponent and mantissa fields directly.
 //
-// Mapping: eight lanes per 32-element block, four consecutive elements per lane, so a wave reads
-// 1 KB (fp32) of contiguous input per instruction and writes 128 contiguous packed bytes.
+// Mapping: the quantizer takes one 32-element block per thread; the decoder eight lanes per block,
+// four consecutive elements per lane.
 #include "mx_device.h"
 #include "mx_launch.h"
 
 namespace mx {
 namespace {
 
-// Bit pattern of (1 + mant23 / 2^23) * 2^e2 as fp32, exact (normal or subnormal) for the
-// decision points used below (their mantissas have at least 21 trailing zero bits and
-// e2 >= -129 keeps the subnormal shift <= 3).
-__device__ __forceinline__ uint32_t pow2_times(uint32_t mant23, int e2) {
-  int be = e2 + 127;
-  if (be >= 1) return ((uint32_t)be << 23) | mant23;
-  return (0x800000u | mant23) >> (1 - be);
-}
-
-// E2M1 magnitude code (0..7) of |x| / 2^s for |x| given as fp32 bits u (sign cleared), using
-// the seven decision points 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (times 2^s). A value exactly at a
-// decision point goes to the code whose mantissa bit is 0: strict ">" where the lower neighbour
-// is even, ">=" where the upper neighbour is even.
-struct Thresholds {
-  uint32_t t[7];
-  __device__ __forceinline__ explicit Thresholds(int s) {
-    t[0] = pow2_times(0x000000u, s - 2);  // 0.25
-    t[1] = pow2_times(0x400000u, s - 1);  // 0.75
-    t[2] = pow2_times(0x200000u, s);      // 1.25
-    t[3] = pow2_times(0x600000u, s);      // 1.75
-    t[4] = pow2_times(0x200000u, s + 1);  // 2.5
-    t[5] = pow2_times(0x600000u, s + 1);  // 3.5
-    t[6] = pow2_times(0x200000u, s + 2);  // 5
-  }
-  __device__ __forceinline__ uint32_t code(uint32_t u) const {
-    return (uint32_t)(u > t[0]) + (uint32_t)(u >= t[1]) + (uint32_t)(u > t[2]) +
-           (uint32_t)(u >= t[3]) + (uint32_t)(u > t[4]) + (uint32_t)(u >= t[5]) +
-           (uint32_t)(u > t[6]);
-  }
-};
-
-// Scale exponent s from the largest |x| bit pattern of the block (m < 0x7f800000: finite).
-__device__ __forceinline__ int scale_exponent(uint32_t m) {
-  uint32_t be = m >> 23;                // biased exponent of amax; 0 for zero or subnormal
-  if (be == 0) return -127;             // floor(log2 amax) <= -127, clamped
-  int s = (int)be - 127 - 2;
-  return s < -127 ? -127 : s;
-}
-
+// One thread per 32-element block (bf16 inputs: quantize_block32_bf16, the function the
+// activation variant's gate_up epilogue uses too; fp32 inputs: the integer quantize_block32):
+// a wave reads 4 KB (bf16) or 8 KB (fp32) of contiguous input and writes 1 KB of packed codes and
+// 64 scale bytes.
 template <bool BF16_IN>
 __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ src,
                                                        int64_t nblocks,
                                                        uint8_t* __restrict__ packed,
                                                        uint8_t* __restrict__ scales) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t blk = gid >> 3;
-  const int sub = (int)(gid & 7);
-  const bool active = blk < nblocks;
-  uint32_t u[4] = {0, 0, 0, 0};
-  if (active) {
-    const int64_t e0 = blk * 32 + sub * 4;
-    if (BF16_IN) {
-      uint2 v = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + e0);
-      u[0] = v.x << 16; u[1] = v.x & 0xffff0000u; u[2] = v.y << 16; u[3] = v.y & 0xffff0000u;
-    } else {
-      uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(src) + e0);
-      u[0] = v.x; u[1] = v.y; u[2] = v.z; u[3] = v.w;
-    }
-  }
-  // Largest magnitude bit pattern of the block: integer max of |x| patterns orders finite values
-  // by magnitude and puts Inf/NaN above them all.
-  uint32_t m = 0;
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= nblocks) return;
+  uint32_t q[4], sb;
+  if (BF16_IN) {  // 8-byte aligned rows of bf16
+    const uint2* p = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(src) + blk * 32);
+    uint32_t w[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) m = max(m, u[i] & 0x7fffffffu);
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 4));
-  if (!active) return;
-
-  uint32_t sbyte, codes = 0;
-  if (m >= 0x7f800000u) {
-    sbyte = 255;                        // NaN or Inf in the block
-  } else {
-    const int s = scale_exponent(m);
-    sbyte = (uint32_t)(s + 127);
-    const Thresholds th(s);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t c = th.code(u[i] & 0x7fffffffu) | ((u[i] >> 28) & 8u);
-      codes |= c << (4 * i);
+    for (int v = 0; v < 8; ++v) {
+      const uint2 d = p[v];
+      w[2 * v] = d.x;
+      w[2 * v + 1] = d.y;
     }
+    sb = quantize_block32_bf16(w, q);
+  } else {        // 16-byte aligned rows of fp32
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(src) + blk * 32);
+    uint32_t u[32];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const uint4 d = p[v];
+      u[4 * v] = d.x; u[4 * v + 1] = d.y; u[4 * v + 2] = d.z; u[4 * v + 3] = d.w;
+    }
+    sb = quantize_block32(u, q);
   }
-  *reinterpret_cast<uint16_t*>(packed + blk * 16 + sub * 2) = (uint16_t)codes;
-  if (sub == 0) scales[blk] = (uint8_t)sbyte;
+  *reinterpret_cast<uint4*>(packed + blk * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+  scales[blk] = (uint8_t)sb;
 }
 
 // fp32 bit pattern of E2M1 code c times 2^(b-127), built field by field.
@@ -174,12 +124,13 @@ __global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restr
 hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8_t* packed,
                            uint8_t* scales, hipStream_t stream) {
   if (nblocks == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((nblocks + 255) / 256);
   if (bf16_in)
-    hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid_for(nblocks)), dim3(256), 0, stream, src,
-                       nblocks, packed, scales);
+    hipLaunchKernelGGL(quantize_kernel<true>, dim3(grid), dim3(256), 0, stream, src, nblocks,
+                       packed, scales);
   else
-    hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid_for(nblocks)), dim3(256), 0, stream, src,
-                       nblocks, packed, scales);
+    hipLaunchKernelGGL(quantize_kernel<false>, dim3(grid), dim3(256), 0, stream, src, nblocks,
+                       packed, scales);
   return hipGetLastError();
 }
 

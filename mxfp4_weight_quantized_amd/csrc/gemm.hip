@@ -49,7 +49,8 @@ struct GemmKArgs {
   int M;                      // dense rows
   int rows_total;             // rows of the (permuted) row space: P grouped, M dense
   int F;                      // gate_up: up rows start at F
-  void* out;
+  void* out;                  // gate_up with FP4 activations: packed codes of h [rows][F/2]
+  uint8_t* out_scales;        //   and their scale bytes [rows][F/32]
   int out_bf16;
   int gn;                     // column tiles per XCD super-tile (set by the launcher)
   int k_splits;               // linear only: K range split over blockIdx.z (<= 1: none); out
@@ -725,13 +726,37 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
               (uint16_t)f32_to_bf16_bits(hv);
         }
     barrier_lds();
-    uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
-    for (int c = tid; c < BM * CPR; c += NT) {
-      const int lr = c / CPR, cc = c % CPR;
-      const int r = r0 + lr, col = nt * BNH + cc * 8;
-      if (r < row_end && col < p.F)
-        *reinterpret_cast<uint4*>(h + (int64_t)r * p.F + col) =
-            *reinterpret_cast<const uint4*>(sh + lr * LDH + cc * 8);
+    if constexpr (AFP4) {
+      // FP4 activations: the down product takes h as MXFP4, so each 32-column block of the bf16
+      // tile is quantized here (the codec's bf16 quantizer, the same function) and only its 16
+      // code bytes and scale byte leave the chip
+      constexpr int BPR = BNH / 32;  // 32-element blocks per tile row
+      uint8_t* hq = reinterpret_cast<uint8_t*>(p.out);
+      for (int c = tid; c < BM * BPR; c += NT) {
+        const int lr = c / BPR, cb = c % BPR;
+        const int r = r0 + lr, col = nt * BNH + cb * 32;
+        if (r >= row_end || col >= p.F) continue;
+        const uint4* src = reinterpret_cast<const uint4*>(sh + lr * LDH + cb * 32);
+        uint32_t w[16];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint4 w8 = src[v];
+          w[4 * v] = w8.x; w[4 * v + 1] = w8.y; w[4 * v + 2] = w8.z; w[4 * v + 3] = w8.w;
+        }
+        uint32_t q[4];
+        const uint32_t sb = quantize_block32_bf16(w, q);
+        *reinterpret_cast<uint4*>(hq + (int64_t)r * (p.F >> 1) + (col >> 1)) = make_uint4(q[0], q[1], q[2], q[3]);
+        p.out_scales[(int64_t)r * (p.F >> 5) + (col >> 5)] = (uint8_t)sb;
+      }
+    } else {
+      uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
+      for (int c = tid; c < BM * CPR; c += NT) {
+        const int lr = c / CPR, cc = c % CPR;
+        const int r = r0 + lr, col = nt * BNH + cc * 8;
+        if (r < row_end && col < p.F)
+          *reinterpret_cast<uint4*>(h + (int64_t)r * p.F + col) =
+              *reinterpret_cast<const uint4*>(sh + lr * LDH + cc * 8);
+      }
     }
   } else if constexpr (MODE == MODE_DOWN && BM * (BN + 4) * 4 <= STAGES * (int)sizeof(Stage)) {
     // Y the same way: the fp32 tile (rows padded by 16 bytes) in the stage buffers, then whole
@@ -1019,6 +1044,8 @@ hipError_t gate_up_tw(GemmKArgs g, const MoeGemmArgs& m, hipStream_t stream) {
   if (m.mx_act) {
     g.A = reinterpret_cast<const uint16_t*>(m.xq);  // packed codes, addressed in bytes
     g.Asc = m.xqs;
+    g.out = m.hq;  // h leaves the epilogue quantized
+    g.out_scales = m.hqs;
     if (pre) return launch_moe_gemm<CfgPreGU4, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);
     if (use_tiny_tiles(m.T, m.k, m.E, 2 * m.F))
       return launch_moe_gemm<CfgTinyGU, MODE_GATE_UP, true, TW>(g, m.max_tiles, m.F, stream);

@@ -68,6 +68,96 @@ __device__ __forceinline__ f32x4 mfma_fp4_16x16x128(u32x4 a, u32x4 b, uint32_t s
 }
 
 // ---------------------------------------------------------------------------------------------
+// MXFP4 quantization (the library's rule, on integer bit patterns only: the results do not
+// depend on the denormal mode). Used by the codec kernels and by the epilogue that quantizes the
+// SwiGLU output of the activation variant.
+// ---------------------------------------------------------------------------------------------
+// Bit pattern of (1 + mant23 / 2^23) * 2^e2 as fp32, exact (normal or subnormal) for the
+// decision points used below (their mantissas have at least 21 trailing zero bits and
+// e2 >= -129 keeps the subnormal shift <= 3).
+__device__ __forceinline__ uint32_t pow2_times(uint32_t mant23, int e2) {
+  int be = e2 + 127;
+  if (be >= 1) return ((uint32_t)be << 23) | mant23;
+  return (0x800000u | mant23) >> (1 - be);
+}
+
+// E2M1 magnitude code (0..7) of |x| / 2^s for |x| given as fp32 bits u (sign cleared), using
+// the seven decision points 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (times 2^s). A value exactly at a
+// decision point goes to the code whose mantissa bit is 0: strict ">" where the lower neighbour
+// is even, ">=" where the upper neighbour is even.
+struct Thresholds {
+  uint32_t t[7];
+  __device__ __forceinline__ explicit Thresholds(int s) {
+    t[0] = pow2_times(0x000000u, s - 2);  // 0.25
+    t[1] = pow2_times(0x400000u, s - 1);  // 0.75
+    t[2] = pow2_times(0x200000u, s);      // 1.25
+    t[3] = pow2_times(0x600000u, s);      // 1.75
+    t[4] = pow2_times(0x200000u, s + 1);  // 2.5
+    t[5] = pow2_times(0x600000u, s + 1);  // 3.5
+    t[6] = pow2_times(0x200000u, s + 2);  // 5
+  }
+  __device__ __forceinline__ uint32_t code(uint32_t u) const {
+    return (uint32_t)(u > t[0]) + (uint32_t)(u >= t[1]) + (uint32_t)(u > t[2]) +
+           (uint32_t)(u >= t[3]) + (uint32_t)(u > t[4]) + (uint32_t)(u >= t[5]) +
+           (uint32_t)(u > t[6]);
+  }
+};
+
+// Scale exponent s from the largest |x| bit pattern of the block (m < 0x7f800000: finite).
+__device__ __forceinline__ int scale_exponent(uint32_t m) {
+  uint32_t be = m >> 23;                // biased exponent of amax; 0 for zero or subnormal
+  if (be == 0) return -127;             // floor(log2 amax) <= -127, clamped
+  int s = (int)be - 127 - 2;
+  return s < -127 ? -127 : s;
+}
+
+// Quantizes one 32-element block given as fp32 bit patterns u[0..31] (bf16 inputs: their bits
+// shifted up by 16). Returns the scale byte and sets the 16 packed bytes (element 2j in the low
+// nibble of byte j) as four dwords. A block holding NaN or Inf gets byte 255 and codes 0.
+__device__ __forceinline__ uint32_t quantize_block32(const uint32_t (&u)[32], uint32_t (&q)[4]) {
+  uint32_t m = 0;  // integer max of |x| orders finite values by magnitude, Inf/NaN above all
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, u[i] & 0x7fffffffu);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = 0;
+  if (m >= 0x7f800000u) return 255u;
+  const int s = scale_exponent(m);
+  const Thresholds th(s);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t c = th.code(u[i] & 0x7fffffffu) | ((u[i] >> 28) & 8u);
+    q[i >> 3] |= c << (4 * (i & 7));
+  }
+  return (uint32_t)(s + 127);
+}
+
+// The same for a block of 32 bf16 values given as 16 dwords (element 2j in the low half of dword
+// j), on the hardware conversion: v_cvt_scalef32_pk_fp4_bf16 with scale 2^s divides by the scale,
+// rounds to the nearest E2M1 value with ties to the even code, saturates at 6 and keeps the sign
+// bit (zeros included) -- the rule above exactly: on gfx950 it gives the integer rule's code for
+// every one of the 65 536 bf16 values at every scale exponent s in [-127, 127] (NaN and Inf, which
+// never reach it, aside). Two codes per instruction instead of about 36 integer operations.
+__device__ __forceinline__ uint32_t quantize_block32_bf16(const uint32_t (&w)[16],
+                                                          uint32_t (&q)[4]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = max(m, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) q[j] = 0;
+  if (m >= 0x7f80u) return 255u;
+  const int s = scale_exponent(m << 16);
+  const float scale = __builtin_amdgcn_ldexpf(1.0f, s);  // exact, 2^-127 included
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // byte b of dword j: elements 8j + 2b, 8j + 2b + 1
+    uint32_t d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, __builtin_bit_cast(bf16x2, w[4 * j]), scale, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[4 * j + 1]), scale, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[4 * j + 2]), scale, 2);
+    q[j] = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[4 * j + 3]), scale, 3);
+  }
+  return (uint32_t)(s + 127);
+}
+
+// ---------------------------------------------------------------------------------------------
 // Memory helpers
 // ---------------------------------------------------------------------------------------------
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
