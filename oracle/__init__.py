@@ -44,6 +44,14 @@ def _P(t):
     return ctypes.POINTER(t)
 
 
+class ActParams(ctypes.Structure):
+    """Mirror of mxo_act_params (the expert activation's parameters)."""
+    _fields_ = [("interleaved", ctypes.c_int), ("alpha", ctypes.c_double),
+                ("limit", ctypes.c_double), ("up_shift", ctypes.c_double),
+                ("gu_bias", ctypes.POINTER(ctypes.c_float)),
+                ("dn_bias", ctypes.POINTER(ctypes.c_float))]
+
+
 def lib():
     """Load the oracle library, building it first if it is not there."""
     global _lib
@@ -79,6 +87,10 @@ def lib():
             "mxo_moe_mlp_ex": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, _P(u16), _P(i32),
                                        _P(f32), _P(u8), _P(u8), _P(u8), _P(u8), _P(i32), c_int,
                                        _P(f64), _P(u16), f64, _P(u16), _P(f64)]),
+            "mxo_moe_mlp_act": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, _P(u16), _P(i32),
+                                        _P(f32), _P(u8), _P(u8), _P(u8), _P(u8), _P(i32), c_int,
+                                        _P(f64), _P(u16), f64, _P(u16), _P(f64),
+                                        ctypes.POINTER(ActParams)]),
             "mxo_num_threads": (c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -211,7 +223,8 @@ def linear(x_bf16, packed, scales, mx_act: bool = False) -> np.ndarray:
 
 
 def moe_mlp(x_bf16, topk_idx, topk_w, gu_packed, gu_scales, dn_packed, dn_scales, E: int,
-            tokens=None, mx_act: bool = False, want_h: bool = False, fragile_c: float | None = None):
+            tokens=None, mx_act: bool = False, want_h: bool = False, fragile_c: float | None = None,
+            act: dict | None = None):
     """mxo_moe_mlp: fp64 output rows [n_tokens, H] (and optionally the bf16 h rows).
 
     Shapes: x [T, H] bf16 bits; topk_idx/topk_w [T, k]; gu_packed [E, 2F, H/2]; gu_scales
@@ -220,7 +233,11 @@ def moe_mlp(x_bf16, topk_idx, topk_w, gu_packed, gu_scales, dn_packed, dn_scales
     fragile_c (activation variant): also return (h_alt [n, k, F], slack [n, H]) from
     mxo_moe_mlp_ex -- the h quantization decisions an fp32 implementation may take the other
     way, with fp32 errors of g and u assumed below fragile_c * 2^-24 * sqrt(H * sum terms^2),
-    and the bound on the output change they can cause. Returned as (out, [h,] h_alt, slack)."""
+    and the bound on the output change they can cause. Returned as (out, [h,] h_alt, slack).
+
+    act (mxo_moe_mlp_act): the expert activation's parameters, a dict with any of interleaved
+    (bool), alpha, limit, up_shift (floats) and gu_bias [E, 2F], dn_bias [E, H] (fp32 arrays);
+    None = the plain SwiGLU."""
     x = _as(x_bf16, np.uint16)
     T, H = x.shape
     idx = _as(topk_idx, np.int32)
@@ -238,13 +255,26 @@ def moe_mlp(x_bf16, topk_idx, topk_w, gu_packed, gu_scales, dn_packed, dn_scales
             _ptr(w, ctypes.c_float), _ptr(gp, ctypes.c_uint8), _ptr(gs, ctypes.c_uint8),
             _ptr(dp, ctypes.c_uint8), _ptr(ds, ctypes.c_uint8), _ptr(tok, ctypes.c_int32), n,
             _ptr(out, ctypes.c_double), _ptr(h, ctypes.c_uint16))
-    if fragile_c is None:
-        rc = lib().mxo_moe_mlp(*args)
-    else:
+    h_alt = slack = None
+    if fragile_c is not None:
         h_alt = np.zeros((n, k, F), np.uint16)
         slack = np.zeros((n, H), np.float64)
-        rc = lib().mxo_moe_mlp_ex(*args, float(fragile_c), _ptr(h_alt, ctypes.c_uint16),
-                                  _ptr(slack, ctypes.c_double))
+    if act is None:
+        if fragile_c is None:
+            rc = lib().mxo_moe_mlp(*args)
+        else:
+            rc = lib().mxo_moe_mlp_ex(*args, float(fragile_c), _ptr(h_alt, ctypes.c_uint16),
+                                      _ptr(slack, ctypes.c_double))
+    else:
+        gb = None if act.get("gu_bias") is None else _as(act["gu_bias"], np.float32)
+        db = None if act.get("dn_bias") is None else _as(act["dn_bias"], np.float32)
+        assert gb is None or gb.size == E * 2 * F
+        assert db is None or db.size == E * H
+        ap = ActParams(int(bool(act.get("interleaved", False))), float(act.get("alpha", 0.0)),
+                       float(act.get("limit", 0.0)), float(act.get("up_shift", 0.0)),
+                       _ptr(gb, ctypes.c_float), _ptr(db, ctypes.c_float))
+        rc = lib().mxo_moe_mlp_act(*args, float(fragile_c or 0.0), _ptr(h_alt, ctypes.c_uint16),
+                                   _ptr(slack, ctypes.c_double), ctypes.byref(ap))
     if rc != 0:
         raise ValueError("expert index out of range")
     res = [out] + ([h] if want_h else [])

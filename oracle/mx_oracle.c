@@ -368,13 +368,29 @@ static int bf16_alternative(double v, uint16_t hb, double dv, uint16_t* alt) {
   return found;
 }
 
-int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
-                   const int32_t* topk_idx, const float* topk_w,
-                   const uint8_t* gu_packed, const uint8_t* gu_scales,
-                   const uint8_t* dn_packed, const uint8_t* dn_scales,
-                   const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out,
-                   double acc_c, uint16_t* h_alt_out, double* slack_out) {
+/* The expert MLP's activation, by the reading stated with mxo_act_params (mx_oracle.h): gate and
+ * up values of output column f are pre-activations gate_row(f) and up_row(f) of the gate_up
+ * product (bias included); h = g' * sigmoid(alpha g') * (u' + shift) with g' = min(g, limit) and
+ * u' = clamp(u, -limit, limit) when limit > 0. With NULL parameters: alpha 1, no clamp, shift 0,
+ * rows [0, F) gate and [F, 2F) up -- h = silu(g) * u. */
+static double act_alpha(const mxo_act_params* act) {
+  return (act && act->alpha != 0.0) ? act->alpha : 1.0;
+}
+
+int mxo_moe_mlp_act(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
+                    const int32_t* topk_idx, const float* topk_w,
+                    const uint8_t* gu_packed, const uint8_t* gu_scales,
+                    const uint8_t* dn_packed, const uint8_t* dn_scales,
+                    const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out,
+                    double acc_c, uint16_t* h_alt_out, double* slack_out,
+                    const mxo_act_params* act) {
   ensure_tables();
+  const double alpha = act_alpha(act);
+  const double limit = act ? act->limit : 0.0;
+  const double shift = act ? act->up_shift : 0.0;
+  const int interleaved = act ? act->interleaved : 0;
+  const float* gu_bias = act ? act->gu_bias : NULL;
+  const float* dn_bias = act ? act->dn_bias : NULL;
   if (!tokens) n_tokens = T;
   for (int i = 0; i < n_tokens; ++i) {
     int t = tokens ? tokens[i] : i;
@@ -414,13 +430,19 @@ int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t
           acc += term;
           if (fragility) sq += term * term;
         }
+        if (gu_bias) acc += (double)gu_bias[(int64_t)e * 2 * F + n];
         a[n] = acc;
         a2[n] = sq;
       }
-      /* SwiGLU, then bf16 rounding of h */
+      /* the activation (SwiGLU or its clamped, scaled form), then bf16 rounding of h */
       for (int f = 0; f < F; ++f) {
-        double g = a[f], u = a[F + f];
-        hv[f] = g / (1.0 + exp(-g)) * u;
+        const int gi = interleaved ? 2 * f : f, ui = interleaved ? 2 * f + 1 : F + f;
+        double g = a[gi], u = a[ui];
+        if (limit > 0.0) {
+          g = fmin(g, limit);
+          u = fmax(fmin(u, limit), -limit);
+        }
+        hv[f] = g / (1.0 + exp(-alpha * g)) * (u + shift);
         hb[f] = mxo_bf16_from_double(hv[f]);
       }
       if (h_out)
@@ -437,12 +459,19 @@ int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t
         if (halt) memcpy(halt, hb, sizeof(uint16_t) * (size_t)F);
         if (mx_act) {
           for (int f = 0; f < F; ++f) {
-            const double g = a[f], u = a[F + f];
-            const double sg = 1.0 / (1.0 + exp(-g));
-            const double dsilu = sg * (1.0 + g * (1.0 - sg));
-            const double dg = acc_c * u32 * sqrt((double)H * a2[f]);
-            const double du = acc_c * u32 * sqrt((double)H * a2[F + f]);
-            const double dv = fabs(dsilu * u) * dg + fabs(g * sg) * du + 16.0 * u32 * fabs(hv[f]);
+            const int gi = interleaved ? 2 * f : f, ui = interleaved ? 2 * f + 1 : F + f;
+            double g = a[gi], u = a[ui];
+            /* a clamped input does not move h: its derivative is 0 there */
+            const int g_clamped = limit > 0.0 && g > limit;
+            const int u_clamped = limit > 0.0 && fabs(u) > limit;
+            if (g_clamped) g = limit;
+            if (u_clamped) u = u > 0 ? limit : -limit;
+            const double sg = 1.0 / (1.0 + exp(-alpha * g));
+            const double dact = sg * (1.0 + alpha * g * (1.0 - sg));  /* d(g sigma(alpha g))/dg */
+            const double dg = g_clamped ? 0.0 : acc_c * u32 * sqrt((double)H * a2[gi]);
+            const double du = u_clamped ? 0.0 : acc_c * u32 * sqrt((double)H * a2[ui]);
+            const double dv = fabs(dact * (u + shift)) * dg + fabs(g * sg) * du +
+                              16.0 * u32 * fabs(hv[f]);
             uint16_t alt;
             if (!bf16_alternative(hv[f], hb[f], dv, &alt)) continue;
             const int b0 = f & ~31;
@@ -475,6 +504,7 @@ int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t
         const uint8_t* srow = dn_scales + ((int64_t)e * H + m) * dn_srow;
         double acc = 0.0;
         for (int f = 0; f < F; ++f) acc += h[f] * weight_elem(prow, srow, f, !mx_act);
+        if (dn_bias) acc += (double)dn_bias[(int64_t)e * H + m];
         o[m] += wt * acc;
       }
     }
@@ -486,6 +516,17 @@ int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t
     free(xr);
   }
   return 0;
+}
+
+int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
+                   const int32_t* topk_idx, const float* topk_w,
+                   const uint8_t* gu_packed, const uint8_t* gu_scales,
+                   const uint8_t* dn_packed, const uint8_t* dn_scales,
+                   const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out,
+                   double acc_c, uint16_t* h_alt_out, double* slack_out) {
+  return mxo_moe_mlp_act(T, H, F, E, k, mx_act, x, topk_idx, topk_w, gu_packed, gu_scales,
+                         dn_packed, dn_scales, tokens, n_tokens, out, h_out, acc_c, h_alt_out,
+                         slack_out, NULL);
 }
 
 int mxo_moe_mlp(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,

@@ -82,6 +82,28 @@ int mxo_moe_mlp_ex(int T, int H, int F, int E, int k, int mx_act, const uint16_t
                    const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out,
                    double acc_c, uint16_t* h_alt_out, double* slack_out);
 
+/* The expert activation of the released gpt-oss models, which the pages do not spell out (reading
+ * of an open point, parameterised so that the zero / NULL parameters give the SwiGLU above):
+ *   a = x W_gu^T + gu_bias[e]   (gu_bias [E][2F] in the weight rows' order, NULL = none)
+ *   g = a[gate_row(f)], u = a[up_row(f)]: rows f and F + f, or (interleaved) 2f and 2f + 1
+ *   limit > 0: g = min(g, limit), u = clamp(u, -limit, limit)   (the gate is clamped above only)
+ *   h = bf16( g * sigmoid(alpha * g) * (u + up_shift) )          (alpha 0 means 1)
+ *   y = h W_dn^T + dn_bias[e]   (dn_bias [E][H], NULL = none), then weighted and summed.
+ * The fragile-decision aid of the activation variant uses the same h. */
+typedef struct {
+  int interleaved;
+  double alpha, limit, up_shift;
+  const float* gu_bias;
+  const float* dn_bias;
+} mxo_act_params;
+int mxo_moe_mlp_act(int T, int H, int F, int E, int k, int mx_act, const uint16_t* x,
+                    const int32_t* topk_idx, const float* topk_w,
+                    const uint8_t* gu_packed, const uint8_t* gu_scales,
+                    const uint8_t* dn_packed, const uint8_t* dn_scales,
+                    const int32_t* tokens, int n_tokens, double* out, uint16_t* h_out,
+                    double acc_c, uint16_t* h_alt_out, double* slack_out,
+                    const mxo_act_params* act);
+
 /* Number of OpenMP threads the oracle uses. */
 int mxo_num_threads(void);
 

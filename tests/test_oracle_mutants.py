@@ -15,7 +15,8 @@ SRC = os.path.join(ROOT, "oracle", "mx_oracle.c")
 PIN_TESTS = [os.path.join(ROOT, "tests", "test_oracle_codec.py"),
              os.path.join(ROOT, "tests", "test_oracle_path.py"),
              os.path.join(ROOT, "tests", "test_oracle_fragile.py"),
-             os.path.join(ROOT, "tests", "test_oracle_operand.py")]
+             os.path.join(ROOT, "tests", "test_oracle_operand.py"),
+             os.path.join(ROOT, "tests", "test_oracle_act.py")]
 
 # (name, exact text in mx_oracle.c, replacement)
 MUTANTS = [
@@ -37,9 +38,10 @@ MUTANTS = [
     ("router-no-bias", "if (br) acc += (double)br[e];", ";"),
     ("permute-unstable", "int32_t row = offsets[e] + fill[e]++;",
      "int32_t row = offsets[e + 1] - 1 - fill[e]++;"),
-    ("swiglu-gate-up-swapped", "double g = a[f], u = a[F + f];\n        hv[f]",
-     "double g = a[F + f], u = a[f];\n        hv[f]"),
-    ("silu-sign", "hv[f] = g / (1.0 + exp(-g)) * u;", "hv[f] = g / (1.0 + exp(g)) * u;"),
+    ("swiglu-gate-up-swapped", "double g = a[gi], u = a[ui];\n        if (limit > 0.0) {",
+     "double g = a[ui], u = a[gi];\n        if (limit > 0.0) {"),
+    ("silu-sign", "hv[f] = g / (1.0 + exp(-alpha * g)) * (u + shift);",
+     "hv[f] = g / (1.0 + exp(alpha * g)) * (u + shift);"),
     ("routing-weight-dropped", "o[m] += wt * acc;", "o[m] += acc;"),
     ("down-expert-stride", "prow = dn_packed + ((int64_t)e * H + m) * dn_row",
      "prow = dn_packed + ((int64_t)e * F + m) * dn_row"),
@@ -56,6 +58,20 @@ MUTANTS = [
      "acc += h[f] * decode_elem(prow, srow, f);"),
     ("tables-subnormal-flush", "g_dq_bf16[b][c] = mxo_double_from_bf16(mxo_bf16_from_double(g_dq_exact[b][c]));",
      "g_dq_bf16[b][c] = fabs(g_dq_exact[b][c]) < 0x1p-126 ? 0.0 : mxo_double_from_bf16(mxo_bf16_from_double(g_dq_exact[b][c]));"),
+    # the parameterised expert activation
+    ("act-gate-clamped-below", "g = fmin(g, limit);", "g = fmax(fmin(g, limit), -limit);"),
+    ("act-up-not-clamped", "u = fmax(fmin(u, limit), -limit);", ";"),
+    ("act-alpha-ignored", "hv[f] = g / (1.0 + exp(-alpha * g)) * (u + shift);",
+     "hv[f] = g / (1.0 + exp(-g)) * (u + shift);"),
+    ("act-shift-dropped", "hv[f] = g / (1.0 + exp(-alpha * g)) * (u + shift);",
+     "hv[f] = g / (1.0 + exp(-alpha * g)) * u;"),
+    ("act-interleave-ignored",
+     "const int gi = interleaved ? 2 * f : f, ui = interleaved ? 2 * f + 1 : F + f;\n        double g",
+     "const int gi = f, ui = F + f;\n        double g"),
+    ("act-gate-up-bias-dropped", "if (gu_bias) acc += (double)gu_bias[(int64_t)e * 2 * F + n];", ";"),
+    ("act-down-bias-unweighted",
+     "if (dn_bias) acc += (double)dn_bias[(int64_t)e * H + m];\n        o[m] += wt * acc;",
+     "o[m] += wt * acc;\n        if (dn_bias) o[m] += (double)dn_bias[(int64_t)e * H + m];"),
     # the fragile-decision aid of the activation variant
     ("fragile-slack-unweighted", "sl[m] += wt * d;", "sl[m] += d;"),
     ("fragile-alt-two-steps", "if (up != neg) return (uint16_t)(b + 1);",
