@@ -109,6 +109,13 @@ mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t
  * ---------------------------------------------------------------------------------------------- */
 mx_status mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t G, int64_t R,
                              int64_t K, uint8_t* packed_t, uint8_t* scales_t, void* stream);
+/* mxfp4_tile_weights_ex -- the same with flags: MX_TILE_DEINTERLEAVE moves rows 2i to i and rows
+ * 2i + 1 to R/2 + i while tiling (interleaved gate/up rows -> gate rows, then up rows; R % 32 ==
+ * 0). Unknown flags: MX_ERR_UNSUPPORTED. */
+#define MX_TILE_DEINTERLEAVE 0x1u
+mx_status mxfp4_tile_weights_ex(const uint8_t* packed, const uint8_t* scales, int64_t G,
+                                int64_t R, int64_t K, uint32_t flags, uint8_t* packed_t,
+                                uint8_t* scales_t, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * moe_route_topk -- router logits, top-k expert selection and softmax over the k selected
@@ -156,7 +163,7 @@ mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, 
  * dedicated kernels instead of a bf16 fallback).
  * ---------------------------------------------------------------------------------------------- */
 typedef struct mx_moe_desc {
-  size_t struct_size;          /* sizeof(mx_moe_desc); other values -> MX_ERR_UNSUPPORTED */
+  size_t struct_size;          /* sizeof(mx_moe_desc) or MX_MOE_DESC_SIZE_V1; else MX_ERR_UNSUPPORTED */
   int32_t T, H, F, E, k;       /* tokens, hidden, expert FFN width, experts, experts per token */
   uint32_t flags;              /* MX_ACT_MXFP4 and/or MX_WEIGHTS_TILED, or 0 */
   mx_dtype out_dtype;          /* dtype of `out` */
@@ -173,7 +180,28 @@ typedef struct mx_moe_desc {
   int32_t* topk_idx_out;       /* [T][k], NULL = not stored (internal routing only) */
   float* topk_w_out;           /* [T][k], NULL = not stored */
   float* logits_out;           /* [T][E], NULL = not stored */
+  /* ---- expert activation (descriptors that end at logits_out -- struct_size ==
+   * MX_MOE_DESC_SIZE_V1 -- read all of these as zero): the released gpt-oss models' clamped,
+   * scaled SwiGLU with biases, which the pages leave open (the library's reading):
+   *   a = x W_gu^T + gu_bias[e]; g, u = gate and up pre-activations of output column f;
+   *   if swiglu_limit > 0: g = min(g, limit), u = clamp(u, -limit, limit) (gate clamped above);
+   *   h = bf16(g * sigmoid(alpha * g) * (u + swiglu_up_shift)), alpha = swiglu_alpha or 1 if 0;
+   *   expert output = h W_dn^T + dn_bias[e], then weighted by the routing weight and summed.
+   * All zero: h = silu(g) * u, no biases -- the SwiGLU above. */
+  uint32_t act_flags;          /* MX_GU_INTERLEAVED or 0 */
+  float swiglu_alpha;          /* sigmoid scale (0 = 1) */
+  float swiglu_limit;          /* clamp limit (<= 0: no clamp) */
+  float swiglu_up_shift;       /* added to the (clamped) up value */
+  const float* gu_bias;        /* [E][2F] fp32 in the caller's gate_up row order, NULL = none */
+  const float* dn_bias;        /* [E][H] fp32, NULL = none */
 } mx_moe_desc;
+/* The descriptor size before the expert activation fields (still accepted). */
+#define MX_MOE_DESC_SIZE_V1 (offsetof(mx_moe_desc, act_flags))
+/* act_flags: the caller's gate_up rows alternate gate and up (row 2i gate i, row 2i + 1 up i), as
+ * in the released checkpoints. The kernels take gate rows first: such weights must be tiled with
+ * mxfp4_tile_weights_ex(..., MX_TILE_DEINTERLEAVE, ...) and passed with MX_WEIGHTS_TILED
+ * (row-major interleaved weights are MX_ERR_UNSUPPORTED); gu_bias stays in the caller's order. */
+#define MX_GU_INTERLEAVED 0x1u
 
 /* Bytes of workspace mxfp4_moe_mlp needs for this descriptor (0 if the shapes are invalid). */
 size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc);

@@ -24,6 +24,8 @@ MX_ACT_MXFP4 = 0x1
 MX_WEIGHTS_TILED = 0x2
 MX_DEVERR_ROUTING = 0x1
 MX_NOALLOC_SCRATCH_BYTES = 32 << 20
+MX_GU_INTERLEAVED = 0x1
+MX_TILE_DEINTERLEAVE = 0x1
 STATUS_NAMES = {0: "MX_OK", 1: "MX_ERR_NULL", 2: "MX_ERR_SHAPE", 3: "MX_ERR_ALIGN",
                 4: "MX_ERR_DTYPE", 5: "MX_ERR_WORKSPACE", 6: "MX_ERR_UNSUPPORTED", 7: "MX_ERR_HIP"}
 
@@ -55,6 +57,9 @@ class MoeDesc(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("topk_idx_out", ctypes.c_void_p), ("topk_w_out", ctypes.c_void_p),
         ("logits_out", ctypes.c_void_p),
+        ("act_flags", ctypes.c_uint32), ("swiglu_alpha", ctypes.c_float),
+        ("swiglu_limit", ctypes.c_float), ("swiglu_up_shift", ctypes.c_float),
+        ("gu_bias", ctypes.c_void_p), ("dn_bias", ctypes.c_void_p),
     ]
 
 
@@ -67,6 +72,7 @@ SIGNATURES = {
     "mxfp4_quantize": (_INT, [_VP, _INT, _I64, _I64, _VP, _VP, _VP]),
     "mxfp4_dequantize": (_INT, [_VP, _VP, _I64, _I64, _VP, _INT, _VP]),
     "mxfp4_tile_weights": (_INT, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP]),
+    "mxfp4_tile_weights_ex": (_INT, [_VP, _VP, _I64, _I64, _I64, _U32, _VP, _VP, _VP]),
     "moe_route_topk": (_INT, [_VP, _VP, _VP, _I32, _I32, _I32, _I32, _VP, _VP, _VP, _VP]),
     "moe_permute_workspace": (_SZ, [_I32, _I32, _I32]),
     "moe_permute": (_INT, [_VP, _I32, _I32, _I32, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -158,15 +164,18 @@ def mxfp4_dequantize(packed: torch.Tensor, scales: torch.Tensor, dtype=torch.flo
     return out
 
 
-def mxfp4_tile_weights(packed: torch.Tensor, scales: torch.Tensor, stream=None):
+def mxfp4_tile_weights(packed: torch.Tensor, scales: torch.Tensor, stream=None,
+                       deinterleave: bool = False):
     """packed [G, R, K/2], scales [G, R, K/32] (or [R, K/2], [R, K/32]) -> (packed_t, scales_t)
     of the same shapes holding the bytes in the tiled layout of the grouped GEMMs (pass
-    MX_WEIGHTS_TILED in the MoE flags to use them)."""
+    MX_WEIGHTS_TILED in the MoE flags to use them). deinterleave: rows alternate gate and up
+    (mxfp4_tile_weights_ex with MX_TILE_DEINTERLEAVE)."""
     G = packed.shape[0] if packed.dim() == 3 else 1
     R, K = packed.shape[-2], packed.shape[-1] * 2
     packed_t, scales_t = torch.empty_like(packed), torch.empty_like(scales)
-    _check(lib().mxfp4_tile_weights(_ptr(packed), _ptr(scales), G, R, K, _ptr(packed_t),
-                                    _ptr(scales_t), _stream(stream)))
+    _check(lib().mxfp4_tile_weights_ex(_ptr(packed), _ptr(scales), G, R, K,
+                                       MX_TILE_DEINTERLEAVE if deinterleave else 0, _ptr(packed_t),
+                                       _ptr(scales_t), _stream(stream)))
     return packed_t, scales_t
 
 
@@ -211,7 +220,9 @@ def get_device_error(stream=None) -> int:
 
 def make_moe_desc(x, gu_packed, gu_scales, dn_packed, dn_scales, k, out, wr=None, br=None,
                   topk_idx=None, topk_w=None, flags=0, topk_idx_out=None, topk_w_out=None,
-                  logits_out=None) -> MoeDesc:
+                  logits_out=None, act=None) -> MoeDesc:
+    """act: the expert activation, a dict with any of interleaved (bool), alpha, limit, up_shift
+    (floats), gu_bias [E, 2F] and dn_bias [E, H] (fp32 device tensors); None = plain SwiGLU."""
     T, H = x.shape
     E, twoF = gu_packed.shape[0], gu_packed.shape[1]
     d = MoeDesc()
@@ -226,6 +237,12 @@ def make_moe_desc(x, gu_packed, gu_scales, dn_packed, dn_scales, k, out, wr=None
     d.out = _ptr(out)
     d.topk_idx_out, d.topk_w_out, d.logits_out = (_ptr(topk_idx_out), _ptr(topk_w_out),
                                                    _ptr(logits_out))
+    if act:
+        d.act_flags = MX_GU_INTERLEAVED if act.get("interleaved") else 0
+        d.swiglu_alpha = float(act.get("alpha", 0.0))
+        d.swiglu_limit = float(act.get("limit", 0.0))
+        d.swiglu_up_shift = float(act.get("up_shift", 0.0))
+        d.gu_bias, d.dn_bias = _ptr(act.get("gu_bias")), _ptr(act.get("dn_bias"))
     return d
 
 
@@ -235,7 +252,7 @@ def mxfp4_moe_mlp_workspace(desc: MoeDesc) -> int:
 
 def mxfp4_moe_mlp(x, gu_packed, gu_scales, dn_packed, dn_scales, k, wr=None, br=None,
                   topk_idx=None, topk_w=None, out_dtype=torch.bfloat16, flags=0, out=None,
-                  workspace=None, return_routing=False, stream=None):
+                  workspace=None, return_routing=False, stream=None, act=None):
     """The whole MoE MLP. Weights: gu_packed [E, 2F, H/2], gu_scales [E, 2F, H/32],
     dn_packed [E, H, F/2], dn_scales [E, H, F/32] (with MX_WEIGHTS_TILED in flags: the same
     shapes as written by mxfp4_tile_weights). Routing: internal from (wr, br) unless
@@ -254,7 +271,7 @@ def mxfp4_moe_mlp(x, gu_packed, gu_scales, dn_packed, dn_scales, k, wr=None, br=
                       topk_idx=topk_idx, topk_w=topk_w, flags=flags,
                       topk_idx_out=routing[1] if routing else None,
                       topk_w_out=routing[2] if routing else None,
-                      logits_out=routing[0] if routing else None)
+                      logits_out=routing[0] if routing else None, act=act)
     nbytes = mxfp4_moe_mlp_workspace(d)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
+#include <cstddef>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -157,9 +159,29 @@ mx_status check_routing_shape(int64_t T, int64_t H, int64_t E, int64_t k) {
   return MX_OK;
 }
 
+// The caller's descriptor as the current version: one that ends at logits_out (the size before
+// the expert activation fields) reads those fields as zero.
+mx_status read_desc(const mx_moe_desc* in, mx_moe_desc* out) {
+  if (in == nullptr) return fail(MX_ERR_NULL, "desc is NULL");
+  if (in->struct_size == sizeof(mx_moe_desc)) {
+    *out = *in;
+  } else if (in->struct_size == MX_MOE_DESC_SIZE_V1) {
+    std::memset(out, 0, sizeof(*out));
+    std::memcpy(out, in, MX_MOE_DESC_SIZE_V1);
+  } else {
+    return fail(MX_ERR_UNSUPPORTED, "desc.struct_size %zu (expected %zu or %zu)", in->struct_size,
+                sizeof(mx_moe_desc), (size_t)MX_MOE_DESC_SIZE_V1);
+  }
+  return MX_OK;
+}
+
+bool act_custom(const mx_moe_desc& d) {
+  return d.act_flags != 0 || d.swiglu_alpha != 0.f || d.swiglu_limit > 0.f ||
+         d.swiglu_up_shift != 0.f || d.gu_bias != nullptr || d.dn_bias != nullptr;
+}
+
 mx_status check_moe_desc(const mx_moe_desc* d) {
   if (d == nullptr) return fail(MX_ERR_NULL, "desc is NULL");
-  if (d->struct_size != sizeof(mx_moe_desc)) return fail(MX_ERR_UNSUPPORTED, "desc.struct_size %zu != %zu", d->struct_size, sizeof(mx_moe_desc));
   mx_status st = check_routing_shape(d->T, d->H, d->E, d->k);
   if (st != MX_OK) return st;
   if (d->F <= 0 || d->H % 32 || d->F % 32) return fail(MX_ERR_SHAPE, "H=%d and F=%d must be positive multiples of 32", d->H, d->F);
@@ -167,6 +189,12 @@ mx_status check_moe_desc(const mx_moe_desc* d) {
   if ((int64_t)d->T * d->H * 2 >= (1LL << 31) || (int64_t)d->T * d->k * d->F * 2 >= (1LL << 31))
     return fail(MX_ERR_SHAPE, "T*H and T*k*F bf16 activations must stay below 2 GiB");
   if (d->flags & ~(MX_ACT_MXFP4 | MX_WEIGHTS_TILED)) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->act_flags & ~MX_GU_INTERLEAVED) return fail(MX_ERR_UNSUPPORTED, "unknown act_flags 0x%x", d->act_flags);
+  if ((d->act_flags & MX_GU_INTERLEAVED) && !(d->flags & MX_WEIGHTS_TILED))
+    return fail(MX_ERR_UNSUPPORTED, "interleaved gate/up rows need the tiled layout "
+                "(mxfp4_tile_weights_ex with MX_TILE_DEINTERLEAVE, flag MX_WEIGHTS_TILED)");
+  if (!std::isfinite(d->swiglu_alpha) || !std::isfinite(d->swiglu_limit) || !std::isfinite(d->swiglu_up_shift))
+    return fail(MX_ERR_SHAPE, "swiglu_alpha, swiglu_limit and swiglu_up_shift must be finite");
   if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "out_dtype %d", (int)d->out_dtype);
   if (d->T == 0) return MX_OK;
   if (!d->x || !d->gu_packed || !d->gu_scales || !d->dn_packed || !d->dn_scales || !d->out)
@@ -213,6 +241,15 @@ MX_API mx_status mxfp4_dequantize(const uint8_t* packed, const uint8_t* scales, 
 MX_API mx_status mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t G,
                                     int64_t R, int64_t K, uint8_t* packed_t, uint8_t* scales_t,
                                     void* stream) {
+  return mxfp4_tile_weights_ex(packed, scales, G, R, K, 0u, packed_t, scales_t, stream);
+}
+
+MX_API mx_status mxfp4_tile_weights_ex(const uint8_t* packed, const uint8_t* scales, int64_t G,
+                                       int64_t R, int64_t K, uint32_t flags, uint8_t* packed_t,
+                                       uint8_t* scales_t, void* stream) {
+  if (flags & ~MX_TILE_DEINTERLEAVE) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", flags);
+  if ((flags & MX_TILE_DEINTERLEAVE) && R % 32)
+    return fail(MX_ERR_SHAPE, "R=%lld: de-interleaving needs R a multiple of 32", (long long)R);
   if (G < 0 || R < 0 || K < 0 || R % 16 || K % 32 || R > INT32_MAX || K > INT32_MAX)
     return fail(MX_ERR_SHAPE, "G=%lld R=%lld K=%lld (R a multiple of 16, K of 32)", (long long)G,
                 (long long)R, (long long)K);
@@ -222,7 +259,9 @@ MX_API mx_status mxfp4_tile_weights(const uint8_t* packed, const uint8_t* scales
   mx_status st = check_device();
   if (st != MX_OK) return st;
   ProfScope ps(PK_TILE, (hipStream_t)stream);
-  hipError_t e = mx::launch_tile_weights(packed, scales, G, (int)R, (int)K, packed_t, scales_t, (hipStream_t)stream);
+  hipError_t e = mx::launch_tile_weights(packed, scales, G, (int)R, (int)K,
+                                         (flags & MX_TILE_DEINTERLEAVE) != 0, packed_t, scales_t,
+                                         (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "tile_weights launch");
 }
 
@@ -271,9 +310,10 @@ MX_API mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int3
 }
 
 MX_API size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc) {
-  if (desc == nullptr || desc->struct_size != sizeof(mx_moe_desc)) return 0;
-  if (check_routing_shape(desc->T, desc->H, desc->E, desc->k) != MX_OK || desc->F <= 0) return 0;
-  return moe_layout(*desc).total;
+  mx_moe_desc d;
+  if (read_desc(desc, &d) != MX_OK) return 0;
+  if (check_routing_shape(d.T, d.H, d.E, d.k) != MX_OK || d.F <= 0) return 0;
+  return moe_layout(d).total;
 }
 
 namespace {
@@ -283,9 +323,11 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
 }  // namespace
 
 MX_API mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void* stream) {
-  mx_status st = check_moe_desc(desc);
+  mx_moe_desc d;
+  mx_status st = read_desc(desc, &d);
   if (st != MX_OK) return st;
-  const mx_moe_desc& d = *desc;
+  st = check_moe_desc(&d);
+  if (st != MX_OK) return st;
   if (d.T == 0) return ok();
   const MoeLayout L = moe_layout(d);
   if (ws == nullptr || ws_bytes < L.total) return fail(MX_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", L.total, ws_bytes);
@@ -324,9 +366,11 @@ char* scratch_on_device() {
 }  // namespace
 
 MX_API mx_status mxfp4_moe_mlp_noalloc(const mx_moe_desc* desc, void* stream) {
-  mx_status st = check_moe_desc(desc);
+  mx_moe_desc d;
+  mx_status st = read_desc(desc, &d);
   if (st != MX_OK) return st;
-  const mx_moe_desc& d = *desc;
+  st = check_moe_desc(&d);
+  if (st != MX_OK) return st;
   if (d.T == 0) return ok();
   const MoeLayout L = moe_layout(d);
   if (L.total > (size_t)MX_NOALLOC_SCRATCH_BYTES)
@@ -419,6 +463,15 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   g.y = reinterpret_cast<float*>(w + L.y);
   g.out = d.out;
   g.out_bf16 = d.out_dtype == MX_BF16;
+  if (act_custom(d)) {
+    g.act_custom = true;
+    g.gu_bias = d.gu_bias;
+    g.dn_bias = d.dn_bias;
+    g.gu_interleaved = (d.act_flags & MX_GU_INTERLEAVED) != 0;
+    g.act_alpha = d.swiglu_alpha != 0.f ? d.swiglu_alpha : 1.f;
+    g.act_limit = d.swiglu_limit;
+    g.act_shift = d.swiglu_up_shift;
+  }
   {
     ProfScope ps(PK_GATE_UP, s);
     e = mx::launch_moe_gate_up(g, s);

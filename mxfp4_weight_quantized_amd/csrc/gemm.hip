@@ -52,6 +52,12 @@ struct GemmKArgs {
   void* out;                  // gate_up with FP4 activations: packed codes of h [rows][F/2]
   uint8_t* out_scales;        //   and their scale bytes [rows][F/32]
   int out_bf16;
+  // expert activation of the gate_up epilogue (act_custom = 0: h = silu(g) * u) and the output
+  // bias of the MoE products (gate_up: [E][2F] in the caller's row order, interleaved or not;
+  // down: [E][N]; NULL = none)
+  const float* bias;
+  int act_custom, bias_interleaved;
+  float act_alpha, act_limit, act_shift;
   int gn;                     // column tiles per XCD super-tile (set by the launcher)
   int k_splits;               // linear only: K range split over blockIdx.z (<= 1: none); out
   int64_t part_stride;        //   then takes fp32 partial sums, split z at z * part_stride
@@ -223,10 +229,17 @@ using AccT = std::conditional_t<MF == 32, f32x16, f32x4>;
 // ln): down -> fp32 at the permuted row (the combine applies the routing weights: the epilogue
 // needs no index or weight loads); linear -> fp32 or bf16. (gate_up stores through LDS, below.)
 template <int MODE, int FM, int FN, int TM, int BN, int WN, int MF>
-__device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&acc)[FM][FN], int r0,
-                                           int row_end, int nt, int wm, int wn, int g, int ln) {
+__device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&acc)[FM][FN], int e,
+                                           int r0, int row_end, int nt, int wm, int wn, int g,
+                                           int ln) {
   constexpr int TN = BN / WN;
   constexpr int NV = MF == 32 ? 16 : 4;
+  float bd[FN];  // down: the expert's output bias of each fragment column
+  if constexpr (MODE == MODE_DOWN) {
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+      bd[f] = p.bias ? p.bias[(int64_t)e * p.N + min(nt * BN + wn * TN + f * MF + ln, p.N - 1)] : 0.f;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -238,7 +251,7 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           const int col = nt * BN + wn * TN + f * MF + ln;
-          if (col < p.N) y[(int64_t)r * p.N + col] = acc[i][f][q];
+          if (col < p.N) y[(int64_t)r * p.N + col] = p.bias ? acc[i][f][q] + bd[f] : acc[i][f][q];
         }
       } else {
         const int64_t zoff = p.k_splits > 1 ? (int64_t)blockIdx.z * p.part_stride : 0;
@@ -714,17 +727,47 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     static_assert(BM * LDH * 2 <= STAGES * (int)sizeof(Stage), "h tile fits the stage buffers");
     uint16_t* sh = reinterpret_cast<uint16_t*>(&stg[0]);
     barrier_lds();  // every wave is done reading the last stage (no loads are in flight)
+    if (p.act_custom) {
+      // the clamped, scaled form: biases (per output column: gate and up rows of the expert, in
+      // the caller's order), gate clamped above and up on both sides at the limit, sigmoid scale
+      // alpha, shift added to up
+      float bg[FN / 2], bu[FN / 2];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int f = 0; f < FN / 2; ++f) {
+        const int col = min(nt * BNH + wn * (BNH / WN) + f * MF + ln, p.F - 1);
+        const float* b = p.bias + (int64_t)e * 2 * p.F;
+        bg[f] = p.bias ? b[p.bias_interleaved ? 2 * col : col] : 0.f;
+        bu[f] = p.bias ? b[p.bias_interleaved ? 2 * col + 1 : p.F + col] : 0.f;
+      }
+      const float lim = p.act_limit, alpha = p.act_alpha, shift = p.act_shift;
 #pragma unroll
-      for (int q = 0; q < NV; ++q)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int f = 0; f < FN / 2; ++f) {
-          const float gt = acc[i][f][q], up = acc[i][FN / 2 + f][q];
-          const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
-          sh[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDH + wn * (BNH / WN) + f * MF + ln] =
-              (uint16_t)f32_to_bf16_bits(hv);
-        }
+        for (int q = 0; q < NV; ++q)
+#pragma unroll
+          for (int f = 0; f < FN / 2; ++f) {
+            float gt = acc[i][f][q] + bg[f], up = acc[i][FN / 2 + f][q] + bu[f];
+            if (lim > 0.f) {
+              gt = fminf(gt, lim);
+              up = fmaxf(fminf(up, lim), -lim);
+            }
+            const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-alpha * gt)) * (up + shift);
+            sh[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDH + wn * (BNH / WN) + f * MF + ln] =
+                (uint16_t)f32_to_bf16_bits(hv);
+          }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+#pragma unroll
+          for (int f = 0; f < FN / 2; ++f) {
+            const float gt = acc[i][f][q], up = acc[i][FN / 2 + f][q];
+            const float hv = gt * __builtin_amdgcn_rcpf(1.f + __expf(-gt)) * up;
+            sh[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDH + wn * (BNH / WN) + f * MF + ln] =
+                (uint16_t)f32_to_bf16_bits(hv);
+          }
+    }
     barrier_lds();
     if constexpr (AFP4) {
       // FP4 activations: the down product takes h as MXFP4, so each 32-column block of the bf16
@@ -764,6 +807,10 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     constexpr int LDY = BN + 4;
     constexpr int CPR = BN / 4;
     float* sy = reinterpret_cast<float*>(&stg[0]);
+    float bd[FN];  // the expert's output bias of each fragment column
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+      bd[f] = p.bias ? p.bias[(int64_t)e * p.N + min(nt * BN + wn * TN + f * MF + ln, p.N - 1)] : 0.f;
     barrier_lds();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -771,7 +818,8 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
       for (int q = 0; q < NV; ++q)
 #pragma unroll
         for (int f = 0; f < FN; ++f)
-          sy[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDY + wn * TN + f * MF + ln] = acc[i][f][q];
+          sy[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDY + wn * TN + f * MF + ln] =
+              p.bias ? acc[i][f][q] + bd[f] : acc[i][f][q];
     barrier_lds();
     float* y = reinterpret_cast<float*>(p.out);
     for (int c = tid; c < BM * CPR; c += NT) {
@@ -782,7 +830,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
             *reinterpret_cast<const float4*>(sy + lr * LDY + cc * 4);
     }
   } else {
-    store_tile<MODE, FM, FN, TM, BN, WN, MF>(p, acc, r0, row_end, nt, wm, wn, g, ln);
+    store_tile<MODE, FM, FN, TM, BN, WN, MF>(p, acc, e, r0, row_end, nt, wm, wn, g, ln);
   }
 }
 
@@ -995,6 +1043,14 @@ GemmKArgs gate_up_args(const MoeGemmArgs& m) {
   g.rows_total = m.T * m.k;
   g.F = m.F;
   g.out = m.h;
+  if (m.act_custom) {
+    g.act_custom = 1;
+    g.bias = m.gu_bias;
+    g.bias_interleaved = m.gu_interleaved ? 1 : 0;
+    g.act_alpha = m.act_alpha;
+    g.act_limit = m.act_limit;
+    g.act_shift = m.act_shift;
+  }
   return g;
 }
 
@@ -1016,6 +1072,7 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
   d.rows_total = m.T * m.k;
   d.F = m.F;
   d.out = m.y;
+  d.bias = m.dn_bias;
   return d;
 }
 

@@ -12,9 +12,11 @@ hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8
                            uint8_t* scales, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t nblocks,
                              void* dst, bool bf16_out, hipStream_t stream);
-// G matrices [R][K] (R % 16 == 0, K % 32 == 0) into the tiled layout of the grouped GEMMs.
+// G matrices [R][K] (R % 16 == 0, K % 32 == 0) into the tiled layout of the grouped GEMMs;
+// deinterleave: rows 2i -> i, 2i + 1 -> R/2 + i on the way (R % 32 == 0).
 hipError_t launch_tile_weights(const uint8_t* packed, const uint8_t* scales, int64_t G, int R,
-                               int K, uint8_t* packed_t, uint8_t* scales_t, hipStream_t stream);
+                               int K, bool deinterleave, uint8_t* packed_t, uint8_t* scales_t,
+                               hipStream_t stream);
 
 // route.hip
 // partials (may be null): fp32 scratch of route_partial_splits(T, H, E) * T * E floats; with it
@@ -78,6 +80,14 @@ struct MoeGemmArgs {
   uint8_t *xq, *xqs, *hq, *hqs;
   // expert weights in the tiled layout (codes [E][R/16][K/32][16][16], scales [E][K/32][R])
   bool tiled;
+  // expert activation: act_custom = 0 is the plain SwiGLU (the rest unused); else biases (NULL =
+  // none; gu_bias in the caller's row order, interleaved or not), clamp limit (<= 0: none),
+  // sigmoid scale and up shift
+  bool act_custom;
+  const float* gu_bias;      // [E][2F]
+  const float* dn_bias;      // [E][H]
+  bool gu_interleaved;
+  float act_alpha, act_limit, act_shift;
 };
 // Tile rows (BM) the grouped GEMMs use for this problem; the permutation's tile list must match.
 int moe_tile_rows(int T, int k, int E, bool mx_act);

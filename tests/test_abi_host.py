@@ -71,7 +71,7 @@ def test_header_declares_the_contract():
         assert name in protos, "header does not declare %s" % name
         assert protos[name] == types, (name, protos[name], types)
     fields = [f for f, _ in mx.MoeDesc._fields_]
-    assert fields == DESC_FIELDS
+    assert fields[:len(DESC_FIELDS)] == DESC_FIELDS  # the expert activation fields follow
 
 
 def test_exports_every_declared_entry_point(L):
@@ -117,6 +117,9 @@ def test_tile_weights_argument_errors(L):
     assert L.mxfp4_tile_weights(p, p, 2, 32, 64, p, None, None) == mx.MX_ERR_NULL
     assert L.mxfp4_tile_weights(ctypes.c_void_p(0x10000008), p, 2, 32, 64, p, p, None) == mx.MX_ERR_ALIGN
     assert L.mxfp4_tile_weights(p, p, 0, 32, 64, p, p, None) == mx.MX_OK  # empty: no-op
+    assert L.mxfp4_tile_weights_ex(p, p, 2, 48, 64, 1, p, p, None) == mx.MX_ERR_SHAPE  # R % 32
+    assert L.mxfp4_tile_weights_ex(p, p, 2, 64, 64, 2, p, p, None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mxfp4_tile_weights_ex(p, p, 0, 64, 64, 1, p, p, None) == mx.MX_OK
 
 
 def test_route_and_permute_argument_errors(L):
@@ -160,7 +163,10 @@ def test_moe_workspace_query_and_errors(L):
     # at least the bf16 SwiGLU output and the fp32 per-pair expert outputs
     assert n >= P * 2880 * 2 + P * 2880 * 4 and n % 256 == 0
     d_mx = _desc(T=64, H=2880, F=2880, E=32, k=4, flags=mx.MX_ACT_MXFP4)
-    assert mx.mxfp4_moe_mlp_workspace(d_mx) > n
+    # the activation variant keeps no bf16 h (gate_up writes it as MXFP4): smaller, still the
+    # fp32 per-pair rows and the packed h
+    n_mx = mx.mxfp4_moe_mlp_workspace(d_mx)
+    assert P * 2880 * 4 + P * 2880 * 17 // 32 <= n_mx < n
     bad = _desc()
     bad.struct_size = 8
     assert mx.mxfp4_moe_mlp_workspace(bad) == 0
@@ -183,6 +189,21 @@ def test_moe_workspace_query_and_errors(L):
     assert L.mxfp4_moe_mlp(ctypes.byref(small), _fake(), need - 1, None) == mx.MX_ERR_WORKSPACE
     assert L.mxfp4_moe_mlp(ctypes.byref(small), None, need, None) == mx.MX_ERR_WORKSPACE
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(T=0)), None, 0, None) == mx.MX_OK
+    # the descriptor without the expert activation fields is accepted (they read as zero)
+    v1 = mx.MoeDesc.act_flags.offset
+    old_desc = _desc(T=64, H=2880, F=2880, E=32, k=4, struct_size=v1)
+    assert mx.mxfp4_moe_mlp_workspace(old_desc) == n
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(struct_size=v1, x=0)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_NULL
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(struct_size=v1 + 4)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_UNSUPPORTED
+    # interleaved gate/up rows need the tiled layout; unknown activation flags; non-finite params
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(act_flags=mx.MX_GU_INTERLEAVED)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(act_flags=4)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(swiglu_limit=float("inf"))), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_SHAPE
     # the allocation-free entry point: same checks, and problems beyond its array are rejected
     # on the host before anything runs
     big = _desc(T=8192, H=2880, F=2880, E=32, k=4)
