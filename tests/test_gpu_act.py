@@ -98,8 +98,8 @@ def test_moe_act_small_pinned_routing(T, H, F, E, k, flags, interleaved):
     else:
         ref, slack = oracle.moe_mlp(x, idx, w, gp, gs, dp, ds, E=E, act=o_act), None
     check_tolerance(to_f64(out), ref, "moe act T=%d" % T, slack=slack)
-    # the clamp is reached in these cases
-    assert np.abs(gb).max() > 2 * RELEASED["limit"]
+    # the clamp is reached in these cases (biases alone put ~8 % of the values past the limit)
+    assert (np.abs(gb) > RELEASED["limit"]).mean() > 0.02
     if not interleaved and not flags:  # row-major weights: the same output as the tiled layout
         rm = mx.mxfp4_moe_mlp(to_dev(x), *moe_weights_dev(seed, E, H, F), k, topk_idx=to_dev(idx),
                               topk_w=to_dev(w), out_dtype=torch.float32, act=g_act)
