@@ -193,7 +193,7 @@ typedef struct mx_moe_desc {
   float swiglu_limit;          /* clamp limit (<= 0: no clamp) */
   float swiglu_up_shift;       /* added to the (clamped) up value */
   const float* gu_bias;        /* [E][2F] fp32 in the caller's gate_up row order, NULL = none */
-  const float* dn_bias;        /* [E][H] fp32, NULL = none */
+  const float* dn_bias;        /* [E][H] fp32, 16-byte aligned, NULL = none */
 } mx_moe_desc;
 /* The descriptor size before the expert activation fields (still accepted). */
 #define MX_MOE_DESC_SIZE_V1 (offsetof(mx_moe_desc, act_flags))

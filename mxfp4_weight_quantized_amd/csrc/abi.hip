@@ -193,6 +193,8 @@ mx_status check_moe_desc(const mx_moe_desc* d) {
   if ((d->act_flags & MX_GU_INTERLEAVED) && !(d->flags & MX_WEIGHTS_TILED))
     return fail(MX_ERR_UNSUPPORTED, "interleaved gate/up rows need the tiled layout "
                 "(mxfp4_tile_weights_ex with MX_TILE_DEINTERLEAVE, flag MX_WEIGHTS_TILED)");
+  if ((d->gu_bias && !aligned(d->gu_bias, 4)) || (d->dn_bias && !aligned(d->dn_bias, 16)))
+    return fail(MX_ERR_ALIGN, "gu_bias must be 4-byte and dn_bias 16-byte aligned");
   if (!std::isfinite(d->swiglu_alpha) || !std::isfinite(d->swiglu_limit) || !std::isfinite(d->swiglu_up_shift))
     return fail(MX_ERR_SHAPE, "swiglu_alpha, swiglu_limit and swiglu_up_shift must be finite");
   if (d->out_dtype != MX_F32 && d->out_dtype != MX_BF16) return fail(MX_ERR_DTYPE, "out_dtype %d", (int)d->out_dtype);
@@ -390,10 +392,12 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   int32_t* status = reinterpret_cast<int32_t*>(w + L.status);
   const int32_t* idx;
   const float* tw;
-  // small batches: the router launch computes the logits only and the permutation launch makes
-  // the top-k selection first (one launch fewer)
+  // small batches: the router launch computes the logits (or their partial sums over H) only and
+  // the permutation launch makes the top-k selection first (one launch fewer)
   bool select_in_permute = false;
-  const float* sel_logits = nullptr;
+  float* sel_logits = nullptr;
+  float* rpart = nullptr;
+  int n_part = 0;
   if (d.topk_idx_in == nullptr) {
     float* logits = d.logits_out ? d.logits_out : reinterpret_cast<float*>(w + L.logits);
     int32_t* oi = d.topk_idx_out ? d.topk_idx_out : reinterpret_cast<int32_t*>(w + L.idx);
@@ -401,11 +405,11 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
     select_in_permute = mx::route_logits_defers_select(d.T, d.E, d.k);
     // the router's partial sums borrow the down projection's output rows (written later)
     const size_t part_bytes = (size_t)mx::route_partial_splits(d.T, d.H, d.E) * d.T * d.E * 4;
-    float* rpart = part_bytes <= (size_t)d.T * d.k * d.H * 4 ? reinterpret_cast<float*>(w + L.y) : nullptr;
+    rpart = part_bytes <= (size_t)d.T * d.k * d.H * 4 ? reinterpret_cast<float*>(w + L.y) : nullptr;
     {
       ProfScope ps(PK_ROUTE, s);
       e = select_in_permute
-              ? mx::launch_route_logits(d.x, d.wr, d.br, d.T, d.H, d.E, logits, s)
+              ? mx::launch_route_logits(d.x, d.wr, d.br, d.T, d.H, d.E, logits, rpart, &n_part, s)
               : mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, rpart, s);
     }
     if (e != hipSuccess) return hip_fail(e, "route launch");
@@ -423,9 +427,9 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   {
     ProfScope ps(PK_PERMUTE, s);
     e = select_in_permute
-            ? mx::launch_select_permute(sel_logits, d.T, d.k, d.E, const_cast<int32_t*>(idx),
-                                        const_cast<float*>(tw), offsets, perm, inv, status,
-                                        L.tile_rows, tiles, status + 1, s)
+            ? mx::launch_select_permute(sel_logits, rpart, n_part, d.br, d.T, d.k, d.E,
+                                        const_cast<int32_t*>(idx), const_cast<float*>(tw), offsets,
+                                        perm, inv, status, L.tile_rows, tiles, status + 1, s)
         : L.pcounts_bytes > 0
             ? mx::launch_permute_sliced(idx, d.T, d.k, d.E, offsets, perm, inv, status, L.tile_rows,
                                         tiles, status + 1, reinterpret_cast<int32_t*>(w + L.pcounts), s)
@@ -457,6 +461,7 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   g.num_tiles = status + 1;
   g.max_tiles = L.max_tiles;
   g.topk_w = tw;
+  g.topk_idx = idx;
   g.gu_packed = d.gu_packed; g.gu_scales = d.gu_scales;
   g.dn_packed = d.dn_packed; g.dn_scales = d.dn_scales;
   g.h = mx_act ? nullptr : reinterpret_cast<uint16_t*>(w + L.h);

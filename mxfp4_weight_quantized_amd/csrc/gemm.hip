@@ -52,9 +52,9 @@ struct GemmKArgs {
   void* out;                  // gate_up with FP4 activations: packed codes of h [rows][F/2]
   uint8_t* out_scales;        //   and their scale bytes [rows][F/32]
   int out_bf16;
-  // expert activation of the gate_up epilogue (act_custom = 0: h = silu(g) * u) and the output
-  // bias of the MoE products (gate_up: [E][2F] in the caller's row order, interleaved or not;
-  // down: [E][N]; NULL = none)
+  // expert activation of the gate_up epilogue (act_custom = 0: h = silu(g) * u) with its bias
+  // [E][2F] in the caller's row order, interleaved or not (NULL = none). (The down bias is added
+  // by the combine.)
   const float* bias;
   int act_custom, bias_interleaved;
   float act_alpha, act_limit, act_shift;
@@ -229,17 +229,10 @@ using AccT = std::conditional_t<MF == 32, f32x16, f32x4>;
 // ln): down -> fp32 at the permuted row (the combine applies the routing weights: the epilogue
 // needs no index or weight loads); linear -> fp32 or bf16. (gate_up stores through LDS, below.)
 template <int MODE, int FM, int FN, int TM, int BN, int WN, int MF>
-__device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&acc)[FM][FN], int e,
-                                           int r0, int row_end, int nt, int wm, int wn, int g,
-                                           int ln) {
+__device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&acc)[FM][FN], int r0,
+                                           int row_end, int nt, int wm, int wn, int g, int ln) {
   constexpr int TN = BN / WN;
   constexpr int NV = MF == 32 ? 16 : 4;
-  float bd[FN];  // down: the expert's output bias of each fragment column
-  if constexpr (MODE == MODE_DOWN) {
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-      bd[f] = p.bias ? p.bias[(int64_t)e * p.N + min(nt * BN + wn * TN + f * MF + ln, p.N - 1)] : 0.f;
-  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -251,7 +244,7 @@ __device__ __forceinline__ void store_tile(const GemmKArgs& p, const AccT<MF> (&
 #pragma unroll
         for (int f = 0; f < FN; ++f) {
           const int col = nt * BN + wn * TN + f * MF + ln;
-          if (col < p.N) y[(int64_t)r * p.N + col] = p.bias ? acc[i][f][q] + bd[f] : acc[i][f][q];
+          if (col < p.N) y[(int64_t)r * p.N + col] = acc[i][f][q];
         }
       } else {
         const int64_t zoff = p.k_splits > 1 ? (int64_t)blockIdx.z * p.part_stride : 0;
@@ -807,10 +800,6 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
     constexpr int LDY = BN + 4;
     constexpr int CPR = BN / 4;
     float* sy = reinterpret_cast<float*>(&stg[0]);
-    float bd[FN];  // the expert's output bias of each fragment column
-#pragma unroll
-    for (int f = 0; f < FN; ++f)
-      bd[f] = p.bias ? p.bias[(int64_t)e * p.N + min(nt * BN + wn * TN + f * MF + ln, p.N - 1)] : 0.f;
     barrier_lds();
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -818,8 +807,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
       for (int q = 0; q < NV; ++q)
 #pragma unroll
         for (int f = 0; f < FN; ++f)
-          sy[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDY + wn * TN + f * MF + ln] =
-              p.bias ? acc[i][f][q] + bd[f] : acc[i][f][q];
+          sy[(wm * TM + i * MF + acc_row<MF>(g, q)) * LDY + wn * TN + f * MF + ln] = acc[i][f][q];
     barrier_lds();
     float* y = reinterpret_cast<float*>(p.out);
     for (int c = tid; c < BM * CPR; c += NT) {
@@ -830,7 +818,7 @@ __device__ __forceinline__ void gemm_body(const GemmKArgs& p) {
             *reinterpret_cast<const float4*>(sy + lr * LDY + cc * 4);
     }
   } else {
-    store_tile<MODE, FM, FN, TM, BN, WN, MF>(p, acc, e, r0, row_end, nt, wm, wn, g, ln);
+    store_tile<MODE, FM, FN, TM, BN, WN, MF>(p, acc, r0, row_end, nt, wm, wn, g, ln);
   }
 }
 
@@ -851,11 +839,15 @@ __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_
 // fp32, then summed); pairs with inv < 0 (skipped routing indices) contribute nothing. Eight
 // columns per thread (two 16-byte loads per row in flight). Each Y element is read once: the
 // loads carry the non-temporal hint (20B-shaped prefill, T = 8192: 82 -> 79 us).
+// With a down bias (bias [E][H], idx the pairs' experts) each row is w * (Y + bias of its expert),
+// the bias added in fp32 before the weight.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int T, int H,
-                                                      int k, void* __restrict__ out) {
+                                                      int k, void* __restrict__ out,
+                                                      const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ bias) {
   const int64_t i8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int h8 = H >> 3;
   if (i8 >= (int64_t)T * h8) return;
@@ -866,8 +858,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int r = inv[(int64_t)t * k + j];
     if (r < 0) continue;
     const float wj = w[(int64_t)t * k + j];
-    const f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r * H + c));
-    const f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r * H + c + 4));
+    f32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r * H + c));
+    f32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r * H + c + 4));
+    if (bias != nullptr) {
+      const float* b = bias + (int64_t)idx[(int64_t)t * k + j] * H + c;
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(b), b1 = *reinterpret_cast<const f32x4*>(b + 4);
+      v0 += b0;
+      v1 += b1;
+    }
     s[0] += __fmul_rn(v0[0], wj); s[1] += __fmul_rn(v0[1], wj);
     s[2] += __fmul_rn(v0[2], wj); s[3] += __fmul_rn(v0[3], wj);
     s[4] += __fmul_rn(v1[0], wj); s[5] += __fmul_rn(v1[1], wj);
@@ -1072,7 +1070,6 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
   d.rows_total = m.T * m.k;
   d.F = m.F;
   d.out = m.y;
-  d.bias = m.dn_bias;
   return d;
 }
 
@@ -1144,12 +1141,13 @@ hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
 hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {
   const int64_t n8 = (int64_t)m.T * (m.H / 8);
   const unsigned grid = (unsigned)((n8 + 255) / 256);
+  const float* bias = m.act_custom ? m.dn_bias : nullptr;
   if (m.out_bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, stream, m.y, m.inv,
-                       m.topk_w, m.T, m.H, m.k, m.out);
+                       m.topk_w, m.T, m.H, m.k, m.out, m.topk_idx, bias);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, stream, m.y, m.inv,
-                       m.topk_w, m.T, m.H, m.k, m.out);
+                       m.topk_w, m.T, m.H, m.k, m.out, m.topk_idx, bias);
   return hipGetLastError();
 }
 

@@ -26,11 +26,15 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
                              int E, int k, float* logits, int32_t* idx, float* w, float* partials,
                              hipStream_t stream);
 int route_partial_splits(int T, int H, int E);
-// Router logits only, when the selection can be left to launch_select_permute (small batches
-// whose logits kernel does not select itself); returns false (nothing launched) otherwise.
+// Router logits only, where the selection is left to launch_select_permute (batches of up to 16
+// tokens whose logits kernel does not select itself, T * E <= kSelectMaxLogits).
+// With partials (route_partial_splits(T, H, E) * T * E floats) the partial tiles of H split over
+// *n_part workgroups are stored there without the bias (else *n_part = 0 and the logits with the
+// bias go to logits).
 bool route_logits_defers_select(int T, int E, int k);
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
-                               int H, int E, float* logits, hipStream_t stream);
+                               int H, int E, float* logits, float* partials, int* n_part,
+                               hipStream_t stream);
 
 // Device error word, one per device, owned by the library: kernels OR error codes into it, and
 // mx_get_device_error reads and clears it. device_error_word() is its device address on the
@@ -41,7 +45,8 @@ int32_t* device_error_word();
 // permute.hip: tiles/num_tiles may be NULL (tile_rows ignored then). With a tile list, perm must
 // hold P + tile_rows entries: the padding (and rows past the last valid pair) are set to pair 0.
 constexpr int kMaxTileRows = 128;
-constexpr int kSelectMaxPairs = 2048;  // launch_select_permute: T * k at most this
+constexpr int kSelectMaxPairs = 2048;   // launch_select_permute: T * k at most this
+constexpr int kSelectMaxLogits = 16384; //   and T * E at most this (its logits stay in LDS)
 constexpr int kSlicePairs = 4096;      // launch_permute_sliced: pairs per workgroup
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm,
                           int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
@@ -53,11 +58,13 @@ hipError_t launch_permute_sliced(const int32_t* idx, int T, int k, int E, int32_
                                  int32_t* perm, int32_t* inv, int32_t* status, int tile_rows,
                                  int2* tiles, int32_t* num_tiles, int32_t* counts,
                                  hipStream_t stream);
-// The same after the top-k selection from the router logits (writes idx and w [T][k]).
-hipError_t launch_select_permute(const float* logits, int T, int k, int E, int32_t* idx, float* w,
-                                 int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
-                                 int tile_rows, int2* tiles, int32_t* num_tiles,
-                                 hipStream_t stream);
+// The same after the top-k selection (writes idx and w [T][k]) from the router's logits, or from
+// its n_part > 0 partial tiles (summed in split order, plus the bias br; the sums are written to
+// logits).
+hipError_t launch_select_permute(float* logits, const float* partials, int n_part, const float* br,
+                                 int T, int k, int E, int32_t* idx, float* w, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv, int32_t* status, int tile_rows,
+                                 int2* tiles, int32_t* num_tiles, hipStream_t stream);
 
 // gemm.hip
 struct MoeGemmArgs {
@@ -70,6 +77,7 @@ struct MoeGemmArgs {
   const int32_t* num_tiles;  // device
   int max_tiles;
   const float* topk_w;       // [P]
+  const int32_t* topk_idx;   // [P] experts of the pairs (read by the combine for the down bias)
   const uint8_t *gu_packed, *gu_scales, *dn_packed, *dn_scales;
   uint16_t* h;               // [P][F] bf16 workspace
   float* y;                  // [P][H] fp32 workspace

@@ -15,8 +15,9 @@
 // stable counting sort, element for element.
 //
 // For small batches the same launch can first make the top-k selection from the router logits
-// (SELECT: one wave per token, the router's selection function), keeping the indices in LDS;
-// this saves the separate selection launch of the router in the MoE MLP.
+// (SELECT: all logits staged in LDS -- summed from the router's partial tiles where H was split
+// over workgroups -- then one wave per token, the router's selection function), keeping the
+// indices in LDS; this saves the separate selection launch of the router in the MoE MLP.
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -74,13 +75,16 @@ __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx
                                                        int32_t* __restrict__ dev_err, int tile_rows,
                                                        int2* __restrict__ tiles,
                                                        int32_t* __restrict__ num_tiles,
-                                                       const float* __restrict__ logits, int k,
-                                                       float* __restrict__ w_out) {
+                                                       float* __restrict__ logits, int k,
+                                                       float* __restrict__ w_out,
+                                                       const float* __restrict__ partials,
+                                                       int n_part, const float* __restrict__ br) {
   __shared__ int cnt[kWaves][kMaxE];
   __shared__ int tot[kMaxE + 1];
   __shared__ int tbase[kMaxE + 1];
   __shared__ int bad;
   __shared__ int sidx[SELECT ? kSelectMaxPairs : 1];
+  __shared__ float slog[SELECT ? kSelectMaxLogits : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int chunk = (P + kWaves - 1) / kWaves;
@@ -90,10 +94,26 @@ __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx
   for (int i = threadIdx.x; i < kWaves * kMaxE; i += blockDim.x) (&cnt[0][0])[i] = 0;
   if (threadIdx.x == 0) bad = 0;
   if constexpr (SELECT) {  // 0. top-k of every token (P = T * k <= kSelectMaxPairs)
+    // all T x E logits into LDS with coalesced loads (from the partial tiles: summed in split
+    // order, plus the bias, and stored as the logits), then one wave per token ranks them there
     const int T = P / k;
+    const int TE = T * E;
+    for (int i = threadIdx.x; i < TE; i += blockDim.x) {
+      float v;
+      if (n_part > 0) {
+        v = partials[i];
+        for (int q = 1; q < n_part; ++q) v += partials[(int64_t)q * TE + i];
+        v += (br != nullptr) ? br[i % E] : 0.f;
+        logits[i] = v;
+      } else {
+        v = logits[i];
+      }
+      slog[i] = v;
+    }
+    __syncthreads();
     for (int t = wave; t < T; t += kWaves) {
-      const int e = select_topk_wave([&](int x) { return logits[(int64_t)t * E + x]; }, lane, t,
-                                     E, k, idx, w_out);
+      const int e = select_topk_wave([&](int x) { return slog[t * E + x]; }, lane, t, E, k, idx,
+                                     w_out);
       if (lane < k) sidx[t * k + lane] = e;
     }
   }
@@ -330,19 +350,20 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offs
   if (tiles == nullptr || num_tiles == nullptr) tile_rows = 0;
   hipLaunchKernelGGL(permute_kernel<false>, dim3(1), dim3(64 * kWaves), 0, stream,
                      const_cast<int32_t*>(idx), P, E, offsets, perm, inv, status,
-                     device_error_word(), tile_rows, tiles, num_tiles, nullptr, k, nullptr);
+                     device_error_word(), tile_rows, tiles, num_tiles, nullptr, k, nullptr, nullptr,
+                     0, nullptr);
   return hipGetLastError();
 }
 
-hipError_t launch_select_permute(const float* logits, int T, int k, int E, int32_t* idx, float* w,
-                                 int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
-                                 int tile_rows, int2* tiles, int32_t* num_tiles,
-                                 hipStream_t stream) {
+hipError_t launch_select_permute(float* logits, const float* partials, int n_part, const float* br,
+                                 int T, int k, int E, int32_t* idx, float* w, int32_t* offsets,
+                                 int32_t* perm, int32_t* inv, int32_t* status, int tile_rows,
+                                 int2* tiles, int32_t* num_tiles, hipStream_t stream) {
   const int P = T * k;
   if (tiles == nullptr || num_tiles == nullptr) tile_rows = 0;
   hipLaunchKernelGGL(permute_kernel<true>, dim3(1), dim3(64 * kWaves), 0, stream, idx, P, E,
                      offsets, perm, inv, status, device_error_word(), tile_rows, tiles, num_tiles,
-                     logits, k, w);
+                     logits, k, w, partials, n_part, br);
   return hipGetLastError();
 }
 

@@ -142,12 +142,14 @@ __global__ __launch_bounds__(256) void route_select_kernel(float* __restrict__ l
 
 }  // namespace
 
-// At most one token per wave of the permutation workgroup: each wave's selection then waits for
-// one round of logit loads (with more tokens per wave the rounds queue up and cost more than the
-// launch saved: 20B-shaped decode, T = 64, measured 10 us slower).
+// At most one token per wave of the permutation workgroup: with more, the selections queue up on
+// its four SIMDs and cost more than the launch saved (20B-shaped decode, T = 64: the permutation
+// launch grew from 7 to 27 us with the logits staged in LDS, against 5.5 us for the selection
+// launch it replaced).
 bool route_logits_defers_select(int T, int E, int k) {
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
-  return groups > 1 && tiles * groups <= kSpreadBelow && T <= 16 && (int64_t)T * k <= kSelectMaxPairs;
+  return groups > 1 && tiles * groups <= kSpreadBelow && T <= 16 && (int64_t)T * k <= kSelectMaxPairs &&
+         (int64_t)T * E <= kSelectMaxLogits;
 }
 
 // Workgroups per token tile and expert group in the spread launch, when partial sums have a
@@ -163,12 +165,18 @@ int route_partial_splits(int T, int H, int E) {
 }
 
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
-                               int H, int E, float* logits, hipStream_t stream) {
+                               int H, int E, float* logits, float* partials, int* n_part,
+                               hipStream_t stream) {
+  *n_part = 0;
   if (T == 0) return hipSuccess;
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
   const int splits = min(16, H / 32);
-  hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups), dim3(64 * splits), 0, stream,
-                     x, wr, br, T, H, E, 1, splits, logits, 0, nullptr, nullptr, nullptr);
+  // with a partials buffer H is also split over so workgroups per tile (splits is 16 then)
+  const int so = partials != nullptr ? route_partial_splits(T, H, E) : 1;
+  if (so > 1) *n_part = so;
+  hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups, so), dim3(64 * (splits / so)), 0,
+                     stream, x, wr, br, T, H, E, 1, splits / so, logits, 0, nullptr, nullptr,
+                     so > 1 ? partials : nullptr);
   return hipGetLastError();
 }
 
