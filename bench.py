@@ -204,6 +204,7 @@ def bench_moe(args, name, shape, flags):
         if st != 0:
             raise mx.MXError(st, mx.last_error())
 
+    settle = settle_clocks(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -275,6 +276,7 @@ def bench_moe(args, name, shape, flags):
                    "out_dtype": "bf16", "router_bias_std": s.bias_std, "seed": s.seed,
                    "parallelism": "single-gpu", "weight_copies": n_w, "token_batches": n_x,
                    "launch": "hip graph per rotation" if args.graph else "eager"},
+        "settle": settle,
         "step": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
                  "hbm_gbs_algorithmic": round(layer_traffic / (ms * 1e-3) / 1e9, 1),
                  "touched_experts": touched},
@@ -285,6 +287,31 @@ def bench_moe(args, name, shape, flags):
         result["cpu_baseline"] = cpu_baseline_moe(args, s, x_all[:s.T], wr_np, br_np, host_w,
                                                   bool(flags))
     return result
+
+
+def settle_clocks(step, settle_ms):
+    """Untimed steps until the GPU has run them for settle_ms milliseconds (by events), before the
+    warm-up steps: after the setup's pauses the chip takes some milliseconds of sustained work to
+    reach the clocks it then holds, and a short warm-up alone leaves the first timed steps slow
+    (20B prefill: 1.640 ms per step after 5 warm-up steps, 1.578 after 20, same box).
+    Returns what it did, for the output line."""
+    import torch
+    if settle_ms <= 0:
+        return {"ms": 0.0, "steps": 0}
+    stream = torch.cuda.current_stream()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    n, el, batch = 0, 0.0, 1
+    a.record(stream)
+    while el < settle_ms:
+        for _ in range(batch):
+            step(n)
+            n += 1
+        b.record(stream)
+        b.synchronize()
+        el = a.elapsed_time(b)
+        batch = min(64, batch * 2)
+    return {"ms": round(el, 1), "steps": n}
 
 
 def host_cpu() -> str:
@@ -349,6 +376,7 @@ def bench_linear(args, name, cfg):
         if st != 0:
             raise mx.MXError(st, mx.last_error())
 
+    settle = settle_clocks(step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -380,6 +408,7 @@ def bench_linear(args, name, cfg):
         "data": "synthetic",
         "config": {"workload": name, "M": M, "K": K, "N": N, "seed": seed, "weight_copies": n_w,
                    "parallelism": "single-gpu"},
+        "settle": settle,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -435,7 +464,8 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
     kinds = {"moe_gate_up_swiglu": ["moe_gate_up_swiglu_kernel"],
              "moe_down_weighted": ["moe_down_weighted_kernel"], "moe_combine": ["combine_kernel"],
              "route_topk": ["route_logits_kernel", "route_select_kernel"],
-             "permute": ["permute_kernel"], "linear": ["linear_kernel"]}
+             "permute": ["permute_kernel"], "linear": ["linear_kernel"],
+             "quantize": ["quantize_kernel"]}
     out = {}
     for kind, syms in kinds.items():
         fk = wk = 0.0
@@ -456,9 +486,79 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
     return out
 
 
-def summarize_trace(trace_dir, command, title):
+def summarize_traffic(workload, bench_json, commands):
+    """Markdown table of the counted HBM bytes per launch of one workload (from traffic.json)
+    beside the algorithmic bytes the bench line of the same workload reports per kernel."""
+    ent = json.load(open(TRAFFIC_FILE))[workload]
+    kern = json.load(open(bench_json)).get("kernels", {})
+    any_k = next(iter(ent.values()))
+    out = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE): %s" % workload, "",
+           "Commands (rocprofv3 output under gpurun_out/; the profiler runs from /tmp with "
+           "TMPDIR=/tmp, REPO is the repository root):", "", "```"] + list(commands) + [
+           "```", "",
+           "`--calibrate-copy` appends a 1 GiB elementwise copy (reads 1 GiB, writes 1 GiB); its "
+           "counters give the scale factors: fetch KiB x %.4f, write KiB x %.4f. Averages over "
+           "every launch of the kernel in the run. Algorithmic bytes: what the kernel must read "
+           "and write once (the bench line's per-kernel `bytes`)."
+           % (any_k["copy_scale_fetch"], any_k["copy_scale_write"]), "",
+           "| kernel | fetch KiB | write KiB | HBM MB / launch | algorithmic MB | ratio |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for k, v in sorted(ent.items(), key=lambda kv: -kv[1]["hbm_bytes_per_launch"]):
+        alg = kern.get(k, {}).get("bytes")
+        out.append("| %s | %s | %s | %.1f | %s | %s |" % (
+            k, format(v["fetch_kib"], ",.0f"), format(v["write_kib"], ",.0f"),
+            v["hbm_bytes_per_launch"] / 1e6, "%.1f" % (alg / 1e6) if alg else "-",
+            "%.2f" % (v["hbm_bytes_per_launch"] / alg) if alg else "-"))
+    out += ["", "Library sources: `%s` (hash of csrc/; the bench reports `traffic` only while "
+            "it matches)." % any_k["source_sha"]]
+    return "\n".join(out) + "\n"
+
+
+def summarize_mfma(pmc_dir, command, title):
+    """Markdown table of MFMA activity per dispatch of the grouped GEMMs from a rocprofv3 --pmc run
+    of GRBM_GUI_ACTIVE, SQ_VALU_MFMA_BUSY_CYCLES and SQ_INSTS_MFMA (with dispatch timestamps).
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs and SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs:
+    cycles per XCD over the dispatch time is the clock the chip held, and busy cycles per SIMD
+    over that the share of cycles the matrix pipes were busy."""
+    files = glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % pmc_dir)
+    disp = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            d = disp.setdefault((f, r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                        "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    out = ["# %s" % title, "", "Command (from the repository root, rocprofv3 output under "
+           "gpurun_out/):", "", "```", command, "```", "",
+           "Per-dispatch averages. GRBM_GUI_ACTIVE is summed over the 8 XCDs (cycles per XCD over "
+           "the dispatch time = the clock the chip held); SQ_VALU_MFMA_BUSY_CYCLES over the 1 024 "
+           "SIMDs (busy cycles per SIMD over the cycles = the share of cycles the matrix pipes were "
+           "busy).", "",
+           "| kernel | dispatches | avg us | clock MHz | MFMA instructions | MFMA busy | busy x clock / 2.4 GHz |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for sym in ("moe_gate_up_swiglu_kernel", "moe_down_weighted_kernel"):
+        ds = [d for d in disp.values() if sym in d["name"] and "GRBM_GUI_ACTIVE" in d]
+        if not ds:
+            continue
+        ns = sum(d["ns"] for d in ds) / len(ds)
+        cyc = sum(d["GRBM_GUI_ACTIVE"] for d in ds) / len(ds) / 8.0
+        busy = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds) / len(ds) / 1024.0
+        ins = sum(d.get("SQ_INSTS_MFMA", 0.0) for d in ds) / len(ds)
+        mhz = cyc / ns * 1e3
+        frac = busy / cyc if cyc else 0.0
+        out.append("| `%s` | %d | %.1f | %.0f | %.2fM | %.1f %% | %.1f %% |" % (
+            sym, len(ds), ns / 1e3, mhz, ins / 1e6, 100 * frac, 100 * frac * mhz / 2400.0))
+    out.append("")
+    out.append("Library sources: `%s` (hash of csrc/)." % source_sha())
+    return "\n".join(out) + "\n"
+
+
+def summarize_trace(trace_dir, command, title, bench_json=None):
     """Markdown table of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv): calls,
-    average / min / max duration and share of GPU time per kernel."""
+    average / min / max duration and share of GPU time per kernel; with bench_json (the traced
+    bench.py run's own output line), the step time and the dominant kernel by HIP events next
+    to the trace's figure for it."""
     files = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
         raise SystemExit("no kernel_stats.csv under %s" % trace_dir)
@@ -473,6 +573,21 @@ def summarize_trace(trace_dir, command, title):
         out.append("| `%s` | %s | %.2f | %.2f | %.2f | %.1f |" % (
             name[:110], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    if bench_json:
+        b = json.loads(open(bench_json).read().strip().splitlines()[-1])
+        roof = b.get("roofline", {})
+        dom = roof.get("kernel")
+        sym = {"moe_gate_up_swiglu": "moe_gate_up_swiglu_kernel", "moe_down_weighted":
+               "moe_down_weighted_kernel", "moe_combine": "combine_kernel", "linear": "linear_kernel"}
+        tr = [r for r in rows if sym.get(dom, "?") in r["Name"]]
+        out += ["", "The traced bench.py run's own line: %.4f ms per step; dominant kernel `%s` "
+                "%.2f us by HIP events (%s), %.2f us in this trace (all calls, warm-up included)."
+                % (b["ms_per_step"], dom, roof.get("avg_ms", 0) * 1e3,
+                   "%.1f %s = %.1f %% of peak" % (roof.get("achieved", 0), roof.get("unit", ""),
+                                                  100 * roof.get("frac", 0)),
+                   float(tr[0]["AverageNs"]) / 1e3 if tr else float("nan")),
+                "Library sources: `%s` (hash of csrc/, as in the bench's traffic lookup)."
+                % source_sha()]
     return "\n".join(out) + "\n"
 
 
@@ -483,6 +598,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20,
                     help="untimed steps first: the clocks settle over the first ~10 ms of work")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed steps for this long before the warm-up steps (clock settling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -494,12 +611,27 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--traffic-workload", default=None,
                     help="with --summarize-counters: workload name to file the numbers under")
-    ap.add_argument("--summarize-trace", nargs=3, metavar=("TRACE_DIR", "COMMAND", "TITLE"),
-                    help="print a markdown summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
+                    help="TRACE_DIR COMMAND TITLE [BENCH_JSON]: print a markdown summary of a "
+                         "rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-traffic", nargs="+",
+                    metavar="WORKLOAD BENCH_JSON [COMMAND ...]",
+                    help="print a markdown table of the committed counter traffic of a workload")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_DIR", "COMMAND", "TITLE"),
+                    help="print a markdown summary of the MFMA counters of a rocprofv3 --pmc run")
     args = ap.parse_args()
 
     if args.summarize_trace:
         sys.stdout.write(summarize_trace(*args.summarize_trace))
+        return 0
+
+    if args.summarize_traffic:
+        wl_, bj = args.summarize_traffic[:2]
+        sys.stdout.write(summarize_traffic(wl_, bj, args.summarize_traffic[2:]))
+        return 0
+
+    if args.summarize_mfma:
+        sys.stdout.write(summarize_mfma(*args.summarize_mfma))
         return 0
 
     if args.summarize_counters:
