@@ -48,6 +48,9 @@ def workloads():
         w["moe-120b-mxact-T%d" % T] = ("moe", s, 1)
     w[inputs.MOE_20B_PREFILL.name + "-mxact"] = ("moe", inputs.MOE_20B_PREFILL, 1)
     w[inputs.MOE_20B_DECODE.name + "-mxact"] = ("moe", inputs.MOE_20B_DECODE, 1)
+    # decode-shaped layers as one launch (MX_SINGLE_LAUNCH = 0x4)
+    for s in (inputs.MOE_20B_DECODE, inputs.MOE_120B[1], inputs.MOE_120B[256]):
+        w[s.name + "-single"] = ("moe", s, 4)
     for M in (1, 8, 32):
         w["linear-decode-M%d" % M] = ("linear", dict(M=M, K=2880, N=5760, seed=1), 0)
     return w
@@ -121,6 +124,9 @@ def kernel_work(name, T, H, F, E, k, touched, P, out_bytes, mxact):
         return 2.0 * T * E * H, T * H * 2 + E * H * 2 + T * E * 4 + T * k * 8
     if name == "permute":
         return 0.0, T * k * 4 * 4 + (E + 1) * 4
+    if name == "moe_single_launch":  # the whole layer: its touched weights, x, W_r, out
+        return (2.0 * P * 3 * F * H + 2.0 * T * E * H,
+                touched * 3 * F * H * wb + T * H * 2 + E * H * 2 + T * H * out_bytes)
     if name == "quantize":   # activation variant: x along H (h is quantized by gate_up)
         return 0.0, T * H * (2 + wb)
     return 0.0, 0.0
@@ -248,10 +254,11 @@ def bench_moe(args, name, shape, flags):
     mx.mx_profile_enable(False)
 
     P = s.T * s.k
-    peak = PEAK_FP4_TFLOPS if flags else PEAK_BF16_TFLOPS
+    mxact = bool(flags & 1)  # MX_ACT_MXFP4
+    peak = PEAK_FP4_TFLOPS if mxact else PEAK_BF16_TFLOPS
     kern = {}
     for kname, (n, tot) in prof.items():
-        fl, by = kernel_work(kname, s.T, s.H, s.F, s.E, s.k, touched, P, 2, bool(flags))
+        fl, by = kernel_work(kname, s.T, s.H, s.F, s.E, s.k, touched, P, 2, mxact)
         kern[kname] = {"avg_ms": round(tot / n, 5), "launches": n, "flops": fl, "bytes": by}
     dom = max(kern, key=lambda k: kern[k]["avg_ms"] * kern[k]["launches"])
     d = kern[dom]
@@ -268,14 +275,15 @@ def bench_moe(args, name, shape, flags):
         "metric": METRIC, "value": round(s.T / (ms * 1e-3), 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": timed_steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp4" if flags else "bf16", "data": "synthetic",
+        "dtype": "fp4" if mxact else "bf16", "data": "synthetic",
         "config": {"workload": name, "T": s.T, "H": s.H, "F": s.F, "E": s.E, "k": s.k,
                    "weights": "mxfp4 (e2m1 + e8m0 per 32)",
                    "weight_layout": "tiled (converted once at load)" if tiled else "row-major",
-                   "activations": "mxfp4" if flags else "bf16",
+                   "activations": "mxfp4" if mxact else "bf16",
                    "out_dtype": "bf16", "router_bias_std": s.bias_std, "seed": s.seed,
                    "parallelism": "single-gpu", "weight_copies": n_w, "token_batches": n_x,
-                   "launch": "hip graph per rotation" if args.graph else "eager"},
+                   "launch": ("one persistent kernel per step" if flags & 4 else
+                              "hip graph per rotation" if args.graph else "eager")},
         "settle": settle,
         "step": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
                  "hbm_gbs_algorithmic": round(layer_traffic / (ms * 1e-3) / 1e9, 1),
@@ -285,7 +293,7 @@ def bench_moe(args, name, shape, flags):
     }
     if want_cpu:
         result["cpu_baseline"] = cpu_baseline_moe(args, s, x_all[:s.T], wr_np, br_np, host_w,
-                                                  bool(flags))
+                                                  mxact)
     return result
 
 

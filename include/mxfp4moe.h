@@ -63,6 +63,9 @@ typedef enum { MX_F32 = 0, MX_BF16 = 1 } mx_dtype;
 #define MX_ACT_MXFP4 0x1u
 /* The expert weights of mxfp4_moe_mlp are in the tiled layout written by mxfp4_tile_weights. */
 #define MX_WEIGHTS_TILED 0x2u
+/* mxfp4_moe_mlp runs the whole MLP (routing included) as one persistent launch whose steps wait
+ * for each other on the GPU; for decode-sized batches (see mxfp4_moe_mlp). */
+#define MX_SINGLE_LAUNCH 0x4u
 
 /* Upper limits checked on the host. */
 #define MX_MAX_EXPERTS 256
@@ -165,7 +168,7 @@ mx_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, 
 typedef struct mx_moe_desc {
   size_t struct_size;          /* sizeof(mx_moe_desc) or MX_MOE_DESC_SIZE_V1; else MX_ERR_UNSUPPORTED */
   int32_t T, H, F, E, k;       /* tokens, hidden, expert FFN width, experts, experts per token */
-  uint32_t flags;              /* MX_ACT_MXFP4 and/or MX_WEIGHTS_TILED, or 0 */
+  uint32_t flags;              /* MX_ACT_MXFP4, MX_WEIGHTS_TILED, MX_SINGLE_LAUNCH, or 0 */
   mx_dtype out_dtype;          /* dtype of `out` */
   const uint16_t* x;           /* [T][H] bf16 */
   const uint16_t* wr;          /* [E][H] bf16 router weight; unused if topk_idx_in is given */
@@ -215,7 +218,17 @@ size_t mxfp4_moe_mlp_workspace(const mx_moe_desc* desc);
  *   Concurrent calls must use distinct workspaces.
  *   Internal routing is moe_route_topk's up to the fp32 summation order of the logits (small
  *   batches split H over more workgroups, partial sums added in a fixed order, so results do not
- *   depend on timing); the top-k is exact given the logits it reports. */
+ *   depend on timing); the top-k is exact given the logits it reports.
+ *   MX_SINGLE_LAUNCH ([GGUF] "생성 루프 최적화": generation is bound by the host-GPU round trips
+ *   around each step): the same computation in one kernel launch -- routing, permutation,
+ *   gate_up, down and combine wait for each other through counters the library keeps on each
+ *   device -- with the same results up to the fp32 summation order of the logits. For
+ *   decode-sized batches: T*k <= 2048, bf16 activations (with MX_ACT_MXFP4:
+ *   MX_ERR_UNSUPPORTED). Calls with this flag must not overlap on one device (different streams
+ *   or threads: serialize them); a wait that gives up (never in a correct run) sets
+ *   MX_DEVERR_SYNC and leaves the outputs invalid. On MI355X the per-step launches (the flag
+ *   left out) measured faster at the decode shapes tried; the flag serves callers that need the
+ *   call to be a single kernel launch. */
 mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
@@ -260,6 +273,8 @@ const char* mx_last_error(void);
  * the library keeps for each device (the current one is read): */
 #define MX_DEVERR_ROUTING 0x1  /* a routing index outside [0, E) was skipped (moe_permute,
                                   mxfp4_moe_mlp with caller routing) */
+#define MX_DEVERR_SYNC 0x2     /* a wait inside an MX_SINGLE_LAUNCH call gave up: its outputs
+                                  are invalid */
 /* Synchronizes `stream`, copies the current device's error word to *code_host (host pointer; 0 =
  * none) and clears it. Calls on other streams of the device share the word. For tests and
  * debugging: it synchronizes. */

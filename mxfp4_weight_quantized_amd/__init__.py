@@ -22,7 +22,9 @@ MX_ERR_WORKSPACE, MX_ERR_UNSUPPORTED, MX_ERR_HIP = 5, 6, 7
 MX_F32, MX_BF16 = 0, 1
 MX_ACT_MXFP4 = 0x1
 MX_WEIGHTS_TILED = 0x2
+MX_SINGLE_LAUNCH = 0x4
 MX_DEVERR_ROUTING = 0x1
+MX_DEVERR_SYNC = 0x2
 MX_NOALLOC_SCRATCH_BYTES = 32 << 20
 MX_GU_INTERLEAVED = 0x1
 MX_TILE_DEINTERLEAVE = 0x1
@@ -212,7 +214,8 @@ def moe_permute(topk_idx: torch.Tensor, E: int, stream=None, use_workspace: bool
 
 def get_device_error(stream=None) -> int:
     """mx_get_device_error: synchronizes the stream, returns and clears the device error word of
-    the current device (0 = none; MX_DEVERR_ROUTING = a routing index was out of range)."""
+    the current device (0 = none; MX_DEVERR_ROUTING = a routing index was out of range,
+    MX_DEVERR_SYNC = a wait inside a single-launch call gave up)."""
     v = ctypes.c_int32(0)
     _check(lib().mx_get_device_error(_stream(stream), ctypes.byref(v)))
     return int(v.value)
@@ -256,7 +259,8 @@ def mxfp4_moe_mlp(x, gu_packed, gu_scales, dn_packed, dn_scales, k, wr=None, br=
     """The whole MoE MLP. Weights: gu_packed [E, 2F, H/2], gu_scales [E, 2F, H/32],
     dn_packed [E, H, F/2], dn_scales [E, H, F/32] (with MX_WEIGHTS_TILED in flags: the same
     shapes as written by mxfp4_tile_weights). Routing: internal from (wr, br) unless
-    (topk_idx, topk_w) are given. Returns out [T, H] (and (logits, idx, w) if asked)."""
+    (topk_idx, topk_w) are given. MX_SINGLE_LAUNCH in flags: the whole call as one launch
+    (decode-sized batches). Returns out [T, H] (and (logits, idx, w) if asked)."""
     T, H = x.shape
     dev = x.device
     if out is None:

@@ -61,10 +61,10 @@ mx_status check_device() {
 
 // ---- opt-in per-kernel timing (benchmarks): HIP events on the caller's stream ----
 enum ProfKind { PK_QUANTIZE, PK_DEQUANTIZE, PK_ROUTE, PK_PERMUTE, PK_GATE_UP, PK_DOWN, PK_COMBINE,
-                PK_LINEAR, PK_TILE, PK_COUNT };
+                PK_LINEAR, PK_TILE, PK_SINGLE, PK_COUNT };
 const char* const kProfNames[PK_COUNT] = {"quantize", "dequantize", "route_topk", "permute",
                                           "moe_gate_up_swiglu", "moe_down_weighted", "moe_combine",
-                                          "linear", "tile_weights"};
+                                          "linear", "tile_weights", "moe_single_launch"};
 struct ProfRec {
   int kind;
   hipEvent_t a, b;
@@ -112,7 +112,8 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // ---- mxfp4_moe_mlp workspace layout ----
 struct MoeLayout {
-  size_t status, logits, idx, w, offsets, perm, inv, tiles, pcounts, h, y, xq, xqs, hq, hqs, total;
+  size_t status, logits, idx, w, offsets, perm, inv, tiles, pcounts, rpart, tile_ends, h, y, xq, xqs, hq, hqs,
+      total;
   size_t pcounts_bytes;
   int tile_rows, max_tiles;
 };
@@ -126,7 +127,8 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
     return o;
   };
   const size_t T = (size_t)d.T, P = (size_t)d.T * d.k, E = (size_t)d.E;
-  L.tile_rows = mx::moe_tile_rows(d.T, d.k, d.E, (d.flags & MX_ACT_MXFP4) != 0);
+  const bool single = (d.flags & MX_SINGLE_LAUNCH) != 0;
+  L.tile_rows = single ? 16 : mx::moe_tile_rows(d.T, d.k, d.E, (d.flags & MX_ACT_MXFP4) != 0);
   L.max_tiles = mx::moe_max_tiles(d.T, d.k, d.E, L.tile_rows);
   L.status = take(256);  // int32 status, int32 tile count
   L.logits = take(T * E * 4);
@@ -136,8 +138,11 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
   L.perm = take((P + mx::kMaxTileRows) * 4);  // tile-row padding (see launch_permute)
   L.inv = take(P * 4);
   L.tiles = take((size_t)L.max_tiles * 8);
-  L.pcounts_bytes = mx::permute_sliced_workspace(d.T, d.k, d.E);  // 0: one-workgroup permutation
+  L.pcounts_bytes = single ? 0 : mx::permute_sliced_workspace(d.T, d.k, d.E);  // 0: one workgroup
   L.pcounts = take(L.pcounts_bytes);
+  // the single launch's partial router logits (the split launches borrow y's rows for theirs)
+  L.rpart = single ? take((size_t)mx::single_route_splits(d.T, d.H, d.E) * T * E * 4) : 0;
+  L.tile_ends = single ? take((size_t)L.max_tiles * 4) : 0;
   // bf16 h (the activation variant quantizes h in the gate_up epilogue and keeps only hq, hqs)
   L.h = (d.flags & MX_ACT_MXFP4) ? 0 : take(P * (size_t)d.F * 2);
   L.y = take(P * (size_t)d.H * 4);
@@ -188,7 +193,12 @@ mx_status check_moe_desc(const mx_moe_desc* d) {
   if (d->H > MX_MAX_MOE_DIM || d->F > MX_MAX_MOE_DIM) return fail(MX_ERR_SHAPE, "H and F must be <= %d in the MoE MLP", MX_MAX_MOE_DIM);
   if ((int64_t)d->T * d->H * 2 >= (1LL << 31) || (int64_t)d->T * d->k * d->F * 2 >= (1LL << 31))
     return fail(MX_ERR_SHAPE, "T*H and T*k*F bf16 activations must stay below 2 GiB");
-  if (d->flags & ~(MX_ACT_MXFP4 | MX_WEIGHTS_TILED)) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if (d->flags & ~(MX_ACT_MXFP4 | MX_WEIGHTS_TILED | MX_SINGLE_LAUNCH)) return fail(MX_ERR_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  if ((d->flags & MX_SINGLE_LAUNCH) && (d->flags & MX_ACT_MXFP4))
+    return fail(MX_ERR_UNSUPPORTED, "MX_SINGLE_LAUNCH takes bf16 activations (not with MX_ACT_MXFP4)");
+  if ((d->flags & MX_SINGLE_LAUNCH) && (int64_t)d->T * d->k > mx::kSingleMaxPairs)
+    return fail(MX_ERR_UNSUPPORTED, "MX_SINGLE_LAUNCH takes decode-sized batches: T*k = %lld > %d",
+                (long long)d->T * d->k, mx::kSingleMaxPairs);
   if (d->act_flags & ~MX_GU_INTERLEAVED) return fail(MX_ERR_UNSUPPORTED, "unknown act_flags 0x%x", d->act_flags);
   if ((d->act_flags & MX_GU_INTERLEAVED) && !(d->flags & MX_WEIGHTS_TILED))
     return fail(MX_ERR_UNSUPPORTED, "interleaved gate/up rows need the tiled layout "
@@ -387,7 +397,68 @@ MX_API mx_status mxfp4_moe_mlp_noalloc(const mx_moe_desc* desc, void* stream) {
 }
 
 namespace {
+// The GEMM-side arguments of a call (routing outputs in the workspace unless the caller asked
+// for them or gave its own routing).
+mx::MoeGemmArgs gemm_args(const mx_moe_desc& d, const MoeLayout& L, char* w, const int32_t* idx,
+                          const float* tw) {
+  const bool mx_act = (d.flags & MX_ACT_MXFP4) != 0;
+  mx::MoeGemmArgs g{};
+  g.T = d.T; g.H = d.H; g.F = d.F; g.E = d.E; g.k = d.k;
+  g.mx_act = mx_act;
+  g.tiled = (d.flags & MX_WEIGHTS_TILED) != 0;
+  g.xq = reinterpret_cast<uint8_t*>(w + L.xq);
+  g.xqs = reinterpret_cast<uint8_t*>(w + L.xqs);
+  g.hq = reinterpret_cast<uint8_t*>(w + L.hq);
+  g.hqs = reinterpret_cast<uint8_t*>(w + L.hqs);
+  g.x = d.x;
+  g.perm = reinterpret_cast<int32_t*>(w + L.perm);
+  g.inv = reinterpret_cast<int32_t*>(w + L.inv);
+  g.offsets = reinterpret_cast<int32_t*>(w + L.offsets);
+  g.tiles = reinterpret_cast<int2*>(w + L.tiles);
+  g.num_tiles = reinterpret_cast<int32_t*>(w + L.status) + 1;
+  g.max_tiles = L.max_tiles;
+  g.topk_w = tw;
+  g.topk_idx = idx;
+  g.gu_packed = d.gu_packed; g.gu_scales = d.gu_scales;
+  g.dn_packed = d.dn_packed; g.dn_scales = d.dn_scales;
+  g.h = mx_act ? nullptr : reinterpret_cast<uint16_t*>(w + L.h);
+  g.y = reinterpret_cast<float*>(w + L.y);
+  g.out = d.out;
+  g.out_bf16 = d.out_dtype == MX_BF16;
+  if (act_custom(d)) {
+    g.act_custom = true;
+    g.gu_bias = d.gu_bias;
+    g.dn_bias = d.dn_bias;
+    g.gu_interleaved = (d.act_flags & MX_GU_INTERLEAVED) != 0;
+    g.act_alpha = d.swiglu_alpha != 0.f ? d.swiglu_alpha : 1.f;
+    g.act_limit = d.swiglu_limit;
+    g.act_shift = d.swiglu_up_shift;
+  }
+  return g;
+}
+
+// MX_SINGLE_LAUNCH: everything in one launch.
+mx_status moe_mlp_single(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStream_t s) {
+  const bool route = d.topk_idx_in == nullptr;
+  const int32_t* idx = route ? (d.topk_idx_out ? d.topk_idx_out : reinterpret_cast<int32_t*>(w + L.idx))
+                             : d.topk_idx_in;
+  const float* tw = route ? (d.topk_w_out ? d.topk_w_out : reinterpret_cast<float*>(w + L.w))
+                          : d.topk_w_in;
+  const mx::MoeGemmArgs g = gemm_args(d, L, w, idx, tw);
+  mx::SingleRouting r{};
+  r.wr = route ? d.wr : nullptr;
+  r.br = d.br;
+  r.logits = route ? d.logits_out : nullptr;
+  r.rpart = reinterpret_cast<float*>(w + L.rpart);
+  r.tile_ends = reinterpret_cast<int32_t*>(w + L.tile_ends);
+  r.status = reinterpret_cast<int32_t*>(w + L.status);
+  ProfScope ps(PK_SINGLE, s);
+  const hipError_t e = mx::launch_moe_single(g, r, s);
+  return e == hipSuccess ? ok() : hip_fail(e, "single launch");
+}
+
 mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStream_t s) {
+  if (d.flags & MX_SINGLE_LAUNCH) return moe_mlp_single(d, L, w, s);
   hipError_t e;
   int32_t* status = reinterpret_cast<int32_t*>(w + L.status);
   const int32_t* idx;
@@ -445,38 +516,7 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
                             reinterpret_cast<uint8_t*>(w + L.xqs), s);
     if (e != hipSuccess) return hip_fail(e, "x quantize launch");
   }
-  mx::MoeGemmArgs g{};
-  g.T = d.T; g.H = d.H; g.F = d.F; g.E = d.E; g.k = d.k;
-  g.mx_act = mx_act;
-  g.tiled = (d.flags & MX_WEIGHTS_TILED) != 0;
-  g.xq = reinterpret_cast<uint8_t*>(w + L.xq);
-  g.xqs = reinterpret_cast<uint8_t*>(w + L.xqs);
-  g.hq = reinterpret_cast<uint8_t*>(w + L.hq);
-  g.hqs = reinterpret_cast<uint8_t*>(w + L.hqs);
-  g.x = d.x;
-  g.perm = perm;
-  g.inv = inv;
-  g.offsets = offsets;
-  g.tiles = tiles;
-  g.num_tiles = status + 1;
-  g.max_tiles = L.max_tiles;
-  g.topk_w = tw;
-  g.topk_idx = idx;
-  g.gu_packed = d.gu_packed; g.gu_scales = d.gu_scales;
-  g.dn_packed = d.dn_packed; g.dn_scales = d.dn_scales;
-  g.h = mx_act ? nullptr : reinterpret_cast<uint16_t*>(w + L.h);
-  g.y = reinterpret_cast<float*>(w + L.y);
-  g.out = d.out;
-  g.out_bf16 = d.out_dtype == MX_BF16;
-  if (act_custom(d)) {
-    g.act_custom = true;
-    g.gu_bias = d.gu_bias;
-    g.dn_bias = d.dn_bias;
-    g.gu_interleaved = (d.act_flags & MX_GU_INTERLEAVED) != 0;
-    g.act_alpha = d.swiglu_alpha != 0.f ? d.swiglu_alpha : 1.f;
-    g.act_limit = d.swiglu_limit;
-    g.act_shift = d.swiglu_up_shift;
-  }
+  const mx::MoeGemmArgs g = gemm_args(d, L, w, idx, tw);
   {
     ProfScope ps(PK_GATE_UP, s);
     e = mx::launch_moe_gate_up(g, s);

@@ -177,93 +177,4 @@ __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// ---- top-k selection (router and the fused selection in the permutation) ----
-// (value desc, index asc) ordering: true if (va, ia) ranks before (vb, ib).
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-// One wave ranks the E logits of token t (logit_of(e) for e < E; lane l holds experts l, l+64,
-// l+128, l+192): k rounds of a wave-wide argmax under (logit desc, expert index asc), then the
-// softmax of the k selected logits; lane j < k writes entry j and returns its expert index.
-template <class LogitOf>
-__device__ __forceinline__ int select_topk_wave(LogitOf logit_of, int lane, int t, int E, int k,
-                                                int32_t* __restrict__ idx_out,
-                                                float* __restrict__ w_out) {
-  float cv[4];
-  int ci[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    ci[q] = e;
-    cv[q] = (e < E) ? logit_of(e) : -INFINITY;
-  }
-  bool used[4] = {false, false, false, false};
-  float sel_v[8];
-  int sel_i[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (!used[q] && ci[q] < E && (bi == 0x7fffffff || ranks_before(cv[q], ci[q], bv, bi))) {
-        bv = cv[q];
-        bi = ci[q];
-      }
-    // wave-wide best: DPP exchanges inside each 16-lane row (partners lane^1, lane^2, then the
-    // mirrored lane in the half row and in the row), then the four rows' bests combined
-    // uniformly from lanes 0, 16, 32 and 48
-    auto take = [&](float ov, int oi) {
-      if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    };
-    auto dpp_step = [&](auto ctrl) {
-      constexpr int C = decltype(ctrl)::value;
-      const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), C, 0xf, 0xf, false));
-      const int oi = __builtin_amdgcn_update_dpp(0, bi, C, 0xf, 0xf, false);
-      take(ov, oi);
-    };
-    dpp_step(std::integral_constant<int, 0xb1>{});   // quad_perm [1,0,3,2]: lane ^ 1
-    dpp_step(std::integral_constant<int, 0x4e>{});   // quad_perm [2,3,0,1]: lane ^ 2
-    dpp_step(std::integral_constant<int, 0x141>{});  // row_half_mirror: 7 - lane in 8
-    dpp_step(std::integral_constant<int, 0x140>{});  // row_mirror: 15 - lane in 16
-#pragma unroll
-    for (int row = 1; row < 4; ++row)
-      take(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 16 * row)),
-           __builtin_amdgcn_readlane(bi, 16 * row));
-    {  // row 0 last, so that every lane ends with the same (uniform) result
-      const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bv), 0));
-      const int i0 = __builtin_amdgcn_readlane(bi, 0);
-      take(v0, i0);
-    }
-    sel_v[j] = bv;
-    sel_i[j] = bi;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (ci[q] == bi) used[q] = true;
-  }
-  float sum = 0.f, mine = 0.f;
-  int mine_i = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    const float ev = expf(sel_v[j] - sel_v[0]);
-    sum += ev;
-    if (lane == j) {
-      mine = ev;
-      mine_i = sel_i[j];
-    }
-  }
-  if (lane < k) {
-    idx_out[(int64_t)t * k + lane] = mine_i;
-    w_out[(int64_t)t * k + lane] = mine / sum;
-  }
-  return mine_i;
-}
-
-
 }  // namespace mx

@@ -40,6 +40,7 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
 // mx_get_device_error reads and clears it. device_error_word() is its device address on the
 // current device (looked up once per device; nullptr if the lookup failed).
 constexpr int32_t kDevErrRouting = 1;  // a routing index outside [0, E) was skipped
+constexpr int32_t kDevErrSync = 2;     // a wait of the single-launch pipeline gave up
 int32_t* device_error_word();
 
 // permute.hip: tiles/num_tiles may be NULL (tile_rows ignored then). With a tile list, perm must
@@ -103,6 +104,22 @@ int moe_max_tiles(int T, int k, int E, int tile_rows);
 hipError_t launch_moe_gate_up(const MoeGemmArgs& a, hipStream_t stream);
 hipError_t launch_moe_down(const MoeGemmArgs& a, hipStream_t stream);
 hipError_t launch_moe_combine(const MoeGemmArgs& a, hipStream_t stream);
+
+// single.hip: the whole MoE MLP of a decode-sized batch (T * k <= kSingleMaxPairs, bf16
+// activations) as one launch on 16-row tiles (tile list of moe_max_tiles(T, k, E, 16) entries).
+// Calls on one device must not overlap: they share the library's counters for the launch.
+constexpr int kSingleMaxPairs = 2048;
+struct SingleRouting {
+  const uint16_t* wr;  // router [E][H] bf16; nullptr: the caller's routing (m.topk_idx, m.topk_w)
+  const float* br;     // router bias [E] or nullptr
+  float* logits;       // [T][E] or nullptr (not stored)
+  float* rpart;        // single_route_splits(T, H, E) * T * E floats
+  int32_t* tile_ends;  // [max_tiles] workspace
+  int32_t* status;     // 1 if a routing index was outside [0, E)
+};
+// With internal routing m.topk_idx and m.topk_w are where the routing is written.
+int single_route_splits(int T, int H, int E);
+hipError_t launch_moe_single(const MoeGemmArgs& m, const SingleRouting& r, hipStream_t stream);
 
 // Dense linear. Decode-sized M splits K over several workgroups (linear_k_splits > 1): the
 // splits' fp32 partial sums go to `partials` (linear_k_splits * M * N floats), then one more

@@ -18,8 +18,7 @@
 // (SELECT: all logits staged in LDS -- summed from the router's partial tiles where H was split
 // over workgroups -- then one wave per token, the router's selection function), keeping the
 // indices in LDS; this saves the separate selection launch of the router in the MoE MLP.
-#include "mx_device.h"
-#include "mx_launch.h"
+#include "route_device.h"
 
 #include <atomic>
 
@@ -46,25 +45,7 @@ int32_t* device_error_word() {
 namespace {
 
 constexpr int kWaves = 16;
-constexpr int kMaxE = 256;
-
-// Exclusive scan of n (<= 256) ints in LDS by one wave; returns the total to every lane.
-__device__ int wave_exclusive_scan(int* v, int n, int lane) {
-  int carry = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    const int x = (i < n) ? v[i] : 0;
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    if (i < n) v[i] = carry + incl - x;
-    carry += __shfl(incl, 63);
-  }
-  return carry;
-}
+constexpr int kMaxE = kPermuteMaxE;
 
 template <bool SELECT>
 __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx, int P,
@@ -87,12 +68,7 @@ __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx
   __shared__ float slog[SELECT ? kSelectMaxLogits : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int chunk = (P + kWaves - 1) / kWaves;
-  const int p_begin = min(P, wave * chunk);
-  const int p_end = min(P, p_begin + chunk);
 
-  for (int i = threadIdx.x; i < kWaves * kMaxE; i += blockDim.x) (&cnt[0][0])[i] = 0;
-  if (threadIdx.x == 0) bad = 0;
   if constexpr (SELECT) {  // 0. top-k of every token (P = T * k <= kSelectMaxPairs)
     // all T x E logits into LDS with coalesced loads (from the partial tiles: summed in split
     // order, plus the bias, and stored as the logits), then one wave per token ranks them there
@@ -116,90 +92,14 @@ __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx
                                      w_out);
       if (lane < k) sidx[t * k + lane] = e;
     }
+    __syncthreads();
   }
-  __syncthreads();
   auto pair_expert = [&](int p) -> int {
     if constexpr (SELECT) return sidx[p];
     else return idx[p];
   };
-
-  // 1. per-wave histogram
-  for (int p = p_begin + lane; p < p_end; p += 64) {
-    const int e = pair_expert(p);
-    if (e >= 0 && e < E) atomicAdd(&cnt[wave][e], 1);
-    else bad = 1;
-  }
-  __syncthreads();
-
-  // 2. totals per expert, scan -> offsets; first row of every (wave, expert)
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int s = 0;
-    for (int w = 0; w < kWaves; ++w) s += cnt[w][e];
-    tot[e] = s;
-    if (tile_rows > 0) tbase[e] = (s + tile_rows - 1) / tile_rows;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int total = wave_exclusive_scan(tot, E, lane);
-    if (lane == 0) tot[E] = total;
-  } else if (wave == 1 && tile_rows > 0) {
-    const int total = wave_exclusive_scan(tbase, E, lane);
-    if (lane == 0) tbase[E] = total;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = tot[e];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = tot[e];
-    for (int w = 0; w < kWaves; ++w) {
-      const int c = cnt[w][e];
-      cnt[w][e] = run;
-      run += c;
-    }
-    if (tile_rows > 0) {
-      const int n = tot[e + 1] - tot[e];
-      const int tb = tbase[e];
-      for (int i = 0; i * tile_rows < n; ++i) tiles[tb + i] = make_int2(e, tot[e] + i * tile_rows);
-    }
-  }
-  if (threadIdx.x == 0) {
-    if (tile_rows > 0) *num_tiles = tbase[E];
-    if (status != nullptr) *status = bad;
-    if (bad && dev_err != nullptr) atomicOr(dev_err, kDevErrRouting);
-  }
-  // With a tile list, perm carries tile_rows entries of padding past P: rows past the last valid
-  // one (and the padding) hold pair 0, so a tile may read its whole row range of perm.
-  if (tile_rows > 0)
-    for (int i = tot[E] + threadIdx.x; i < P + tile_rows; i += blockDim.x) perm[i] = 0;
-  __syncthreads();
-
-  // 3. stable scatter, 64 pairs per step in (token, slot) order
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int g0 = p_begin; g0 < p_end; g0 += 64) {
-    const int p = g0 + lane;
-    int e = (p < p_end) ? pair_expert(p) : -1;
-    const bool ok = (e >= 0 && e < E);
-    if (!ok) {
-      if (p < p_end) inv[p] = -1;
-      e = 0;
-    }
-    uint64_t peers = __ballot(ok);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bb = __ballot(bit);
-      peers &= bit ? bb : ~bb;
-    }
-    const int rank = __popcll(peers & lt_mask);
-    int pos = 0;
-    if (ok) pos = cnt[wave][e] + rank;
-    __builtin_amdgcn_wave_barrier();
-    if (ok) {
-      perm[pos] = p;
-      inv[p] = pos;
-      if (rank == 0) cnt[wave][e] = pos + __popcll(peers);
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
+  permute_pairs<kWaves>(pair_expert, P, E, offsets, perm, inv, status, dev_err, tile_rows, tiles,
+                        num_tiles, &cnt[0][0], tot, tbase, &bad);
 }
 
 // Pass 1 of the sliced permutation: counts[s][e] = pairs of slice s routed to expert e; column

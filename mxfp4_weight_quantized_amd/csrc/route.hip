@@ -16,8 +16,7 @@
 // then ranks its tokens' logits from LDS (no second kernel). Otherwise route_select_kernel: one
 // wave per token (adds up the partial tiles and the bias first, if there are partials) ranks the
 // logits (wave-wide argmax k times) and writes the top-k indices and their softmax.
-#include "mx_device.h"
-#include "mx_launch.h"
+#include "route_device.h"
 
 namespace mx {
 namespace {
@@ -54,28 +53,7 @@ __global__ __launch_bounds__(1024) void route_logits_kernel(
   const int all_splits = n_splits * gridDim.z, gsplit = blockIdx.z * n_splits + split;
   const int s0 = nsteps * gsplit / all_splits;
   const int s1 = nsteps * (gsplit + 1) / all_splits;
-  const int tok = min(t0 + m, T - 1);
-  const int ex = min(grp * 16 + m, E - 1);
-  const uint16_t* xa = x + (int64_t)tok * H + g * 8;
-  const uint16_t* wb = wr + (int64_t)ex * H + g * 8;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // batches of BATCH steps, branch-free: all loads of a batch go out before its MFMAs; steps past
-  // the split's end re-read its last step and are zeroed, so they add nothing
-  constexpr int kBatch = BATCH;
-  for (int st = s0; st < s1; st += kBatch) {
-    u32x4 a[kBatch], b[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int su = min(st + u, s1 - 1);
-      a[u] = *reinterpret_cast<const u32x4*>(xa + 32 * su);
-      b[u] = *reinterpret_cast<const u32x4*>(wb + 32 * su);
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const u32x4 av = (st + u < s1) ? a[u] : u32x4{0u, 0u, 0u, 0u};
-      acc = mfma16x16x32(u32x4_as_bf16x8(av), u32x4_as_bf16x8(b[u]), acc);
-    }
-  }
+  f32x4 acc = logit_tile_partial<BATCH>(x, wr, T, H, E, t0, grp * 16, s0, s1, lane);
   // every split's tile goes to LDS; the first split of each group sums them in split order
   if (n_splits > 1) {
 #pragma unroll

@@ -174,8 +174,9 @@ def test_moe_workspace_query_and_errors(L):
     assert L.mxfp4_moe_mlp(None, _fake(), 1 << 30, None) == mx.MX_ERR_NULL
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(H=48)), _fake(), 1 << 30, None) == mx.MX_ERR_SHAPE
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(k=9)), _fake(), 1 << 30, None) == mx.MX_ERR_SHAPE
-    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(flags=4)), _fake(), 1 << 30, None) == mx.MX_ERR_UNSUPPORTED
-    for fl in (mx.MX_WEIGHTS_TILED, mx.MX_WEIGHTS_TILED | mx.MX_ACT_MXFP4):  # accepted flags
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(flags=8)), _fake(), 1 << 30, None) == mx.MX_ERR_UNSUPPORTED
+    for fl in (mx.MX_WEIGHTS_TILED, mx.MX_WEIGHTS_TILED | mx.MX_ACT_MXFP4, mx.MX_SINGLE_LAUNCH,
+               mx.MX_SINGLE_LAUNCH | mx.MX_WEIGHTS_TILED):  # accepted flags
         assert L.mxfp4_moe_mlp(ctypes.byref(_desc(flags=fl, x=0)), _fake(), 1 << 30,
                                None) == mx.MX_ERR_NULL
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(out_dtype=5)), _fake(), 1 << 30, None) == mx.MX_ERR_DTYPE
@@ -204,6 +205,18 @@ def test_moe_workspace_query_and_errors(L):
                            None) == mx.MX_ERR_UNSUPPORTED
     assert L.mxfp4_moe_mlp(ctypes.byref(_desc(swiglu_limit=float("inf"))), _fake(), 1 << 30,
                            None) == mx.MX_ERR_SHAPE
+    # the single launch: decode-sized batches of bf16 activations only; its workspace adds the
+    # partial router logits and drops the sliced permutation's counts
+    S = mx.MX_SINGLE_LAUNCH
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(flags=S | mx.MX_ACT_MXFP4)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_UNSUPPORTED
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(T=513, k=4, flags=S)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_UNSUPPORTED
+    assert "decode-sized" in mx.last_error()
+    assert L.mxfp4_moe_mlp(ctypes.byref(_desc(T=512, k=4, flags=S, x=0)), _fake(), 1 << 30,
+                           None) == mx.MX_ERR_NULL
+    n_single = mx.mxfp4_moe_mlp_workspace(_desc(T=64, H=2880, F=2880, E=32, k=4, flags=S))
+    assert n < n_single <= n + 8 * 64 * 32 * 4 + 2 * 256
     # the allocation-free entry point: same checks, and problems beyond its array are rejected
     # on the host before anything runs
     big = _desc(T=8192, H=2880, F=2880, E=32, k=4)
