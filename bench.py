@@ -473,7 +473,7 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
              "moe_down_weighted": ["moe_down_weighted_kernel"], "moe_combine": ["combine_kernel"],
              "route_topk": ["route_logits_kernel", "route_select_kernel"],
              "permute": ["permute_kernel"], "linear": ["linear_kernel"],
-             "quantize": ["quantize_kernel"]}
+             "quantize": ["quantize_kernel"], "moe_single_launch": ["moe_single_launch_kernel"]}
     out = {}
     for kind, syms in kinds.items():
         fk = wk = 0.0
@@ -512,6 +512,8 @@ def summarize_traffic(workload, bench_json, commands):
            "| kernel | fetch KiB | write KiB | HBM MB / launch | algorithmic MB | ratio |",
            "|---|---:|---:|---:|---:|---:|"]
     for k, v in sorted(ent.items(), key=lambda kv: -kv[1]["hbm_bytes_per_launch"]):
+        if kern and k not in kern:  # (a kernel of the set-up, such as the weights' quantization)
+            continue
         alg = kern.get(k, {}).get("bytes")
         out.append("| %s | %s | %s | %.1f | %s | %s |" % (
             k, format(v["fetch_kib"], ",.0f"), format(v["write_kib"], ",.0f"),
@@ -586,7 +588,8 @@ def summarize_trace(trace_dir, command, title, bench_json=None):
         roof = b.get("roofline", {})
         dom = roof.get("kernel")
         sym = {"moe_gate_up_swiglu": "moe_gate_up_swiglu_kernel", "moe_down_weighted":
-               "moe_down_weighted_kernel", "moe_combine": "combine_kernel", "linear": "linear_kernel"}
+               "moe_down_weighted_kernel", "moe_combine": "combine_kernel", "linear": "linear_kernel",
+               "moe_single_launch": "moe_single_launch_kernel"}
         tr = [r for r in rows if sym.get(dom, "?") in r["Name"]]
         out += ["", "The traced bench.py run's own line: %.4f ms per step; dominant kernel `%s` "
                 "%.2f us by HIP events (%s), %.2f us in this trace (all calls, warm-up included)."
