@@ -285,9 +285,14 @@ def bench_moe(args, name, shape, flags):
                    "launch": ("one persistent kernel per step" if flags & 4 else
                               "hip graph per rotation" if args.graph else "eager")},
         "settle": settle,
+        # the whole call against the same roofline as the dominant kernel (whose figure
+        # "roofline" is kernel-level): MFMA peak for prefill-shaped layers, HBM for decode-shaped
         "step": {"tflops": round(layer_flops / (ms * 1e-3) / 1e12, 2),
                  "hbm_gbs_algorithmic": round(layer_traffic / (ms * 1e-3) / 1e9, 1),
-                 "touched_experts": touched},
+                 "touched_experts": touched,
+                 "bound": roof["bound"],
+                 "frac": round(layer_flops / (ms * 1e-3) / 1e12 / peak if roof["bound"] == "mfma"
+                               else layer_traffic / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "kernels": kern,
         "roofline": roof,
     }

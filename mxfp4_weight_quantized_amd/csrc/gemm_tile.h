@@ -989,12 +989,16 @@ struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 2
 struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT, MF = 16; };
 struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT, MF = 16; };
 // Activation variant, prefill-shaped: FP4 activations take a quarter of the LDS and need no
-// decode instructions, so wide tiles with fewer bytes per MFMA pay: 128 x 512 (gate_up, eight
-// waves of 64 x 128) and 128 x 384 (down: 2880 columns split into 7.5 rather than 5.6 tiles),
-// 3 stages. Measured on the 20B prefill shapes against 64 x 256 (about 15% slower), 128 x 256,
-// 128 x 384 with 2 or 4 stages and 8-block stages (spills).
-struct CfgPreGU4 { static constexpr int BM = 128, BN = 512, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
-struct CfgPreDn4 { static constexpr int BM = 128, BN = 384, WM = 2, WN = 4, KT = 4, ST = 3, GM = 4, OCC = 1, SCM = SCM_STAGE, MF = 16; };
+// decode instructions, so wide wave tiles with fewer bytes per MFMA pay: 128 x 256 workgroup
+// tiles of four waves of 64 x 128, 3 stages, two workgroups per CU (the eight waves a CU holds
+// as two independent workgroups, whose barriers no longer stall each other: against one
+// workgroup of eight waves on 128 x 512, 20B-shaped prefill gate_up 581 -> 482 us, 120B-shaped
+// T = 4096 449 -> 391 us), down with row tiles grouped by 2 (311 -> 293 us). Also measured: 64 x
+// 256 (about 15% slower), 128 x 384 with 2 or 4 stages, 8-block stages (spills), three
+// workgroups per CU with 2 stages (spills: 5x slower), groups of 8 row tiles, and 128 x 256 as
+// one wave row of four.
+struct CfgPreGU4 { static constexpr int BM = 128, BN = 256, WM = 2, WN = 2, KT = 4, ST = 3, GM = 4, OCC = 2, SCM = SCM_STAGE, MF = 16; };
+struct CfgPreDn4 { static constexpr int BM = 128, BN = 256, WM = 2, WN = 2, KT = 4, ST = 3, GM = 2, OCC = 2, SCM = SCM_STAGE, MF = 16; };
 // Few pairs (a handful of experts touched): with fewer tiles than CUs each workgroup's own weight
 // stream is the bound, so these tiles keep more stages in flight. The down GEMM (2880 columns: 23
 // tiles of 128 per expert) also takes 64-column tiles, twice the workgroups. 120B-shaped decode,
