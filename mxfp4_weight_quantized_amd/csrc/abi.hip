@@ -81,8 +81,10 @@ hipEvent_t prof_event() {
     g_event_pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence when the event is recorded (a cache write-back and
+  // invalidation that lengthened every bracketed decode-sized kernel by a few us)
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
