@@ -40,9 +40,12 @@ def _both(x, wd, k, idx, w, flags, out_dtype, act=None):
     return split, single
 
 
-# decode-shaped problems (T*k < 64 E: decode tiles in both forms), few-expert (T = 1) included
+# decode-shaped problems (T*k < 64 E: decode tiles in both forms), few-expert (T = 1) included,
+# and the largest batches the single launch takes (T*k = 2048: 128 token tiles, and with E = 256
+# the longest tile list, 384 row tiles)
 CASES = [(1, 2880, 2880, 128, 4), (5, 256, 192, 8, 2), (37, 256, 320, 16, 4),
-         (64, 2880, 2880, 32, 4), (130, 128, 96, 8, 1), (17, 96, 64, 256, 8)]
+         (64, 2880, 2880, 32, 4), (130, 128, 96, 8, 1), (17, 96, 64, 256, 8),
+         (2048, 128, 96, 256, 1), (256, 128, 64, 256, 8)]
 
 
 @pytest.mark.parametrize("T,H,F,E,k", CASES)
@@ -123,11 +126,36 @@ def test_single_back_to_back_problems():
     assert mx.get_device_error() == 0
 
 
+# (and a small layer at the launch's limit of 2048 pairs, internal routing over 32 token tiles)
+LIMIT = inputs.MoEShape("moe-limit-T512", T=512, H=256, F=256, E=32, k=4, seed=981)
+
+
 @pytest.mark.parametrize("shape,tiled", [(inputs.MOE_20B_DECODE, True), (inputs.MOE_20B_DECODE, False),
-                                         (inputs.MOE_120B[1], True), (inputs.MOE_120B[256], True)],
-                         ids=["20b-decode-tiled", "20b-decode-rowmajor", "120b-T1", "120b-T256"])
+                                         (inputs.MOE_120B[1], True), (inputs.MOE_120B[256], True),
+                                         (LIMIT, True)],
+                         ids=["20b-decode-tiled", "20b-decode-rowmajor", "120b-T1", "120b-T256",
+                              "limit-T512"])
 def test_single_full_layer(shape, tiled):
     """Every token of a full-size layer with internal routing, fp32 and bf16 outputs, against
     the oracle."""
     check_full_layer(shape, S, tiled=tiled)
+    assert mx.get_device_error() == 0
+
+
+def test_single_through_the_allocation_free_entry_point():
+    """MX_SINGLE_LAUNCH with the library's own workspace: the same output as with a caller
+    workspace, twice in a row (the second call smaller)."""
+    for (T, H, F, E, k) in [(40, 256, 192, 16, 4), (9, 128, 96, 8, 2)]:
+        seed = 990 + T
+        x = to_dev(inputs.activations(seed, T, H))
+        wd = tiled_dev(tuple(to_dev(a) for a in moe_weights(seed, E, H, F)))
+        wr, _ = inputs.router(seed, E, H, 0.0)
+        kw = dict(wr=to_dev(wr), out_dtype=torch.float32, flags=S | TILED)
+        ref = mx.mxfp4_moe_mlp(x, *wd, k, **kw)
+        out = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        d = mx.make_moe_desc(x, *wd, k, out, wr=kw["wr"], flags=S | TILED)
+        note("single, allocation-free entry point, T=%d" % T)
+        mx.mxfp4_moe_mlp_noalloc(d)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
     assert mx.get_device_error() == 0
