@@ -20,8 +20,10 @@ hipError_t launch_tile_weights(const uint8_t* packed, const uint8_t* scales, int
 
 // route.hip
 // partials (may be null): fp32 scratch of route_partial_splits(T, H, E) * T * E floats; with it
-// small batches split H over more workgroups. logits may be null (not stored): then every
-// workgroup covers all experts of its tokens and makes the selection itself.
+// small batches split H over more workgroups, and large ones (with logits, H % 64 == 0) run as
+// 64-token tiles over all experts with H split over route_partial_splits workgroups per tile.
+// logits may be null (not stored): then every workgroup covers all experts of its tokens and
+// makes the selection itself.
 hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
                              int E, int k, float* logits, int32_t* idx, float* w, float* partials,
                              hipStream_t stream);

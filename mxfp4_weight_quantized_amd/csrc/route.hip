@@ -16,6 +16,14 @@
 // then ranks its tokens' logits from LDS (no second kernel). Otherwise route_select_kernel: one
 // wave per token (adds up the partial tiles and the bias first, if there are partials) ranks the
 // logits (wave-wide argmax k times) and writes the top-k indices and their softmax.
+//
+// Large batches with a logits buffer take route_tile_kernel instead: 64 tokens per workgroup
+// against every expert, operands staged through LDS. The cost of the 16-token kernel above is
+// not arithmetic but W_r streaming into every CU again for every 16 tokens (each CU pulls its
+// share of L2 at a limited rate); with 64-token tiles that stream is four times shorter, and H is
+// split over 2 to 8 workgroups per tile so that the launch still covers the CUs. The splits'
+// partial logits go through memory to route_select_kernel, which sums them in split order.
+#include "gemm_tile.h"
 #include "route_device.h"
 
 namespace mx {
@@ -118,6 +126,147 @@ __global__ __launch_bounds__(256) void route_select_kernel(float* __restrict__ l
       lane, t, E, k, idx_out, w_out);
 }
 
+// ---- large batches: 64-token tiles over all experts, staged through LDS ----
+constexpr int kTileTok = 64;  // tokens per workgroup
+constexpr int kTileK = 64;    // elements of H per stage: one 128-byte row per token / expert
+
+template <int NB>  // 16-expert blocks (E <= 16 NB)
+struct RouteTile {
+  static constexpr int ROWS = kTileTok + 16 * NB;    // LDS rows per stage: tokens, then experts
+  static constexpr int STAGE = ROWS * 128;            // bytes
+  static constexpr int STAGES = NB >= 16 ? 3 : NB >= 8 ? 4 : 6;
+  static constexpr int INSTR = ROWS / 8;              // 64 x 16-byte loads fill 8 rows
+  static constexpr int PW = (INSTR + 3) / 4;          // loads per wave and stage (4 waves)
+  static_assert((STAGES - 2) * PW < 64, "vmcnt range");
+};
+
+// Workgroup (blockIdx.x, blockIdx.y): tokens [64 bx, 64 bx + 64) x all experts over the
+// 64-element chunks [c0, c1) of H that split by owns. Each stage holds the tile's 64 token rows
+// and 16 NB expert rows (rows past T or E read as zeros) as 128-byte rows, chunks XOR-swizzled by
+// row. Wave w computes tokens 16w .. 16w + 15 against every expert block. With one split the
+// logits (plus the bias) go to logits, else the partial sums to partials[by][T][E].
+template <int NB>
+__global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ wr,
+                                                         const float* __restrict__ br, int T, int H,
+                                                         int E, float* __restrict__ logits,
+                                                         float* __restrict__ partials) {
+  using RT = RouteTile<NB>;
+  __shared__ __align__(1024) uint8_t smem[RT::STAGES * RT::STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * kTileTok;
+  const int nc = H / kTileK, S = gridDim.y;
+  const int c0 = nc * (int)blockIdx.y / S, c1 = nc * ((int)blockIdx.y + 1) / S, n = c1 - c0;
+  const i32x4 rx = make_res(x, (int64_t)T * H * 2);
+  const i32x4 rw = make_res(wr, (int64_t)E * H * 2);
+
+  // lane offsets of this wave's loads (fixed over the stages; chunk j adds 128 j bytes)
+  uint32_t voff[RT::PW];
+  int ldst[RT::PW];
+#pragma unroll
+  for (int q = 0; q < RT::PW; ++q) {
+    const int i = (wave * RT::PW + q) % RT::INSTR;
+    const int row = 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ swz_rows<8>(row);
+    const int src = row < kTileTok ? t0 + row : row - kTileTok;
+    const bool ok = row < kTileTok ? src < T : src < E;
+    voff[q] = ok ? (uint32_t)src * (uint32_t)(H * 2) + 16u * c + 128u * c0 : kOutOfRange;
+    ldst[q] = 1024 * i;
+  }
+  auto issue = [&](int j) {
+    uint8_t* st = smem + (j % RT::STAGES) * RT::STAGE;
+#pragma unroll
+    for (int q = 0; q < RT::PW; ++q) {
+      const bool is_x = __builtin_amdgcn_readfirstlane(ldst[q]) < kTileTok * 128;
+      dma_b128(is_x ? rx : rw, off_add(voff[q], 128u * j), 0, st + ldst[q]);
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int m = lane & 15, g = lane >> 4;
+  const int ar = 16 * wave + m;
+
+#pragma unroll
+  for (int j = 0; j < RT::STAGES - 1; ++j)
+    if (j < n) issue(j);
+  for (int j = 0; j < n; ++j) {
+    if (j + RT::STAGES - 1 <= n) wait_vmcnt<(RT::STAGES - 2) * RT::PW>();
+    else wait_vmcnt<0>();
+    barrier_lds();
+    if (j + RT::STAGES - 1 < n) issue(j + RT::STAGES - 1);
+    const uint8_t* st = smem + (j % RT::STAGES) * RT::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = 4 * ks + g;
+      const u32x4 a = lds_read_b128(st + ar * 128 + ((ch ^ swz_rows<8>(ar)) << 4));
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int r = kTileTok + 16 * b + m;
+        const u32x4 w = lds_read_b128(st + r * 128 + ((ch ^ swz_rows<8>(r)) << 4));
+        acc[b] = mfma16x16x32(u32x4_as_bf16x8(a), u32x4_as_bf16x8(w), acc[b]);
+      }
+    }
+  }
+
+  // value i of acc[b] in lane (m, g): token 16 w + 4 g + i, expert 16 b + m
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int e = 16 * b + m;
+    if (e >= E) continue;
+    const float bias = (S == 1 && br != nullptr) ? br[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wave + 4 * g + i;
+      if (t >= T) continue;
+      if (S == 1) logits[(int64_t)t * E + e] = acc[b][i] + bias;
+      else partials[((int64_t)blockIdx.y * T + t) * E + e] = acc[b][i];
+    }
+  }
+}
+
+// Splits of H per 64-token tile: doubled (to at most 8, each split at least two chunks) while
+// the launch has fewer than 256 workgroups.
+int route_tile_splits(int T, int H) {
+  const int tiles = (T + kTileTok - 1) / kTileTok, nc = H / kTileK;
+  int S = 1;
+  while (S < 8 && tiles * S < 256 && nc >= 4 * S) S *= 2;
+  return S;
+}
+
+// The tiled router applies to large batches (the ones the 16-token kernel runs with every expert
+// group in one workgroup) whose H is a multiple of 64.
+bool route_tiled(int T, int H, int E) {
+  const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
+  return H % kTileK == 0 && tiles * groups > kSpreadBelow;
+}
+
+hipError_t launch_route_tile(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
+                             int E, float* logits, float* partials, int S, hipStream_t stream) {
+  const dim3 grid((T + kTileTok - 1) / kTileTok, S), block(256);
+  const int nb = (E + 15) / 16;
+  if (nb <= 1) hipLaunchKernelGGL(route_tile_kernel<1>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else if (nb <= 2) hipLaunchKernelGGL(route_tile_kernel<2>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else if (nb <= 4) hipLaunchKernelGGL(route_tile_kernel<4>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else if (nb <= 8) hipLaunchKernelGGL(route_tile_kernel<8>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else hipLaunchKernelGGL(route_tile_kernel<16>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
+  return hipGetLastError();
+}
+
+// Workgroups per token tile and expert group in the spread launch, when partial sums have a
+// buffer: doubled (up to 4) while the launch stays within 256 workgroups (20B-shaped router,
+// T = 64: 8 tiles, 17 -> 12 us with 4; 120B-shaped, T = 256: 128 tiles, 17.5 -> 14 us with 2).
+int route_spread_splits(int T, int H, int E) {
+  const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
+  const int base = tiles * groups;
+  if (base > kSpreadBelow || H / 32 < 16) return 1;
+  int so = 1;
+  while (so < 4 && base * so * 2 <= 256) so *= 2;
+  return so;
+}
+
 }  // namespace
 
 // At most one token per wave of the permutation workgroup: with more, the selections queue up on
@@ -130,16 +279,8 @@ bool route_logits_defers_select(int T, int E, int k) {
          (int64_t)T * E <= kSelectMaxLogits;
 }
 
-// Workgroups per token tile and expert group in the spread launch, when partial sums have a
-// buffer: doubled (up to 4) while the launch stays within 256 workgroups (20B-shaped router,
-// T = 64: 8 tiles, 17 -> 12 us with 4; 120B-shaped, T = 256: 128 tiles, 17.5 -> 14 us with 2).
 int route_partial_splits(int T, int H, int E) {
-  const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
-  const int base = tiles * groups;
-  if (base > kSpreadBelow || H / 32 < 16) return 1;
-  int so = 1;
-  while (so < 4 && base * so * 2 <= 256) so *= 2;
-  return so;
+  return route_tiled(T, H, E) ? route_tile_splits(T, H) : route_spread_splits(T, H, E);
 }
 
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
@@ -150,7 +291,7 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
   const int splits = min(16, H / 32);
   // with a partials buffer H is also split over so workgroups per tile (splits is 16 then)
-  const int so = partials != nullptr ? route_partial_splits(T, H, E) : 1;
+  const int so = partials != nullptr ? route_spread_splits(T, H, E) : 1;
   if (so > 1) *n_part = so;
   hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups, so), dim3(64 * (splits / so)), 0,
                      stream, x, wr, br, T, H, E, 1, splits / so, logits, 0, nullptr, nullptr,
@@ -162,6 +303,16 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
                              int E, int k, float* logits, int32_t* idx, float* w, float* partials,
                              hipStream_t stream) {
   if (T == 0) return hipSuccess;
+  if (logits != nullptr && route_tiled(T, H, E)) {
+    const int S = route_tile_splits(T, H);
+    if (S == 1 || partials != nullptr) {
+      hipError_t e = launch_route_tile(x, wr, br, T, H, E, logits, partials, S, stream);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T,
+                         E, k, idx, w, partials, S > 1 ? S : 0, br);
+      return hipGetLastError();
+    }
+  }
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
   // G groups per workgroup, H split so that G x splits fills up to 16 waves. Without a logits
   // buffer every workgroup covers all experts of its tokens and selects from LDS.
@@ -177,7 +328,7 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
     return hipGetLastError();
   }
   // (G is 1 here: one expert group per workgroup; splits is 16 wherever so > 1)
-  const int so = partials != nullptr ? route_partial_splits(T, H, E) : 1;
+  const int so = partials != nullptr ? route_spread_splits(T, H, E) : 1;
   hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups, so), dim3(64 * (splits / so)), 0,
                      stream, x, wr, br, T, H, E, 1, splits / so, logits, k, idx, w, partials);
   hipError_t e = hipGetLastError();
