@@ -14,8 +14,9 @@
 // over 2 or 4 workgroups per tile, whose partial tiles the selection kernel sums in split order.
 // With many tokens G covers all experts and each token tile is read once, and the same workgroup
 // then ranks its tokens' logits from LDS (no second kernel). Otherwise route_select_kernel: one
-// wave per token (adds up the partial tiles and the bias first, if there are partials) ranks the
-// logits (wave-wide argmax k times) and writes the top-k indices and their softmax.
+// 16-lane row of a wave per token (adds up the partial tiles and the bias first, if there are
+// partials) ranks the logits (argmax k times, inside the row) and writes the top-k indices and
+// their softmax.
 //
 // Large batches with a logits buffer take route_tile_kernel instead: 64 tokens per workgroup
 // against every expert, operands staged through LDS. The cost of the 16-token kernel above is
@@ -101,29 +102,74 @@ __global__ __launch_bounds__(1024) void route_logits_kernel(
   }
 }
 
-// One wave per token, logits read back from memory; with n_part > 0 partial tiles, the wave
-// first sums partials[0..n_part)[t][e] in that order, adds the bias and writes the logits.
+// One 16-lane row per token (16 tokens per workgroup), logits read back from memory; with
+// NP > 0 partial tiles, the row first sums partials[0..NP)[t][e] in that order, adds the bias and
+// writes the logits (a compile-time NP lets all of a lane's loads go out together). NQ: experts
+// per lane (E <= 16 NQ).
+template <int NQ, int NP>
 __global__ __launch_bounds__(256) void route_select_kernel(float* __restrict__ logits, int T, int E,
                                                            int k, int32_t* __restrict__ idx_out,
                                                            float* __restrict__ w_out,
                                                            const float* __restrict__ partials,
-                                                           int n_part, const float* __restrict__ br) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                           const float* __restrict__ br) {
+  const int j16 = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
   if (t >= T) return;
-  if (n_part == 0) {
-    select_topk_wave([&](int e) { return logits[(int64_t)t * E + e]; }, lane, t, E, k, idx_out, w_out);
-    return;
+  float cv[NQ];
+  if constexpr (NP == 0) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = j16 + 16 * q;
+      cv[q] = (e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
+    }
+  } else {
+    float part[NP][NQ];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int e = min(j16 + 16 * q, E - 1);
+        part[p][q] = partials[((int64_t)p * T + t) * E + e];
+      }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = j16 + 16 * q;
+      float s = part[0][q];
+#pragma unroll
+      for (int p = 1; p < NP; ++p) s += part[p][q];
+      s += (br != nullptr) ? br[min(e, E - 1)] : 0.f;
+      if (e < E) logits[(int64_t)t * E + e] = s;
+      cv[q] = (e < E) ? s : -INFINITY;
+    }
   }
-  select_topk_wave(
-      [&](int e) {
-        float s = partials[(int64_t)t * E + e];
-        for (int p = 1; p < n_part; ++p) s += partials[((int64_t)p * T + t) * E + e];
-        s += (br != nullptr) ? br[e] : 0.f;
-        logits[(int64_t)t * E + e] = s;
-        return s;
-      },
-      lane, t, E, k, idx_out, w_out);
+  select_topk_row16<NQ>(cv, j16, t, E, k, idx_out, w_out);
+}
+
+template <int NP>
+void launch_select_np(int nq, dim3 grid, float* logits, int T, int E, int k, int32_t* idx, float* w,
+                      const float* partials, const float* br, hipStream_t stream) {
+  const dim3 block(256);
+  if (nq <= 1) hipLaunchKernelGGL((route_select_kernel<1, NP>), grid, block, 0, stream, logits, T, E, k, idx, w, partials, br);
+  else if (nq <= 2) hipLaunchKernelGGL((route_select_kernel<2, NP>), grid, block, 0, stream, logits, T, E, k, idx, w, partials, br);
+  else if (nq <= 4) hipLaunchKernelGGL((route_select_kernel<4, NP>), grid, block, 0, stream, logits, T, E, k, idx, w, partials, br);
+  else if (nq <= 8) hipLaunchKernelGGL((route_select_kernel<8, NP>), grid, block, 0, stream, logits, T, E, k, idx, w, partials, br);
+  else hipLaunchKernelGGL((route_select_kernel<16, NP>), grid, block, 0, stream, logits, T, E, k, idx, w, partials, br);
+}
+
+// n_part: 0 (logits complete) or 2, 4, 8 partial tiles.
+hipError_t launch_route_select(float* logits, int T, int E, int k, int32_t* idx, float* w,
+                               const float* partials, int n_part, const float* br,
+                               hipStream_t stream) {
+  const dim3 grid((T + 15) / 16);
+  const int nq = (E + 15) / 16;
+  switch (n_part) {
+    case 0: launch_select_np<0>(nq, grid, logits, T, E, k, idx, w, partials, br, stream); break;
+    case 2: launch_select_np<2>(nq, grid, logits, T, E, k, idx, w, partials, br, stream); break;
+    case 4: launch_select_np<4>(nq, grid, logits, T, E, k, idx, w, partials, br, stream); break;
+    case 8: launch_select_np<8>(nq, grid, logits, T, E, k, idx, w, partials, br, stream); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ---- large batches: 64-token tiles over all experts, staged through LDS ----
@@ -308,9 +354,7 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
     if (S == 1 || partials != nullptr) {
       hipError_t e = launch_route_tile(x, wr, br, T, H, E, logits, partials, S, stream);
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T,
-                         E, k, idx, w, partials, S > 1 ? S : 0, br);
-      return hipGetLastError();
+      return launch_route_select(logits, T, E, k, idx, w, partials, S > 1 ? S : 0, br, stream);
     }
   }
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
@@ -333,9 +377,7 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
                      stream, x, wr, br, T, H, E, 1, splits / so, logits, k, idx, w, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, logits, T, E, k,
-                     idx, w, partials, so > 1 ? so : 0, br);
-  return hipGetLastError();
+  return launch_route_select(logits, T, E, k, idx, w, partials, so > 1 ? so : 0, br, stream);
 }
 
 }  // namespace mx

@@ -140,6 +140,66 @@ __device__ __forceinline__ int select_topk_wave(LogitOf logit_of, int lane, int 
   return mine_i;
 }
 
+// The same selection on one 16-lane row of a wave per token: lane j of the row holds the logits
+// of experts j, j + 16, ..., j + 16 (NQ - 1) in cv (entries past E are ignored). The four DPP
+// exchanges inside the row leave the row's best in every lane of it, so no step crosses rows.
+// Every lane of the row calls it; row lane j < k writes entry j. The softmax is the same
+// arithmetic as select_topk_wave's.
+template <int NQ>
+__device__ __forceinline__ void select_topk_row16(const float (&cv)[NQ], int j16, int t, int E,
+                                                  int k, int32_t* __restrict__ idx_out,
+                                                  float* __restrict__ w_out) {
+  uint32_t used = 0;
+  float sel_v[8];
+  int sel_i[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = j16 + 16 * q;
+      if (!((used >> q) & 1u) && e < E && (bi == 0x7fffffff || ranks_before(cv[q], e, bv, bi))) {
+        bv = cv[q];
+        bi = e;
+      }
+    }
+    auto dpp_step = [&](auto ctrl) {
+      constexpr int C = decltype(ctrl)::value;
+      const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), C, 0xf, 0xf, false));
+      const int oi = __builtin_amdgcn_update_dpp(0, bi, C, 0xf, 0xf, false);
+      if (oi != 0x7fffffff && (bi == 0x7fffffff || ranks_before(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    };
+    dpp_step(std::integral_constant<int, 0xb1>{});   // quad_perm [1,0,3,2]: lane ^ 1
+    dpp_step(std::integral_constant<int, 0x4e>{});   // quad_perm [2,3,0,1]: lane ^ 2
+    dpp_step(std::integral_constant<int, 0x141>{});  // row_half_mirror: 7 - lane in 8
+    dpp_step(std::integral_constant<int, 0x140>{});  // row_mirror: 15 - lane in 16
+    sel_v[j] = bv;
+    sel_i[j] = bi;
+    if ((bi & 15) == j16) used |= 1u << (bi >> 4);
+  }
+  float sum = 0.f, mine = 0.f;
+  int mine_i = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    const float ev = expf(sel_v[j] - sel_v[0]);
+    sum += ev;
+    if (j16 == j) {
+      mine = ev;
+      mine_i = sel_i[j];
+    }
+  }
+  if (j16 < k) {
+    idx_out[(int64_t)t * k + j16] = mine_i;
+    w_out[(int64_t)t * k + j16] = mine / sum;
+  }
+}
+
 // ---- stable counting sort of the (token, slot) pairs by expert ----
 // Exclusive scan of n (<= 256) ints in LDS by one wave; returns the total to every lane.
 __device__ __forceinline__ int wave_exclusive_scan(int* v, int n, int lane) {
