@@ -146,8 +146,8 @@ mx_status moe_route_topk(const uint16_t* x, const uint16_t* wr, const float* br,
  *   inv [T*k] int32 out: inv[t*k + j] = its permuted row.
  *   ws: device workspace of moe_permute_workspace(T, k, E) bytes, 256-byte aligned, owned by the
  *   caller (contents need not be initialized). Large batches are then permuted by many
- *   workgroups (a histogram of every 4096-pair slice, then each slice placed from all slice
- *   histograms). ws may be NULL (ws_bytes ignored): one workgroup then does the whole
+ *   workgroups (a histogram of every 1024-pair slice, then each slice placed from all slice
+ *   histograms; from T*k >= 8192). ws may be NULL (ws_bytes ignored): one workgroup then does the whole
  *   permutation, with the same results element for element. A non-NULL ws smaller than the
  *   query is MX_ERR_WORKSPACE. The query is 0 for small batches.
  *   Indices outside [0, E) are left out of perm, their inv entry is -1, and the device error

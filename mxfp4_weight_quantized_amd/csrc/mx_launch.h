@@ -50,7 +50,8 @@ int32_t* device_error_word();
 constexpr int kMaxTileRows = 128;
 constexpr int kSelectMaxPairs = 2048;   // launch_select_permute: T * k at most this
 constexpr int kSelectMaxLogits = 16384; //   and T * E at most this (its logits stay in LDS)
-constexpr int kSlicePairs = 4096;      // launch_permute_sliced: pairs per workgroup
+constexpr int kSlicePairs = 1024;      // launch_permute_sliced: pairs per workgroup
+constexpr int kSlicedMinPairs = 8192;  //   used from this many pairs (with a workspace)
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* offsets, int32_t* perm,
                           int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
                           int32_t* num_tiles, hipStream_t stream);

@@ -8,11 +8,14 @@
 // chunk 64 pairs at a time, ranking equal experts among the 64 lanes with ballots. The order is
 // the stable (token, slot) order by construction, so the result is deterministic.
 //
-// Large batches (P >= kSlicePairs * 2, with a workspace) take two launches over many workgroups
+// Large batches (P >= kSlicedMinPairs, with a workspace) take two launches over many workgroups
 // instead: a histogram of every kSlicePairs-pair slice, then per slice the same scan (each
-// workgroup derives its slice's first row per expert from all slice histograms) and the same
-// ballot-ranked scatter. Slices are contiguous in (token, slot) order, so the result is the same
-// stable counting sort, element for element.
+// workgroup derives its slice's first row per expert from all slice histograms, staged through
+// LDS with every count loaded at once) and the same ballot-ranked scatter. Slices are contiguous
+// in (token, slot) order, so the result is the same stable counting sort, element for element.
+// Both kernels are latency chains: small slices keep them short (4096-pair slices with the
+// counts read one slice after another: 17.5 us for 32768 pairs; 1024-pair slices: see the
+// results of the library's benchmark).
 //
 // For small batches the same launch can first make the top-k selection from the router logits
 // (SELECT: all logits staged in LDS -- summed from the router's partial tiles where H was split
@@ -46,6 +49,7 @@ namespace {
 
 constexpr int kWaves = 16;
 constexpr int kMaxE = kPermuteMaxE;
+constexpr int kCountLds = 8192;  // ints of slice histograms staged at once (>= 31 slices of E + 1)
 
 template <bool SELECT>
 __global__ __launch_bounds__(1024) void permute_kernel(int32_t* __restrict__ idx, int P,
@@ -108,12 +112,18 @@ __global__ __launch_bounds__(256) void slice_hist_kernel(const int32_t* __restri
                                                          int E, int32_t* __restrict__ counts) {
   __shared__ int h[kMaxE + 1];
   for (int i = threadIdx.x; i <= E; i += blockDim.x) h[i] = 0;
-  __syncthreads();
   const int p0 = blockIdx.x * kSlicePairs, p1 = min(P, p0 + kSlicePairs);
-  for (int p = p0 + threadIdx.x; p < p1; p += blockDim.x) {
-    const int e = idx[p];
-    atomicAdd(&h[(e >= 0 && e < E) ? e : E], 1);
+  constexpr int kPer = kSlicePairs / 256;
+  int ev[kPer];  // every load of the thread first, then the LDS counts
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int p = p0 + threadIdx.x + 256 * u;
+    ev[u] = p < p1 ? idx[p] : 0;
   }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (p0 + (int)threadIdx.x + 256 * u < p1) atomicAdd(&h[(ev[u] >= 0 && ev[u] < E) ? ev[u] : E], 1);
   __syncthreads();
   for (int i = threadIdx.x; i <= E; i += blockDim.x) counts[(int64_t)blockIdx.x * (E + 1) + i] = h[i];
 }
@@ -129,6 +139,8 @@ __global__ __launch_bounds__(1024) void slice_scatter_kernel(
   __shared__ int tot[kMaxE + 1];
   __shared__ int pre[kMaxE];
   __shared__ int tbase[kMaxE + 1];
+  __shared__ int cst[kCountLds];
+  __shared__ int sbad;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int slice = blockIdx.x;
@@ -138,17 +150,44 @@ __global__ __launch_bounds__(1024) void slice_scatter_kernel(
   const int p_end = min(s1, p_begin + chunk);
 
   for (int i = threadIdx.x; i < kWaves * kMaxE; i += blockDim.x) (&cnt[0][0])[i] = 0;
-  // totals over all slices and this slice's prefix (slices before it), per expert
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int s = 0, before = 0;
-    for (int w = 0; w < n_slices; ++w) {
-      const int c = counts[(int64_t)w * (E + 1) + e];
-      if (w < slice) before += c;
-      s += c;
+  // totals over all slices and this slice's prefix (slices before it), per expert (thread e < E),
+  // and (thread E) whether any slice skipped an index outside [0, E): the slice histograms go
+  // through LDS in chunks of whole slices, all of a chunk's counts loaded at once
+  const int per = kCountLds / (E + 1);
+  int s_all = 0, before = 0;
+  for (int w0 = 0; w0 < n_slices; w0 += per) {
+    const int n = min(per, n_slices - w0) * (E + 1);
+    for (int i0 = 0; i0 < n; i0 += 4 * 64 * kWaves) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + threadIdx.x + 64 * kWaves * u;
+        v[u] = i < n ? counts[(int64_t)w0 * (E + 1) + i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + threadIdx.x + 64 * kWaves * u;
+        if (i < n) cst[i] = v[u];
+      }
     }
-    tot[e] = s;
+    __syncthreads();
+    if (threadIdx.x <= E) {
+      const int e = threadIdx.x;
+      for (int w = 0; w * (E + 1) < n; ++w) {
+        const int c = cst[w * (E + 1) + e];
+        if (w0 + w < slice) before += c;
+        s_all += c;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    tot[e] = s_all;
     pre[e] = before;
-    if (tile_rows > 0) tbase[e] = (s + tile_rows - 1) / tile_rows;
+    if (tile_rows > 0) tbase[e] = (s_all + tile_rows - 1) / tile_rows;
+  } else if (threadIdx.x == E) {
+    sbad = s_all != 0;
   }
   __syncthreads();
   for (int p = p_begin + lane; p < p_end; p += 64) {  // per-wave histogram of the slice
@@ -172,10 +211,8 @@ __global__ __launch_bounds__(1024) void slice_scatter_kernel(
       }
     if (threadIdx.x == 0) {
       if (tile_rows > 0) *num_tiles = tbase[E];
-      int bad = 0;
-      for (int w = 0; w < n_slices; ++w) bad |= counts[(int64_t)w * (E + 1) + E] != 0;
-      if (status != nullptr) *status = bad;
-      if (bad && dev_err != nullptr) atomicOr(dev_err, kDevErrRouting);
+      if (status != nullptr) *status = sbad;
+      if (sbad && dev_err != nullptr) atomicOr(dev_err, kDevErrRouting);
     }
     if (tile_rows > 0)
       for (int i = tot[E] + threadIdx.x; i < P + tile_rows; i += blockDim.x) perm[i] = 0;
@@ -223,7 +260,7 @@ __global__ __launch_bounds__(1024) void slice_scatter_kernel(
 
 size_t permute_sliced_workspace(int T, int k, int E) {
   const int64_t P = (int64_t)T * k;
-  if (P < 2LL * kSlicePairs) return 0;
+  if (P < kSlicedMinPairs) return 0;
   return (size_t)((P + kSlicePairs - 1) / kSlicePairs) * (E + 1) * 4;
 }
 

@@ -124,11 +124,14 @@ def test_permute_bit_exact(T, k, E, skew):
 
 @pytest.mark.parametrize("T,k,E,skew,bad", [(2048, 4, 32, 0, 0), (8192, 4, 32, 1, 0),
                                             (4096, 4, 128, 0, 0), (10001, 3, 7, 1, 0),
-                                            (3000, 8, 256, 1, 0), (5000, 4, 16, 0, 1)])
+                                            (3000, 8, 256, 1, 0), (5000, 4, 16, 0, 1),
+                                            (5000, 8, 256, 1, 1)])
 def test_permute_sliced_bit_exact(T, k, E, skew, bad):
     """moe_permute with its workspace: large batches go through the per-slice histogram and
     scatter (two launches, many workgroups); the result must be the oracle's counting sort
-    element for element, and equal the one-workgroup form (ws = NULL)."""
+    element for element, and equal the one-workgroup form (ws = NULL). T=5000/k=8/E=256 has
+    more slices (40) than one LDS chunk of slice histograms holds (31), with skipped indices in
+    both chunks."""
     r = np.random.default_rng(70 + T)
     if skew:
         p = np.exp(r.normal(0, 1.5, E)); p /= p.sum()
