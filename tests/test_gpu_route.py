@@ -46,10 +46,10 @@ def test_route_topk_parity(T, H, E, k, bias):
 
 
 # Routing inside mxfp4_moe_mlp: small batches with more than one expert group split H over 2 or
-# 4 workgroups per tile, whose partial sums the selection adds up in split order (T=64/E=32 and
-# T=17/E=20: four splits, the latter with a ragged token tile and expert group; T=256/E=128:
-# two; E=40: a ragged expert group). T=9/E=4 is one expert group: the logits kernel selects
-# itself, no split. Large batches take the 64-token tiles over all experts with H split over S
+# 4 workgroups per tile, whose partial sums the selection kernel adds up in split order (T=64/E=32,
+# T=100/E=32 and T=17/E=20: four splits, the latter with a ragged token tile and expert group;
+# T=256/E=128: two; E=40: a ragged expert group). T=9/E=4 is one expert group: the logits
+# kernel selects itself, no split. Large batches take the 64-token tiles over all experts with H split over S
 # workgroups: T=8192/E=32 (2 expert blocks, S = 2) and T=4096/E=128 (8 blocks, S = 4) are the
 # 20B and 120B prefill routers; T=600/E=256 (16 blocks, S = 8, ragged token tile), T=3000/E=40
 # (4 blocks for 3 groups: a ragged block, S = 4 over 10 chunks: uneven splits) and
@@ -59,7 +59,8 @@ def test_route_topk_parity(T, H, E, k, bias):
                                           (9, 3072, 4, 2, 0.5), (256, 2880, 128, 4, 1.0),
                                           (17, 2880, 20, 4, 0.5), (8192, 2880, 32, 4, 0.5),
                                           (4096, 2880, 128, 4, 1.0), (600, 1024, 256, 8, 1.0),
-                                          (3000, 640, 40, 4, 0.5), (9000, 128, 16, 2, 0.5)])
+                                          (3000, 640, 40, 4, 0.5), (9000, 128, 16, 2, 0.5),
+                                          (100, 2880, 32, 4, 0.5)])
 def test_route_inside_moe_call(T, H, E, k, bias):
     seed, F = 35 + T, 64
     x = inputs.activations(seed, T, H)
