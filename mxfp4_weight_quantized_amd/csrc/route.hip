@@ -176,28 +176,31 @@ hipError_t launch_route_select(float* logits, int T, int E, int k, int32_t* idx,
 constexpr int kTileTok = 64;  // tokens per workgroup
 constexpr int kTileK = 64;    // elements of H per stage: one 128-byte row per token / expert
 
-template <int NB>  // 16-expert blocks (E <= 16 NB)
+template <int NB, int NW>  // 16-expert blocks (E <= 16 NB); waves (4, or 8: two per token group)
 struct RouteTile {
   static constexpr int ROWS = kTileTok + 16 * NB;    // LDS rows per stage: tokens, then experts
   static constexpr int STAGE = ROWS * 128;            // bytes
   static constexpr int STAGES = NB >= 16 ? 3 : NB >= 8 ? 4 : 6;
   static constexpr int INSTR = ROWS / 8;              // 64 x 16-byte loads fill 8 rows
-  static constexpr int PW = (INSTR + 3) / 4;          // loads per wave and stage (4 waves)
+  static constexpr int PW = (INSTR + NW - 1) / NW;    // loads per wave and stage
+  static constexpr int NBW = NB * 4 / NW;             // expert blocks per wave
   static_assert((STAGES - 2) * PW < 64, "vmcnt range");
+  static_assert(NW == 4 || (NW == 8 && NB >= 2), "wave layout");
 };
 
 // Workgroup (blockIdx.x, blockIdx.y): tokens [64 bx, 64 bx + 64) x all experts over the
 // 64-element chunks [c0, c1) of H that split by owns. Each stage holds the tile's 64 token rows
 // and 16 NB expert rows (rows past T or E read as zeros) as 128-byte rows, chunks XOR-swizzled by
-// row. Wave w computes tokens 16w .. 16w + 15 against every expert block. With one split the
-// logits (plus the bias) go to logits, else the partial sums to partials[by][T][E].
-template <int NB>
-__global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restrict__ x,
+// row. Wave w computes tokens 16 (w % 4) .. + 15 against expert blocks [w / 4 * NBW, + NBW) (all
+// of them with four waves; half with eight, two waves per SIMD). With one split the logits (plus
+// the bias) go to logits, else the partial sums to partials[by][T][E].
+template <int NB, int NW>
+__global__ __launch_bounds__(64 * NW) void route_tile_kernel(const uint16_t* __restrict__ x,
                                                          const uint16_t* __restrict__ wr,
                                                          const float* __restrict__ br, int T, int H,
                                                          int E, float* __restrict__ logits,
                                                          float* __restrict__ partials) {
-  using RT = RouteTile<NB>;
+  using RT = RouteTile<NB, NW>;
   __shared__ __align__(1024) uint8_t smem[RT::STAGES * RT::STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,11 +232,12 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
     }
   };
 
-  f32x4 acc[NB];
+  f32x4 acc[RT::NBW];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < RT::NBW; ++b) acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int m = lane & 15, g = lane >> 4;
-  const int ar = 16 * wave + m;
+  const int tg = wave & 3, b0 = (wave >> 2) * RT::NBW;
+  const int ar = 16 * tg + m;
 
 #pragma unroll
   for (int j = 0; j < RT::STAGES - 1; ++j)
@@ -249,23 +253,23 @@ __global__ __launch_bounds__(256) void route_tile_kernel(const uint16_t* __restr
       const int ch = 4 * ks + g;
       const u32x4 a = lds_read_b128(st + ar * 128 + ((ch ^ swz_rows<8>(ar)) << 4));
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int r = kTileTok + 16 * b + m;
+      for (int b = 0; b < RT::NBW; ++b) {
+        const int r = kTileTok + 16 * (b0 + b) + m;
         const u32x4 w = lds_read_b128(st + r * 128 + ((ch ^ swz_rows<8>(r)) << 4));
         acc[b] = mfma16x16x32(u32x4_as_bf16x8(a), u32x4_as_bf16x8(w), acc[b]);
       }
     }
   }
 
-  // value i of acc[b] in lane (m, g): token 16 w + 4 g + i, expert 16 b + m
+  // value i of acc[b] in lane (m, g): token 16 tg + 4 g + i, expert 16 (b0 + b) + m
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int e = 16 * b + m;
+  for (int b = 0; b < RT::NBW; ++b) {
+    const int e = 16 * (b0 + b) + m;
     if (e >= E) continue;
     const float bias = (S == 1 && br != nullptr) ? br[e] : 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 16 * wave + 4 * g + i;
+      const int t = t0 + 16 * tg + 4 * g + i;
       if (t >= T) continue;
       if (S == 1) logits[(int64_t)t * E + e] = acc[b][i] + bias;
       else partials[((int64_t)blockIdx.y * T + t) * E + e] = acc[b][i];
@@ -291,13 +295,13 @@ bool route_tiled(int T, int H, int E) {
 
 hipError_t launch_route_tile(const uint16_t* x, const uint16_t* wr, const float* br, int T, int H,
                              int E, float* logits, float* partials, int S, hipStream_t stream) {
-  const dim3 grid((T + kTileTok - 1) / kTileTok, S), block(256);
+  const dim3 grid((T + kTileTok - 1) / kTileTok, S), b4(256), b8(512);
   const int nb = (E + 15) / 16;
-  if (nb <= 1) hipLaunchKernelGGL(route_tile_kernel<1>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
-  else if (nb <= 2) hipLaunchKernelGGL(route_tile_kernel<2>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
-  else if (nb <= 4) hipLaunchKernelGGL(route_tile_kernel<4>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
-  else if (nb <= 8) hipLaunchKernelGGL(route_tile_kernel<8>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
-  else hipLaunchKernelGGL(route_tile_kernel<16>, grid, block, 0, stream, x, wr, br, T, H, E, logits, partials);
+  if (nb <= 1) hipLaunchKernelGGL((route_tile_kernel<1, 4>), grid, b4, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else if (nb <= 2) hipLaunchKernelGGL((route_tile_kernel<2, 8>), grid, b8, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else if (nb <= 4) hipLaunchKernelGGL((route_tile_kernel<4, 8>), grid, b8, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else if (nb <= 8) hipLaunchKernelGGL((route_tile_kernel<8, 8>), grid, b8, 0, stream, x, wr, br, T, H, E, logits, partials);
+  else hipLaunchKernelGGL((route_tile_kernel<16, 8>), grid, b8, 0, stream, x, wr, br, T, H, E, logits, partials);
   return hipGetLastError();
 }
 
