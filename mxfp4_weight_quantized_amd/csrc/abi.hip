@@ -152,7 +152,7 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
     L.xq = take(T * (size_t)d.H / 2);
     L.xqs = take(T * (size_t)d.H / 32);
     L.hq = take(P * (size_t)d.F / 2);
-    L.hqs = take(P * (size_t)d.F / 32);
+    L.hqs = take((P + 3) / 4 * 4 * (size_t)d.F / 32);  // block-major [F/32][P rounded up to 4]
   }
   L.total = off;
   return L;
@@ -412,6 +412,7 @@ mx::MoeGemmArgs gemm_args(const mx_moe_desc& d, const MoeLayout& L, char* w, con
   g.xqs = reinterpret_cast<uint8_t*>(w + L.xqs);
   g.hq = reinterpret_cast<uint8_t*>(w + L.hq);
   g.hqs = reinterpret_cast<uint8_t*>(w + L.hqs);
+  g.hqs_pitch = ((int64_t)d.T * d.k + 3) / 4 * 4;
   g.x = d.x;
   g.perm = reinterpret_cast<int32_t*>(w + L.perm);
   g.inv = reinterpret_cast<int32_t*>(w + L.inv);

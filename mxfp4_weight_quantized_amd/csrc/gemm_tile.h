@@ -36,7 +36,9 @@ constexpr int kResidentNb = 96;  // resident scales hold up to K = 3072 (32-bloc
 struct GemmKArgs {
   const uint16_t* A;          // bf16 activation rows of length K
   int64_t a_rows;             // rows in A (bounds the buffer view of A)
-  const uint8_t* Asc;         // A scales [a_rows][K/32] when A is MXFP4 (else unused)
+  const uint8_t* Asc;         // A scales when A is MXFP4 (else unused): [a_rows][K/32], or in the
+                              // down product block-major [K/32][sc_pitch]
+  int64_t sc_pitch;           // FP4 h scales, block-major (gate_up writes them, down reads them)
   const int32_t* a_gather;    // A row of permuted row r = a_gather[r] / a_div (NULL: r)
   int a_div;
   const uint8_t* Bp;          // packed weights, expert-major
@@ -52,7 +54,7 @@ struct GemmKArgs {
   int rows_total;             // rows of the (permuted) row space: P grouped, M dense
   int F;                      // gate_up: up rows start at F
   void* out;                  // gate_up with FP4 activations: packed codes of h [rows][F/2]
-  uint8_t* out_scales;        //   and their scale bytes [rows][F/32]
+  uint8_t* out_scales;        //   and their scale bytes, block-major [F/32][sc_pitch]
   int out_bf16;
   // expert activation of the gate_up epilogue (act_custom = 0: h = silu(g) * u) with its bias
   // [E][2F] in the caller's row order, interleaved or not (NULL = none). (The down bias is added
@@ -294,7 +296,12 @@ struct GemmLds {
   // (stage scale dwords padded to a whole number of instructions per wave: no repeated loads)
   static constexpr int S_DW = SCM == SCM_STAGE ? ((TW ? KT * BN / 4 : BN * SD) + 64 * NW - 1) / (64 * NW) * (64 * NW)
                                                : SCM == SCM_BYTE ? BN * KT : 64;
-  static constexpr int SA_DW = (BM * SD + 63) / 64 * 64;  // activation scale dwords
+  // FP4 activation scales of a stage: row-major rows' SD dwords each, or (SBM: the down product,
+  // whose tile rows are consecutive rows of h) per block the SW aligned dwords that cover the
+  // tile's BM bytes of that block's row of the block-major array
+  static constexpr bool SBM = AFP4 && MODE == MODE_DOWN;
+  static constexpr int SW = BM / 4 + 1;
+  static constexpr int SA_DW = ((SBM ? KT * SW : BM * SD) + 63) / 64 * 64;  // activation scale dwords
   // resident scales: region 1 (up rows of gate_up) starts at dword R1; whole instructions
   static constexpr int R1 = (BNH * kResidentNb + 8) / 4;
   static constexpr int RS_DW = ((TW ? kResidentNb * BN / 4 : SWIGLU ? 2 * R1 : (BN * kResidentNb + 8) / 4) + 63) / 64 * 64;
@@ -387,7 +394,7 @@ __device__ __forceinline__ void gemm_tile(
   const int n_valid = min(BM, row_end - r0);                      // tile rows of this expert
   const i32x4 rA = make_res(p.A, p.a_rows * (AFP4 ? (K >> 1) : K * 2));
   // activation scales live in the library's workspace, padded past a whole dword
-  const i32x4 rSA = make_res(p.Asc, AFP4 ? (p.a_rows * nb + 3) / 4 * 4 : 0);
+  const i32x4 rSA = make_res(p.Asc, !AFP4 ? 0 : LD::SBM ? (int64_t)nb * p.sc_pitch : (p.a_rows * nb + 3) / 4 * 4);
   uint32_t voffB[IB];
   int bblk[IB];
 #pragma unroll
@@ -553,21 +560,27 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
   for (int q = 0; q < ISA; ++q) {
     const int idx = PSA::instr(wave, q) * 64 + lane;
-    voffSA[q] = idx < n_valid * SD
-                    ? (((uint32_t)sArow[idx / SD] * (uint32_t)nb) & ~3u) + 4 * (idx % SD)
-                    : kOutOfRange;
+    if constexpr (LD::SBM)  // block j of the stage: dwords d of the window over rows r0 ..
+      voffSA[q] = idx < KT * LD::SW ? (uint32_t)(idx / LD::SW) * (uint32_t)p.sc_pitch +
+                                          ((uint32_t)r0 & ~3u) + 4u * (uint32_t)(idx % LD::SW)
+                                    : kOutOfRange;
+    else
+      voffSA[q] = idx < n_valid * SD
+                      ? (((uint32_t)sArow[idx / SD] * (uint32_t)nb) & ~3u) + 4 * (idx % SD)
+                      : kOutOfRange;
   }
   int ash[AFP4 ? FM : 1];  // FP4 A: byte of block 0 of each fragment row's scales
 #pragma unroll
   for (int i = 0; i < (AFP4 ? FM : 0); ++i) {
     const int r = wm * TM + i * MF + ln;
-    ash[i] = r * SD * 4 + (int)(((uint32_t)sArow[r] * (uint32_t)nb) & 3u);
+    if constexpr (LD::SBM) ash[i] = (r0 & 3) + r;
+    else ash[i] = r * SD * 4 + (int)(((uint32_t)sArow[r] * (uint32_t)nb) & 3u);
   }
   auto issue_a = [&](Stage& sg, int kt) {
     const int kb = kt * KT;
 #pragma unroll
     for (int q = 0; q < ISA; ++q)
-      dma_b32(rSA, off_add(voffSA[q], (uint32_t)kb), 0,
+      dma_b32(rSA, off_add(voffSA[q], LD::SBM ? (uint32_t)kb * (uint32_t)p.sc_pitch : (uint32_t)kb), 0,
               &sg.Sa[PSA::instr(wave, q) * 64]);
     constexpr int A_KB = AFP4 ? 16 : 64;  // bytes of A per 32-element block
     auto load_a = [&](uint32_t voff, const void* lds) {
@@ -637,7 +650,7 @@ __device__ __forceinline__ void gemm_tile(
         for (int i = 0; i < FL; ++i) {
           const int r = wm * TM + i * MF + ln;
           a[i] = lds_read_b128(As + r * A_ROW + (((LG * j + g) ^ swz_rows<ACH>(r)) << 4));
-          sca[i] = past ? 127u : (uint32_t)Sab[ash[i] + LG * j + g];
+          sca[i] = past ? 127u : (uint32_t)Sab[ash[i] + (LG * j + g) * (LD::SBM ? 4 * LD::SW : 1)];
         }
 #pragma unroll
         for (int f = 0; f < FN; ++f)
@@ -805,7 +818,7 @@ __device__ __forceinline__ void gemm_tile(
         uint32_t q[4];
         const uint32_t sb = quantize_block32_bf16(w, q);
         *reinterpret_cast<uint4*>(hq + (int64_t)r * (p.F >> 1) + (col >> 1)) = make_uint4(q[0], q[1], q[2], q[3]);
-        p.out_scales[(int64_t)r * (p.F >> 5) + (col >> 5)] = (uint8_t)sb;
+        p.out_scales[(int64_t)(col >> 5) * p.sc_pitch + r] = (uint8_t)sb;  // block-major
       }
     } else {
       uint16_t* h = reinterpret_cast<uint16_t*>(p.out);
@@ -930,6 +943,7 @@ GemmKArgs gate_up_args(const MoeGemmArgs& m) {
   g.rows_total = m.T * m.k;
   g.F = m.F;
   g.out = m.h;
+  g.sc_pitch = m.hqs_pitch;
   if (m.act_custom) {
     g.act_custom = 1;
     g.bias = m.gu_bias;
@@ -959,6 +973,7 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
   d.rows_total = m.T * m.k;
   d.F = m.F;
   d.out = m.y;
+  d.sc_pitch = m.hqs_pitch;
   return d;
 }
 

@@ -87,9 +87,11 @@ struct MoeGemmArgs {
   float* y;                  // [P][H] fp32 workspace
   void* out;                 // [T][H]
   bool out_bf16;
-  // activation variant: x and h MXFP4-quantized (packed [rows][K/2], scales [rows][K/32])
+  // activation variant: x and h MXFP4-quantized (packed [rows][K/2]; x's scales [T][H/32], h's
+  // block-major [F/32][hqs_pitch], hqs_pitch = T*k rounded up to a multiple of 4)
   bool mx_act;
   uint8_t *xq, *xqs, *hq, *hqs;
+  int64_t hqs_pitch;
   // expert weights in the tiled layout (codes [E][R/16][K/32][16][16], scales [E][K/32][R])
   bool tiled;
   // expert activation: act_custom = 0 is the plain SwiGLU (the rest unused); else biases (NULL =
