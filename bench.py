@@ -506,8 +506,8 @@ def summarize_traffic(workload, bench_json, commands):
     kern = json.load(open(bench_json)).get("kernels", {})
     any_k = next(iter(ent.values()))
     out = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE): %s" % workload, "",
-           "Commands (rocprofv3 output under gpurun_out/; the profiler runs from /tmp with "
-           "TMPDIR=/tmp, REPO is the repository root):", "", "```"] + list(commands) + [
+           "Commands (the profiler runs from /tmp with TMPDIR=/tmp and writes under the -d "
+           "directory; REPO is the repository root):", "", "```"] + list(commands) + [
            "```", "",
            "`--calibrate-copy` appends a 1 GiB elementwise copy (reads 1 GiB, writes 1 GiB); its "
            "counters give the scale factors: fetch KiB x %.4f, write KiB x %.4f. Averages over "
@@ -544,8 +544,8 @@ def summarize_mfma(pmc_dir, command, title):
             d = disp.setdefault((f, r["Dispatch_Id"]), {"name": r["Kernel_Name"],
                                                         "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    out = ["# %s" % title, "", "Command (from the repository root, rocprofv3 output under "
-           "gpurun_out/):", "", "```", command, "```", "",
+    out = ["# %s" % title, "", "Command (run from /tmp with TMPDIR=/tmp, output under the -d "
+           "directory; REPO is the repository root):", "", "```", command, "```", "",
            "Per-dispatch averages. GRBM_GUI_ACTIVE is summed over the 8 XCDs (cycles per XCD over "
            "the dispatch time = the clock the chip held); SQ_VALU_MFMA_BUSY_CYCLES over the 1 024 "
            "SIMDs (busy cycles per SIMD over the cycles = the share of cycles the matrix pipes were "
@@ -579,8 +579,8 @@ def summarize_trace(trace_dir, command, title, bench_json=None):
         raise SystemExit("no kernel_stats.csv under %s" % trace_dir)
     rows = list(csv.DictReader(open(files[0])))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
-    out = ["# %s" % title, "", "Command (from the repository root, rocprofv3 output under "
-           "gpurun_out/):", "", "```", command, "```", "",
+    out = ["# %s" % title, "", "Command (run from /tmp with TMPDIR=/tmp, output under the -d "
+           "directory; REPO is the repository root):", "", "```", command, "```", "",
            "| kernel | calls | avg us | min us | max us | share % |",
            "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
