@@ -473,10 +473,14 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
     ck = max(copy_k, key=lambda k: fetch[k])
     f_fetch = copy_bytes / (fetch[ck] * 1024.0)
     f_write = copy_bytes / (write[ck] * 1024.0)
-    # kind -> kernel symbols of one launch of it (the router is two kernels)
+    # kind -> kernel symbols of one launch of it (the router is two kernels: the 64-token tile
+    # kernel or the spread logits kernel, then the selection; the set-up's routing of every batch,
+    # outside the timed region, runs the logits kernel's selecting form, which is left out)
+    router = (["route_tile_kernel"] if any("route_tile_kernel" in k for k in fetch)
+              else ["route_logits_kernel<false"])
     kinds = {"moe_gate_up_swiglu": ["moe_gate_up_swiglu_kernel"],
              "moe_down_weighted": ["moe_down_weighted_kernel"], "moe_combine": ["combine_kernel"],
-             "route_topk": ["route_logits_kernel", "route_select_kernel"],
+             "route_topk": router + ["route_select_kernel"],
              "permute": ["permute_kernel"], "linear": ["linear_kernel"],
              "quantize": ["quantize_kernel"], "moe_single_launch": ["moe_single_launch_kernel"]}
     out = {}
