@@ -12,6 +12,10 @@ timed on a bounded sample of the same workload.
 
 Decode-shaped workloads rotate through several copies of the weights (and several token
 batches) so the working set exceeds the 256 MB Infinity Cache and every step reads HBM.
+
+The default run (the prefill layer) also times the 20B-shaped decode layer (T = 64) in the same
+process and adds it to the line as ``decode`` (the metric's decode HBM GB/s half); --no-decode
+leaves it out.
 """
 from __future__ import annotations
 
@@ -300,6 +304,32 @@ def bench_moe(args, name, shape, flags):
         result["cpu_baseline"] = cpu_baseline_moe(args, s, x_all[:s.T], wr_np, br_np, host_w,
                                                   mxact)
     return result
+
+
+DECODE_WORKLOAD = "moe-20b-decode-T64"
+
+
+def decode_summary(args, wl):
+    """The decode-shaped 20B layer (T = 64, every step reading its weights from HBM) timed the same
+    way as the main workload, reduced to its HBM figures: the whole step's algorithmic bytes per
+    second and the dominant kernel's (the gate_up product's weight stream)."""
+    import copy
+    _, cfg, flags = wl[DECODE_WORKLOAD]
+    sub = copy.copy(args)
+    sub.no_cpu_baseline = True
+    sub.graph = False
+    r = bench_moe(sub, DECODE_WORKLOAD, cfg, flags)
+    st, rf = r["step"], r["roofline"]
+    return {"workload": DECODE_WORKLOAD, "ms_per_step": r["ms_per_step"],
+            "tokens_per_s": r["value"], "steps": r["steps"],
+            "weight_copies": r["config"]["weight_copies"],
+            "token_batches": r["config"]["token_batches"],
+            "step_hbm_gbs_algorithmic": st["hbm_gbs_algorithmic"],
+            "step_frac_of_hbm_peak": st["frac"],
+            "dominant_kernel": rf["kernel"], "kernel_avg_ms": rf["avg_ms"],
+            "kernel_gbs_algorithmic": rf["achieved"], "kernel_frac_of_hbm_peak": rf["frac"],
+            "kernel_traffic_bytes": rf["traffic"],
+            "kernels": r["kernels"]}
 
 
 def settle_clocks(step, settle_ms):
@@ -622,6 +652,8 @@ def main():
                     help="untimed steps for this long before the warm-up steps (clock settling)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="default workload only: leave out the decode layer's line")
     ap.add_argument("--graph", action="store_true",
                     help="replay the steps from a HIP graph instead of launching them one by one")
     ap.add_argument("--row-major-weights", action="store_true",
@@ -682,6 +714,8 @@ def main():
     kind, cfg, flags = wl[args.workload]
     if kind == "moe":
         res = bench_moe(args, args.workload, cfg, flags)
+        if args.workload == DEFAULT_WORKLOAD and not args.no_decode:
+            res["decode"] = decode_summary(args, wl)
     else:
         res = bench_linear(args, args.workload, cfg)
     if args.calibrate_copy:

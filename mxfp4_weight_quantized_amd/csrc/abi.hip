@@ -16,6 +16,7 @@
 #include "mx_launch.h"
 
 #define MX_API extern "C" __attribute__((visibility("default")))
+static_assert(MX_MAX_TOPK <= 8 && MX_MAX_MOE_DIM <= 3072, "combine launch: k <= 8, H / 8 <= 384 threads");
 
 namespace {
 

@@ -75,6 +75,89 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   combine8<BF16_OUT>(Y, inv, w, (int)(i8 / h8), (int)(i8 % h8) * 8, H, k, T * k, out, idx, bias);
 }
 
+// The combine with one workgroup per token (the per-step path): the token's KK (row, weight) pairs
+// are the same for the whole workgroup, so they come through the scalar cache and the vector
+// memory path carries only the rows. Each thread takes 8 columns and issues the loads of all KK
+// rows before summing. The arithmetic is combine8's (each product w * Y, or w * (Y + bias),
+// rounded to fp32, then added in slot order), so both give the same bits: a pair whose row index
+// lies outside [0, P) (a skipped routing index) reads row 0 and adds +0 instead of its product,
+// which leaves the sum unchanged (it starts at +0 and cannot become -0).
+constexpr int kCombineThreads = 384;  // 8 columns per thread: H <= 3072
+constexpr int kMaxTopK = 8;           // experts per token (the C ABI's limit)
+template <bool BF16_OUT, int KK>
+__global__ __launch_bounds__(kCombineThreads) void combine_token_kernel(
+    const float* __restrict__ Y, const int32_t* __restrict__ inv, const float* __restrict__ w,
+    int H, int P, void* __restrict__ out, const int32_t* __restrict__ idx,
+    const float* __restrict__ bias) {
+#pragma clang fp contract(off)  // each product rounded before it is added (no fused multiply-add)
+  const int64_t t = blockIdx.x;
+  const int c = threadIdx.x * 8;
+  if (c >= H) return;
+  int r[KK];
+  bool ok[KK];
+  float wj[KK];
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+    const int rr = inv[t * KK + j];
+    ok[j] = rr >= 0 && rr < P;
+    r[j] = ok[j] ? rr : 0;
+    wj[j] = w[t * KK + j];
+  }
+  f32x4 v0[KK], v1[KK];
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+    v0[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r[j] * H + c));
+    v1[j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Y + (int64_t)r[j] * H + c + 4));
+  }
+  if (bias != nullptr) {
+#pragma unroll
+    for (int j = 0; j < KK; ++j) {
+      const float* bb = bias + (int64_t)(ok[j] ? idx[t * KK + j] : 0) * H + c;
+      v0[j] += *reinterpret_cast<const f32x4*>(bb);
+      v1[j] += *reinterpret_cast<const f32x4*>(bb + 4);
+    }
+  }
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < KK; ++j) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s[u] += ok[j] ? __fmul_rn(v0[j][u], wj[j]) : 0.f;
+      s[4 + u] += ok[j] ? __fmul_rn(v1[j][u], wj[j]) : 0.f;
+    }
+  }
+  if (BF16_OUT) {
+    uint32_t q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = f32_to_bf16_bits(s[2 * u]) | (f32_to_bf16_bits(s[2 * u + 1]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out) + t * H + c) = make_uint4(q[0], q[1], q[2], q[3]);
+  } else {
+    float* o = reinterpret_cast<float*>(out) + t * H + c;
+    *reinterpret_cast<float4*>(o) = make_float4(s[0], s[1], s[2], s[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(s[4], s[5], s[6], s[7]);
+  }
+}
+
+template <bool BF16_OUT, int KK>
+void launch_combine_k(const MoeGemmArgs& m, const float* bias, hipStream_t stream) {
+  const int threads = (m.H / 8 + 63) / 64 * 64;
+  hipLaunchKernelGGL((combine_token_kernel<BF16_OUT, KK>), dim3(m.T), dim3(threads), 0, stream,
+                     m.y, m.inv, m.topk_w, m.H, m.T * m.k, m.out, m.topk_idx, bias);
+}
+template <bool BF16_OUT>
+void launch_combine(const MoeGemmArgs& m, const float* bias, hipStream_t stream) {
+  switch (m.k) {
+    case 1: launch_combine_k<BF16_OUT, 1>(m, bias, stream); break;
+    case 2: launch_combine_k<BF16_OUT, 2>(m, bias, stream); break;
+    case 3: launch_combine_k<BF16_OUT, 3>(m, bias, stream); break;
+    case 4: launch_combine_k<BF16_OUT, 4>(m, bias, stream); break;
+    case 5: launch_combine_k<BF16_OUT, 5>(m, bias, stream); break;
+    case 6: launch_combine_k<BF16_OUT, 6>(m, bias, stream); break;
+    case 7: launch_combine_k<BF16_OUT, 7>(m, bias, stream); break;
+    default: launch_combine_k<BF16_OUT, kMaxTopK>(m, bias, stream); break;
+  }
+}
+
 // Split linear: out[i] = sum over z of part[z * n + i], in split order, as fp32 or bf16.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int S,
@@ -232,15 +315,9 @@ hipError_t launch_moe_down(const MoeGemmArgs& m, hipStream_t stream) {
 }
 
 hipError_t launch_moe_combine(const MoeGemmArgs& m, hipStream_t stream) {
-  const int64_t n8 = (int64_t)m.T * (m.H / 8);
-  const unsigned grid = (unsigned)((n8 + 255) / 256);
   const float* bias = m.act_custom ? m.dn_bias : nullptr;
-  if (m.out_bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(grid), dim3(256), 0, stream, m.y, m.inv,
-                       m.topk_w, m.T, m.H, m.k, m.out, m.topk_idx, bias);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(grid), dim3(256), 0, stream, m.y, m.inv,
-                       m.topk_w, m.T, m.H, m.k, m.out, m.topk_idx, bias);
+  if (m.out_bf16) launch_combine<true>(m, bias, stream);
+  else launch_combine<false>(m, bias, stream);
   return hipGetLastError();
 }
 

@@ -877,6 +877,7 @@ __device__ __forceinline__ void combine8(const float* __restrict__ Y, const int3
                                          int P, void* __restrict__ out,
                                          const int32_t* __restrict__ idx,
                                          const float* __restrict__ bias) {
+#pragma clang fp contract(off)  // each product rounded before it is added (no fused multiply-add)
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const int r = ld_int<COH>(inv + (int64_t)t * k + j);
