@@ -509,7 +509,7 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
     router = (["route_tile_kernel"] if any("route_tile_kernel" in k for k in fetch)
               else ["route_logits_kernel<false"])
     kinds = {"moe_gate_up_swiglu": ["moe_gate_up_swiglu_kernel"],
-             "moe_down_weighted": ["moe_down_weighted_kernel"], "moe_combine": ["combine_kernel"],
+             "moe_down_weighted": ["moe_down_weighted_kernel"], "moe_combine": ["combine_token_kernel"],
              "route_topk": router + ["route_select_kernel"],
              "permute": ["permute_kernel"], "linear": ["linear_kernel"],
              "quantize": ["quantize_kernel"], "moe_single_launch": ["moe_single_launch_kernel"]}
@@ -627,7 +627,7 @@ def summarize_trace(trace_dir, command, title, bench_json=None):
         roof = b.get("roofline", {})
         dom = roof.get("kernel")
         sym = {"moe_gate_up_swiglu": "moe_gate_up_swiglu_kernel", "moe_down_weighted":
-               "moe_down_weighted_kernel", "moe_combine": "combine_kernel", "linear": "linear_kernel",
+               "moe_down_weighted_kernel", "moe_combine": "combine_token_kernel", "linear": "linear_kernel",
                "moe_single_launch": "moe_single_launch_kernel"}
         tr = [r for r in rows if sym.get(dom, "?") in r["Name"]]
         out += ["", "The traced bench.py run's own line: %.4f ms per step; dominant kernel `%s` "

@@ -61,20 +61,6 @@ template <int BM, int BN, int WM, int WN, int KT, int ST, int GM, int OCC, bool 
 __global__ __launch_bounds__(WM * WN * 64, (OCC * WM * WN + 3) / 4) void linear_kernel(GemmKArgs p) {
   gemm_body<BM, BN, WM, WN, KT, ST, MODE_LINEAR, GM, AFP4, SCM, false, MF>(p);
 }
-// The combine, one thread per token and 8 columns (combine8).
-template <bool BF16_OUT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
-                                                      const int32_t* __restrict__ inv,
-                                                      const float* __restrict__ w, int T, int H,
-                                                      int k, void* __restrict__ out,
-                                                      const int32_t* __restrict__ idx,
-                                                      const float* __restrict__ bias) {
-  const int64_t i8 = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int h8 = H >> 3;
-  if (i8 >= (int64_t)T * h8) return;
-  combine8<BF16_OUT>(Y, inv, w, (int)(i8 / h8), (int)(i8 % h8) * 8, H, k, T * k, out, idx, bias);
-}
-
 // The combine with one workgroup per token (the per-step path): the token's KK (row, weight) pairs
 // are the same for the whole workgroup, so they come through the scalar cache and the vector
 // memory path carries only the rows. Each thread takes 8 columns and issues the loads of all KK
