@@ -151,7 +151,7 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
   L.y = take(P * (size_t)d.H * 4);
   if (d.flags & MX_ACT_MXFP4) {
     L.xq = take(T * (size_t)d.H / 2);
-    L.xqs = take(T * (size_t)d.H / 32);
+    L.xqs = take((P + 3) / 4 * 4 * (size_t)d.H / 32);  // block-major [H/32][P rounded up to 4]
     L.hq = take(P * (size_t)d.F / 2);
     L.hqs = take((P + 3) / 4 * 4 * (size_t)d.F / 32);  // block-major [F/32][P rounded up to 4]
   }
@@ -514,10 +514,12 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   if (e != hipSuccess) return hip_fail(e, "permute launch");
   const bool mx_act = (d.flags & MX_ACT_MXFP4) != 0;
   if (mx_act) {
-    // activation variant: x quantized along H in 32-blocks (the same rule as the weights)
+    // activation variant: x quantized along H in 32-blocks (the same rule as the weights); the
+    // scale bytes go block-major to every pair of their token (the gate_up stages' layout)
     ProfScope ps(PK_QUANTIZE, s);
-    e = mx::launch_quantize(d.x, true, (int64_t)d.T * (d.H / 32), reinterpret_cast<uint8_t*>(w + L.xq),
-                            reinterpret_cast<uint8_t*>(w + L.xqs), s);
+    e = mx::launch_quantize_x_pairs(d.x, d.T, d.H, inv, d.k, ((int64_t)d.T * d.k + 3) / 4 * 4,
+                                    reinterpret_cast<uint8_t*>(w + L.xq),
+                                    reinterpret_cast<uint8_t*>(w + L.xqs), s);
     if (e != hipSuccess) return hip_fail(e, "x quantize launch");
   }
   const mx::MoeGemmArgs g = gemm_args(d, L, w, idx, tw);

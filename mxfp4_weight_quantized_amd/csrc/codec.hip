@@ -55,6 +55,37 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   scales[blk] = (uint8_t)sb;
 }
 
+// The MoE MLP's activation variant: x [T][H] bf16 quantized along H (one thread per block, as
+// above), codes in token order, and each block's scale byte written to every pair of its token
+// that the permutation kept, block-major in pair order: scales_bm[b * pitch + inv[t * k + j]].
+// The grouped GEMM's stages then load a tile's scale bytes as one contiguous run per block, where
+// the rows of a tile (consecutive pairs) belong to scattered tokens.
+__global__ __launch_bounds__(256) void quantize_x_pairs_kernel(const uint16_t* __restrict__ x,
+                                                               int64_t nblocks, int nb,
+                                                               const int32_t* __restrict__ inv,
+                                                               int k, int P, int64_t pitch,
+                                                               uint8_t* __restrict__ packed,
+                                                               uint8_t* __restrict__ scales_bm) {
+  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= nblocks) return;
+  const uint2* src = reinterpret_cast<const uint2*>(x + blk * 32);
+  uint32_t w[16], q[4];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const uint2 d = src[v];
+    w[2 * v] = d.x;
+    w[2 * v + 1] = d.y;
+  }
+  const uint32_t sb = quantize_block32_bf16(w, q);
+  *reinterpret_cast<uint4*>(packed + blk * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+  const int64_t t = blk / nb;
+  const int b = (int)(blk - t * nb);
+  for (int j = 0; j < k; ++j) {
+    const int r = inv[t * k + j];
+    if (r >= 0 && r < P) scales_bm[b * pitch + r] = (uint8_t)sb;
+  }
+}
+
 // fp32 bit pattern of E2M1 code c times 2^(b-127), built field by field.
 __device__ __forceinline__ uint32_t decode_f32_bits(uint32_t c, uint32_t b) {
   const uint32_t sign = (c & 8u) << 28;
@@ -125,6 +156,16 @@ __global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restr
 }
 
 }  // namespace
+
+hipError_t launch_quantize_x_pairs(const uint16_t* x, int T, int H, const int32_t* inv, int k,
+                                   int64_t pitch, uint8_t* packed, uint8_t* scales_bm,
+                                   hipStream_t stream) {
+  const int64_t nblocks = (int64_t)T * (H / 32);
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_x_pairs_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
+                     stream, x, nblocks, H / 32, inv, k, T * k, pitch, packed, scales_bm);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8_t* packed,
                            uint8_t* scales, hipStream_t stream) {

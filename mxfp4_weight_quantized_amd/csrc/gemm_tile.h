@@ -296,10 +296,12 @@ struct GemmLds {
   // (stage scale dwords padded to a whole number of instructions per wave: no repeated loads)
   static constexpr int S_DW = SCM == SCM_STAGE ? ((TW ? KT * BN / 4 : BN * SD) + 64 * NW - 1) / (64 * NW) * (64 * NW)
                                                : SCM == SCM_BYTE ? BN * KT : 64;
-  // FP4 activation scales of a stage: row-major rows' SD dwords each, or (SBM: the down product,
-  // whose tile rows are consecutive rows of h) per block the SW aligned dwords that cover the
-  // tile's BM bytes of that block's row of the block-major array
-  static constexpr bool SBM = AFP4 && MODE == MODE_DOWN;
+  // FP4 activation scales of a stage: row-major rows' SD dwords each (the dense linear), or (SBM:
+  // the MoE products, whose tile rows are consecutive pairs; the gate_up epilogue writes h's
+  // scales block-major in pair order, and the x quantizer writes x's so for every pair of each
+  // token) per block the SW aligned dwords that cover the tile's BM bytes of that block's row of
+  // the block-major array
+  static constexpr bool SBM = AFP4 && MODE != MODE_LINEAR;
   static constexpr int SW = BM / 4 + 1;
   static constexpr int SA_DW = ((SBM ? KT * SW : BM * SD) + 63) / 64 * 64;  // activation scale dwords
   // resident scales: region 1 (up rows of gate_up) starts at dword R1; whole instructions

@@ -10,6 +10,12 @@ namespace mx {
 // codec.hip
 hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8_t* packed,
                            uint8_t* scales, hipStream_t stream);
+// x [T][H] bf16 quantized along H for the MoE MLP's activation variant: codes [T][H/2] in token
+// order, scale bytes block-major in pair order ([H/32][pitch], pitch >= T * k): the scale of
+// (token t, block b) at b * pitch + inv[t * k + j] for every slot j whose inv is in [0, T * k).
+hipError_t launch_quantize_x_pairs(const uint16_t* x, int T, int H, const int32_t* inv, int k,
+                                   int64_t pitch, uint8_t* packed, uint8_t* scales_bm,
+                                   hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t nblocks,
                              void* dst, bool bf16_out, hipStream_t stream);
 // G matrices [R][K] (R % 16 == 0, K % 32 == 0) into the tiled layout of the grouped GEMMs;
