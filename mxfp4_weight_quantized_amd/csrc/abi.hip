@@ -115,7 +115,8 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // ---- mxfp4_moe_mlp workspace layout ----
 struct MoeLayout {
-  size_t status, logits, idx, w, offsets, perm, inv, tiles, pcounts, rpart, tile_ends, h, y, xq, xqs, hq, hqs,
+  size_t status, logits, idx, w, offsets, perm, inv, tiles, pcounts, rpart, tile_ends, h, y, xq, xq_tok, xqs_tok, xqs,
+      hq, hqs,
       total;
   size_t pcounts_bytes;
   int tile_rows, max_tiles;
@@ -150,9 +151,16 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
   L.h = (d.flags & MX_ACT_MXFP4) ? 0 : take(P * (size_t)d.F * 2);
   L.y = take(P * (size_t)d.H * 4);
   if (d.flags & MX_ACT_MXFP4) {
-    L.xq = take(T * (size_t)d.H / 2);
+    // scales block-major in pair order; codes: prefill-shaped calls take x in token order, then
+    // x and h in pair order tiled by 16 rows ([P/16][K/32][16][16]); decode-shaped calls x in
+    // token order and h in pair order, row-major
+    const bool pre = L.tile_rows != 16;
+    const size_t P16 = (P + 15) / 16 * 16;
+    L.xq = take((pre ? P16 : T) * (size_t)d.H / 2);
+    L.xq_tok = pre ? take(T * (size_t)d.H / 2) : 0;
+    L.xqs_tok = pre ? take(T * (size_t)d.H / 32) : 0;
     L.xqs = take((P + 3) / 4 * 4 * (size_t)d.H / 32);  // block-major [H/32][P rounded up to 4]
-    L.hq = take(P * (size_t)d.F / 2);
+    L.hq = take((pre ? P16 : P) * (size_t)d.F / 2);
     L.hqs = take((P + 3) / 4 * 4 * (size_t)d.F / 32);  // block-major [F/32][P rounded up to 4]
   }
   L.total = off;
@@ -514,12 +522,22 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   if (e != hipSuccess) return hip_fail(e, "permute launch");
   const bool mx_act = (d.flags & MX_ACT_MXFP4) != 0;
   if (mx_act) {
-    // activation variant: x quantized along H in 32-blocks (the same rule as the weights); the
-    // scale bytes go block-major to every pair of their token (the gate_up stages' layout)
+    // activation variant: x quantized along H in 32-blocks (the same rule as the weights), its
+    // scales block-major in pair order; prefill-shaped calls then copy the codes into pair
+    // order, tiled (the layouts the gate_up stages read)
     ProfScope ps(PK_QUANTIZE, s);
-    e = mx::launch_quantize_x_pairs(d.x, d.T, d.H, inv, d.k, ((int64_t)d.T * d.k + 3) / 4 * 4,
-                                    reinterpret_cast<uint8_t*>(w + L.xq),
-                                    reinterpret_cast<uint8_t*>(w + L.xqs), s);
+    const int64_t pitch = ((int64_t)d.T * d.k + 3) / 4 * 4;
+    uint8_t* xq = reinterpret_cast<uint8_t*>(w + L.xq);
+    uint8_t* xqs = reinterpret_cast<uint8_t*>(w + L.xqs);
+    if (L.tile_rows != 16) {
+      uint8_t* xq_tok = reinterpret_cast<uint8_t*>(w + L.xq_tok);
+      uint8_t* xs_tok = reinterpret_cast<uint8_t*>(w + L.xqs_tok);
+      e = mx::launch_quantize(d.x, true, (int64_t)d.T * (d.H / 32), xq_tok, xs_tok, s);
+      if (e == hipSuccess)
+        e = mx::launch_x_pair_copy(xq_tok, xs_tok, d.H, perm, d.k, d.T * d.k, pitch, xq, xqs, s);
+    } else {
+      e = mx::launch_quantize_x_scatter(d.x, d.T, d.H, inv, d.k, pitch, xq, xqs, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "x quantize launch");
   }
   const mx::MoeGemmArgs g = gemm_args(d, L, w, idx, tw);

@@ -55,17 +55,17 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   scales[blk] = (uint8_t)sb;
 }
 
-// The MoE MLP's activation variant: x [T][H] bf16 quantized along H (one thread per block, as
-// above), codes in token order, and each block's scale byte written to every pair of its token
-// that the permutation kept, block-major in pair order: scales_bm[b * pitch + inv[t * k + j]].
-// The grouped GEMM's stages then load a tile's scale bytes as one contiguous run per block, where
-// the rows of a tile (consecutive pairs) belong to scattered tokens.
-__global__ __launch_bounds__(256) void quantize_x_pairs_kernel(const uint16_t* __restrict__ x,
-                                                               int64_t nblocks, int nb,
-                                                               const int32_t* __restrict__ inv,
-                                                               int k, int P, int64_t pitch,
-                                                               uint8_t* __restrict__ packed,
-                                                               uint8_t* __restrict__ scales_bm) {
+// The MoE MLP's activation variant, decode-shaped calls: x [T][H] bf16 quantized along H (one
+// thread per block, as above), codes in token order (the GEMM gathers their rows), and each
+// block's scale byte written to every pair of its token that the permutation kept, block-major
+// in pair order: scales_bm[b * pitch + inv[t * k + j]]. A stage's scale loads are then one
+// contiguous run per block, where the rows of a tile (consecutive pairs) are scattered tokens.
+__global__ __launch_bounds__(256) void quantize_x_scatter_kernel(const uint16_t* __restrict__ x,
+                                                                 int64_t nblocks, int nb,
+                                                                 const int32_t* __restrict__ inv,
+                                                                 int k, int P, int64_t pitch,
+                                                                 uint8_t* __restrict__ packed,
+                                                                 uint8_t* __restrict__ scales_bm) {
   const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (blk >= nblocks) return;
   const uint2* src = reinterpret_cast<const uint2*>(x + blk * 32);
@@ -84,6 +84,30 @@ __global__ __launch_bounds__(256) void quantize_x_pairs_kernel(const uint16_t* _
     const int r = inv[t * k + j];
     if (r >= 0 && r < P) scales_bm[b * pitch + r] = (uint8_t)sb;
   }
+}
+
+// Prefill-shaped calls: x's codes and scales, quantized in token order ([T][nb] blocks), copied
+// into pair order in the layout the prefill GEMM stages read: for pair row p (token perm[p] / k)
+// and block b, the 16 code bytes at ((p / 16) * nb + b) * 256 + (p % 16) * 16 (block b of 16
+// consecutive pairs as one 256-byte run) and the scale byte at b * pitch + p. One thread per
+// (pair, block), consecutive threads on consecutive pairs of one block: whole runs stored, the
+// packed token rows read k times (a quarter of the bytes of re-reading x).
+__global__ __launch_bounds__(256) void x_pair_copy_kernel(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales,
+                                                          int nb, const int32_t* __restrict__ perm,
+                                                          int k, int P, int64_t pitch,
+                                                          uint8_t* __restrict__ packed,
+                                                          uint8_t* __restrict__ scales_bm) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t g = i / (16 * nb);
+  const int rem = (int)(i - g * 16 * nb);
+  const int b = rem >> 4;
+  const int64_t pr = g * 16 + (rem & 15);
+  if (pr >= P) return;
+  const int64_t tb = (int64_t)(perm[pr] / k) * nb + b;
+  *reinterpret_cast<uint4*>(packed + (g * nb + b) * 256 + (rem & 15) * 16) =
+      *reinterpret_cast<const uint4*>(codes + tb * 16);
+  scales_bm[b * pitch + pr] = scales[tb];
 }
 
 // fp32 bit pattern of E2M1 code c times 2^(b-127), built field by field.
@@ -157,13 +181,23 @@ __global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restr
 
 }  // namespace
 
-hipError_t launch_quantize_x_pairs(const uint16_t* x, int T, int H, const int32_t* inv, int k,
-                                   int64_t pitch, uint8_t* packed, uint8_t* scales_bm,
-                                   hipStream_t stream) {
+hipError_t launch_quantize_x_scatter(const uint16_t* x, int T, int H, const int32_t* inv, int k,
+                                     int64_t pitch, uint8_t* packed, uint8_t* scales_bm,
+                                     hipStream_t stream) {
   const int64_t nblocks = (int64_t)T * (H / 32);
   if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_x_pairs_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0,
-                     stream, x, nblocks, H / 32, inv, k, T * k, pitch, packed, scales_bm);
+  hipLaunchKernelGGL(quantize_x_scatter_kernel, dim3((unsigned)((nblocks + 255) / 256)), dim3(256),
+                     0, stream, x, nblocks, H / 32, inv, k, T * k, pitch, packed, scales_bm);
+  return hipGetLastError();
+}
+
+hipError_t launch_x_pair_copy(const uint8_t* codes, const uint8_t* scales, int H,
+                              const int32_t* perm, int k, int P, int64_t pitch, uint8_t* packed,
+                              uint8_t* scales_bm, hipStream_t stream) {
+  const int64_t n = (int64_t)(P + 15) / 16 * 16 * (H / 32);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(x_pair_copy_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     codes, scales, H / 32, perm, k, P, pitch, packed, scales_bm);
   return hipGetLastError();
 }
 

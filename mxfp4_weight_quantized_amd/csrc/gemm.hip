@@ -259,6 +259,10 @@ hipError_t gate_up_tw(GemmKArgs g, const MoeGemmArgs& m, hipStream_t stream) {
   const bool pre = use_prefill_tiles(m.T, m.k, m.E);
   if (m.mx_act) {
     g.A = reinterpret_cast<const uint16_t*>(m.xq);  // packed codes, addressed in bytes
+    if (pre) {  // prefill tiles: x's codes already in pair order (tiled), no gather
+      g.a_gather = nullptr;
+      g.a_rows = (int64_t)m.T * m.k;
+    }
     g.Asc = m.xqs;
     g.out = m.hq;  // h leaves the epilogue quantized
     g.out_scales = m.hqs;

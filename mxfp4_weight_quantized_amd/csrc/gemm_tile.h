@@ -34,11 +34,13 @@ enum { SCM_BYTE = 0, SCM_STAGE = 1, SCM_RESIDENT = 2 };  // how weight scales re
 constexpr int kResidentNb = 96;  // resident scales hold up to K = 3072 (32-blocks per row)
 
 struct GemmKArgs {
-  const uint16_t* A;          // bf16 activation rows of length K
+  const uint16_t* A;          // bf16 activation rows of length K; MXFP4 codes: [a_rows][K/2] in
+                              // the dense linear, tiled in pair order [a_rows/16][K/32][16][16]
+                              // in the MoE products
   int64_t a_rows;             // rows in A (bounds the buffer view of A)
-  const uint8_t* Asc;         // A scales when A is MXFP4 (else unused): [a_rows][K/32], or in the
-                              // down product block-major [K/32][sc_pitch]
-  int64_t sc_pitch;           // FP4 h scales, block-major (gate_up writes them, down reads them)
+  const uint8_t* Asc;         // A scales when A is MXFP4 (else unused): [a_rows][K/32] in the
+                              // linear, block-major in pair order [K/32][sc_pitch] in the MoE
+  int64_t sc_pitch;           // FP4 x and h scales, block-major (rows of P, rounded up to 4)
   const int32_t* a_gather;    // A row of permuted row r = a_gather[r] / a_div (NULL: r)
   int a_div;
   const uint8_t* Bp;          // packed weights, expert-major
@@ -53,7 +55,8 @@ struct GemmKArgs {
   int M;                      // dense rows
   int rows_total;             // rows of the (permuted) row space: P grouped, M dense
   int F;                      // gate_up: up rows start at F
-  void* out;                  // gate_up with FP4 activations: packed codes of h [rows][F/2]
+  void* out;                  // gate_up with FP4 activations: packed codes of h, tiled in pair
+                              // order [rows/16][F/32][16][16]
   uint8_t* out_scales;        //   and their scale bytes, block-major [F/32][sc_pitch]
   int out_bf16;
   // expert activation of the gate_up epilogue (act_custom = 0: h = silu(g) * u) with its bias
@@ -302,6 +305,13 @@ struct GemmLds {
   // token) per block the SW aligned dwords that cover the tile's BM bytes of that block's row of
   // the block-major array
   static constexpr bool SBM = AFP4 && MODE != MODE_LINEAR;
+  // FP4 activation codes of the prefill-shaped MoE products (tiles of 64 rows or more) in the
+  // tiled layout, in pair order: [P/16][K/32][16 rows][16 bytes] (block b of rows 16q..16q+15
+  // as one 256-byte run; the x pair copy and the gate_up epilogue write them so), so a stage's A
+  // loads are whole 256-byte runs. Decode-shaped tiles (16 rows, weight streaming) keep
+  // row-major codes: x in token order, gathered, and h in pair order (the tiled form measured
+  // 6 % slower there).
+  static constexpr bool ATW = AFP4 && MODE != MODE_LINEAR && BM >= 64;
   static constexpr int SW = BM / 4 + 1;
   static constexpr int SA_DW = ((SBM ? KT * SW : BM * SD) + 63) / 64 * 64;  // activation scale dwords
   // resident scales: region 1 (up rows of gate_up) starts at dword R1; whole instructions
@@ -394,7 +404,7 @@ __device__ __forceinline__ void gemm_tile(
   const i32x4 rB = make_res(p.Bp + (int64_t)e * rpe * (K >> 1), rpe * (K >> 1));
   const i32x4 rS = make_res(p.Bs, (int64_t)(e + 1) * rpe * nb);  // absolute, 4-aligned offsets
   const int n_valid = min(BM, row_end - r0);                      // tile rows of this expert
-  const i32x4 rA = make_res(p.A, p.a_rows * (AFP4 ? (K >> 1) : K * 2));
+  const i32x4 rA = make_res(p.A, (LD::ATW ? (p.a_rows + 15) / 16 * 16 : p.a_rows) * (AFP4 ? (K >> 1) : K * 2));
   // activation scales live in the library's workspace, padded past a whole dword
   const i32x4 rSA = make_res(p.Asc, !AFP4 ? 0 : LD::SBM ? (int64_t)nb * p.sc_pitch : (p.a_rows * nb + 3) / 4 * 4);
   uint32_t voffB[IB];
@@ -550,7 +560,12 @@ __device__ __forceinline__ void gemm_tile(
     if constexpr (AFP4) {
       const int chunk = ((off % A_ROW) >> 4) ^ swz_rows<ACH>(lrow);
       ablk[q] = chunk;
-      voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K >> 1) + chunk * 16;
+      if constexpr (LD::ATW) {  // row r0 + lrow of the pair-ordered tiled codes
+        const uint32_t pr = (uint32_t)(r0 + lrow);
+        voffA[q] = ((pr >> 4) * (uint32_t)nb + (uint32_t)chunk) * 256u + (pr & 15u) * 16u;
+      } else {
+        voffA[q] = (uint32_t)sArow[lrow] * (uint32_t)(K >> 1) + chunk * 16;
+      }
     } else {
       const int chunk = ((off % A_ROW) >> 4) ^ swz_rows<ACH>(lrow);
       ablk[q] = chunk >> 2;
@@ -584,7 +599,7 @@ __device__ __forceinline__ void gemm_tile(
     for (int q = 0; q < ISA; ++q)
       dma_b32(rSA, off_add(voffSA[q], LD::SBM ? (uint32_t)kb * (uint32_t)p.sc_pitch : (uint32_t)kb), 0,
               &sg.Sa[PSA::instr(wave, q) * 64]);
-    constexpr int A_KB = AFP4 ? 16 : 64;  // bytes of A per 32-element block
+    constexpr int A_KB = LD::ATW ? 256 : AFP4 ? 16 : 64;  // bytes between a row's 32-element blocks
     auto load_a = [&](uint32_t voff, const void* lds) {
       if constexpr (COH && MODE == MODE_DOWN) dma_b128_coherent(rA, voff, 0, lds);
       else dma_b128(rA, voff, 0, lds);
@@ -804,10 +819,14 @@ __device__ __forceinline__ void gemm_tile(
       // FP4 activations: the down product takes h as MXFP4, so each 32-column block of the bf16
       // tile is quantized here (the codec's bf16 quantizer, the same function) and only its 16
       // code bytes and scale byte leave the chip
+      // (prefill tiles: codes in the tiled layout, [P/16][F/32][16 rows][16 bytes], consecutive
+      // threads on consecutive rows of one block, so 16 of them store one 256-byte run; decode
+      // tiles: row-major [P][F/2])
       constexpr int BPR = BNH / 32;  // 32-element blocks per tile row
       uint8_t* hq = reinterpret_cast<uint8_t*>(p.out);
+      const int nbf = p.F >> 5;
       for (int c = tid; c < BM * BPR; c += NT) {
-        const int lr = c / BPR, cb = c % BPR;
+        const int lr = LD::ATW ? c % BM : c / BPR, cb = LD::ATW ? c / BM : c % BPR;
         const int r = r0 + lr, col = nt * BNH + cb * 32;
         if (r >= row_end || col >= p.F) continue;
         const uint4* src = reinterpret_cast<const uint4*>(sh + lr * LDH + cb * 32);
@@ -819,7 +838,9 @@ __device__ __forceinline__ void gemm_tile(
         }
         uint32_t q[4];
         const uint32_t sb = quantize_block32_bf16(w, q);
-        *reinterpret_cast<uint4*>(hq + (int64_t)r * (p.F >> 1) + (col >> 1)) = make_uint4(q[0], q[1], q[2], q[3]);
+        const int64_t at = LD::ATW ? ((int64_t)(r >> 4) * nbf + (col >> 5)) * 256 + (r & 15) * 16
+                                   : (int64_t)r * (p.F >> 1) + (col >> 1);
+        *reinterpret_cast<uint4*>(hq + at) = make_uint4(q[0], q[1], q[2], q[3]);
         p.out_scales[(int64_t)(col >> 5) * p.sc_pitch + r] = (uint8_t)sb;  // block-major
       }
     } else {

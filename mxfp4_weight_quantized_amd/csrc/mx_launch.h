@@ -10,12 +10,19 @@ namespace mx {
 // codec.hip
 hipError_t launch_quantize(const void* src, bool bf16_in, int64_t nblocks, uint8_t* packed,
                            uint8_t* scales, hipStream_t stream);
-// x [T][H] bf16 quantized along H for the MoE MLP's activation variant: codes [T][H/2] in token
-// order, scale bytes block-major in pair order ([H/32][pitch], pitch >= T * k): the scale of
-// (token t, block b) at b * pitch + inv[t * k + j] for every slot j whose inv is in [0, T * k).
-hipError_t launch_quantize_x_pairs(const uint16_t* x, int T, int H, const int32_t* inv, int k,
-                                   int64_t pitch, uint8_t* packed, uint8_t* scales_bm,
-                                   hipStream_t stream);
+// The MoE MLP's activation variant. Decode-shaped calls: x [T][H] bf16 quantized along H, codes
+// [T][H/2] in token order, scale bytes block-major in pair order ([H/32][pitch], pitch >= T * k):
+// the scale of (token t, block b) at b * pitch + inv[t * k + j] for every slot j whose inv is in
+// [0, T * k).
+hipError_t launch_quantize_x_scatter(const uint16_t* x, int T, int H, const int32_t* inv, int k,
+                                     int64_t pitch, uint8_t* packed, uint8_t* scales_bm,
+                                     hipStream_t stream);
+// Prefill-shaped calls: x's codes [T][H/2] and scales [T][H/32] (token order, launch_quantize)
+// copied into pair order (row p is token perm[p] / k, p < P): codes tiled [P/16][H/32][16][16
+// bytes] (P rounded up to 16 rows), scales block-major [H/32][pitch].
+hipError_t launch_x_pair_copy(const uint8_t* codes, const uint8_t* scales, int H,
+                              const int32_t* perm, int k, int P, int64_t pitch, uint8_t* packed,
+                              uint8_t* scales_bm, hipStream_t stream);
 hipError_t launch_dequantize(const uint8_t* packed, const uint8_t* scales, int64_t nblocks,
                              void* dst, bool bf16_out, hipStream_t stream);
 // G matrices [R][K] (R % 16 == 0, K % 32 == 0) into the tiled layout of the grouped GEMMs;
