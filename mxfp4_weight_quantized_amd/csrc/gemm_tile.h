@@ -1032,11 +1032,13 @@ struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4
 // tiles of four waves of 64 x 128, 3 stages, two workgroups per CU (the eight waves a CU holds
 // as two independent workgroups, whose barriers no longer stall each other: against one
 // workgroup of eight waves on 128 x 512, 20B-shaped prefill gate_up 581 -> 482 us, 120B-shaped
-// T = 4096 449 -> 391 us), down with row tiles grouped by 2 (311 -> 293 us). Also measured: 64 x
+// T = 4096 449 -> 391 us), down with row tiles grouped by 2 (311 -> 293 us); with the pair-ordered
+// tiled activations, gate_up row tiles grouped by 8 (455 -> 451 us; down by 4: 266 -> 275 us,
+// by 1: 310 us; 2 stages: 478 us). Also measured: 64 x
 // 256 (about 15% slower), 128 x 384 with 2 or 4 stages, 8-block stages (spills), three
 // workgroups per CU with 2 stages (spills: 5x slower), groups of 8 row tiles, and 128 x 256 as
 // one wave row of four.
-struct CfgPreGU4 { static constexpr int BM = 128, BN = 256, WM = 2, WN = 2, KT = 4, ST = 3, GM = 4, OCC = 2, SCM = SCM_STAGE, MF = 16; };
+struct CfgPreGU4 { static constexpr int BM = 128, BN = 256, WM = 2, WN = 2, KT = 4, ST = 3, GM = 8, OCC = 2, SCM = SCM_STAGE, MF = 16; };
 struct CfgPreDn4 { static constexpr int BM = 128, BN = 256, WM = 2, WN = 2, KT = 4, ST = 3, GM = 2, OCC = 2, SCM = SCM_STAGE, MF = 16; };
 // Few pairs (a handful of experts touched): with fewer tiles than CUs each workgroup's own weight
 // stream is the bound, so these tiles keep more stages in flight. The down GEMM (2880 columns: 23
