@@ -511,8 +511,10 @@ def summarize_counters(fetch_dir, write_dir, copy_bytes=1 << 30):
     kinds = {"moe_gate_up_swiglu": ["moe_gate_up_swiglu_kernel"],
              "moe_down_weighted": ["moe_down_weighted_kernel"], "moe_combine": ["combine_token_kernel"],
              "route_topk": router + ["route_select_kernel"],
-             "permute": ["permute_kernel"], "linear": ["linear_kernel"],
-             "quantize": ["quantize_kernel"], "moe_single_launch": ["moe_single_launch_kernel"]}
+             "permute": ["permute_kernel", "slice_hist_kernel", "slice_scatter_kernel"],
+             "linear": ["linear_kernel"],
+             "quantize": ["quantize_kernel<true>", "x_pair_copy_kernel", "quantize_x_scatter_kernel"],
+             "moe_single_launch": ["moe_single_launch_kernel"]}
     out = {}
     for kind, syms in kinds.items():
         fk = wk = 0.0
@@ -603,6 +605,47 @@ def summarize_mfma(pmc_dir, command, title):
     return "\n".join(out) + "\n"
 
 
+def summarize_vmem(command, title, dirs):
+    """Markdown table of the vector memory pipeline per dispatch of the MoE kernels from rocprofv3
+    --pmc runs (one directory per workload, named pmc_ta_<workload>) of GRBM_GUI_ACTIVE, the TA and
+    TD busy and L1-stall counters, the L1's pending and tag-conflict stalls and its L2 read
+    requests with their summed latency. GRBM_GUI_ACTIVE is summed over the 8 XCDs, the TA, TD and
+    TCP counters over the 256 CUs: each of those is shown as a share of 256 x the dispatch's
+    cycles per XCD."""
+    out = ["# %s" % title, "", "Command per workload (run from /tmp with TMPDIR=/tmp, output under "
+           "the -d directory; REPO is the repository root; WL = %s):" % ", then ".join(
+               os.path.basename(d.rstrip("/")).replace("pmc_ta_", "") for d in dirs), "", "```",
+           command, "```", "",
+           "Per-dispatch averages. L2 latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ (cycles "
+           "per L1 -> L2 read request). Library sources: `%s` (hash of csrc/)." % source_sha(), "",
+           "| workload | kernel | dispatches | avg us | TA busy | TA stalled by L1 | TD busy | "
+           "TD stalled by L1 | L1 pending stall | L1 tag conflict | L2 latency (cycles) | "
+           "L1->L2 requests |",
+           "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for d in dirs:
+        wl = os.path.basename(d.rstrip("/")).replace("pmc_ta_", "")
+        disp = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                e = disp.setdefault((f, r["Dispatch_Id"]), {
+                    "name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for sym in ("moe_gate_up_swiglu_kernel", "moe_down_weighted_kernel", "combine_token_kernel"):
+            ds = [e for e in disp.values() if sym in e["name"] and "GRBM_GUI_ACTIVE" in e]
+            if not ds:
+                continue
+            avg = lambda c: sum(e.get(c, 0.0) for e in ds) / len(ds)
+            cu = 256.0 * avg("GRBM_GUI_ACTIVE") / 8.0
+            pct = lambda c: "%.1f %%" % (100.0 * avg(c) / cu)
+            req = avg("TCP_TCC_READ_REQ")
+            out.append("| %s | `%s` | %d | %.1f | %s | %s | %s | %s | %s | %s | %.0f | %.1fM |" % (
+                wl, sym, len(ds), avg("ns") / 1e3, pct("TA_TA_BUSY"),
+                pct("TA_ADDR_STALLED_BY_TC_CYCLES"), pct("TD_TD_BUSY"), pct("TD_TC_STALL"),
+                pct("TCP_PENDING_STALL_CYCLES"), pct("TCP_READ_TAGCONFLICT_STALL_CYCLES"),
+                avg("TCP_TCC_READ_REQ_LATENCY") / req if req else float("nan"), req / 1e6))
+    return "\n".join(out) + "\n"
+
+
 def summarize_trace(trace_dir, command, title, bench_json=None):
     """Markdown table of a rocprofv3 --kernel-trace --stats run (its *kernel_stats.csv): calls,
     average / min / max duration and share of GPU time per kernel; with bench_json (the traced
@@ -669,6 +712,8 @@ def main():
     ap.add_argument("--summarize-traffic", nargs="+",
                     metavar="WORKLOAD BENCH_JSON [COMMAND ...]",
                     help="print a markdown table of the committed counter traffic of a workload")
+    ap.add_argument("--summarize-vmem", nargs="+", metavar="ARG",
+                    help="COMMAND TITLE DIR [DIR ...]: markdown summary of vector memory counters")
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_DIR", "COMMAND", "TITLE"),
                     help="print a markdown summary of the MFMA counters of a rocprofv3 --pmc run")
     args = ap.parse_args()
@@ -680,6 +725,11 @@ def main():
     if args.summarize_traffic:
         wl_, bj = args.summarize_traffic[:2]
         sys.stdout.write(summarize_traffic(wl_, bj, args.summarize_traffic[2:]))
+        return 0
+
+    if args.summarize_vmem:
+        sys.stdout.write(summarize_vmem(args.summarize_vmem[0], args.summarize_vmem[1],
+                                        args.summarize_vmem[2:]))
         return 0
 
     if args.summarize_mfma:
