@@ -134,7 +134,7 @@ MoeLayout moe_layout(const mx_moe_desc& d) {
   const bool single = (d.flags & MX_SINGLE_LAUNCH) != 0;
   L.tile_rows = single ? 16 : mx::moe_tile_rows(d.T, d.k, d.E, (d.flags & MX_ACT_MXFP4) != 0);
   L.max_tiles = mx::moe_max_tiles(d.T, d.k, d.E, L.tile_rows);
-  L.status = take(256);  // int32 status, int32 tile count
+  L.status = take(256);  // int32 status, int32 tile count, int32 counter of the routing launch
   L.logits = take(T * E * 4);
   L.idx = take(P * 4);
   L.w = take(P * 4);
@@ -478,6 +478,9 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   // small batches: the router launch computes the logits (or their partial sums over H) only and
   // the permutation launch makes the top-k selection first (one launch fewer)
   bool select_in_permute = false;
+  // decode-sized batches on the spread router: selection and permutation as one launch, which
+  // counts its workgroups in on status[2] (set to zero by the router launch)
+  bool select_permute = false;
   float* sel_logits = nullptr;
   float* rpart = nullptr;
   int n_part = 0;
@@ -486,13 +489,15 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
     int32_t* oi = d.topk_idx_out ? d.topk_idx_out : reinterpret_cast<int32_t*>(w + L.idx);
     float* ow = d.topk_w_out ? d.topk_w_out : reinterpret_cast<float*>(w + L.w);
     select_in_permute = mx::route_logits_defers_select(d.T, d.E, d.k);
+    select_permute = L.pcounts_bytes == 0 && mx::route_select_permute_fits(d.T, d.H, d.E, d.k);
     // the router's partial sums borrow the down projection's output rows (written later)
     const size_t part_bytes = (size_t)mx::route_partial_splits(d.T, d.H, d.E) * d.T * d.E * 4;
     rpart = part_bytes <= (size_t)d.T * d.k * d.H * 4 ? reinterpret_cast<float*>(w + L.y) : nullptr;
     {
       ProfScope ps(PK_ROUTE, s);
-      e = select_in_permute
-              ? mx::launch_route_logits(d.x, d.wr, d.br, d.T, d.H, d.E, logits, rpart, &n_part, s)
+      e = (select_in_permute || select_permute)
+              ? mx::launch_route_logits(d.x, d.wr, d.br, d.T, d.H, d.E, logits, rpart, &n_part, s,
+                                        select_permute ? status + 2 : nullptr)
               : mx::launch_route_topk(d.x, d.wr, d.br, d.T, d.H, d.E, d.k, logits, oi, ow, rpart, s);
     }
     if (e != hipSuccess) return hip_fail(e, "route launch");
@@ -509,7 +514,12 @@ mx_status moe_mlp_run(const mx_moe_desc& d, const MoeLayout& L, char* w, hipStre
   int2* tiles = reinterpret_cast<int2*>(w + L.tiles);
   {
     ProfScope ps(PK_PERMUTE, s);
-    e = select_in_permute
+    e = select_permute
+            ? mx::launch_route_select_permute(sel_logits, rpart, n_part, d.br, d.T, d.E, d.k,
+                                              const_cast<int32_t*>(idx), const_cast<float*>(tw),
+                                              status + 2, offsets, perm, inv, status, L.tile_rows,
+                                              tiles, status + 1, s)
+        : select_in_permute
             ? mx::launch_select_permute(sel_logits, rpart, n_part, d.br, d.T, d.k, d.E,
                                         const_cast<int32_t*>(idx), const_cast<float*>(tw), offsets,
                                         perm, inv, status, L.tile_rows, tiles, status + 1, s)

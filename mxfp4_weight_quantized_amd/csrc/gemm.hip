@@ -200,12 +200,12 @@ hipError_t launch_linear_tiles(const GemmKArgs& g, int M, int N, hipStream_t str
       return dw ? launch_gemm<C, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
                 : launch_gemm<C, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
   }
-  const int mt = (M + CfgDecDn::BM - 1) / CfgDecDn::BM;
+  const int mt = (M + CfgDecDn128::BM - 1) / CfgDecDn128::BM;
   // (split K: each split needs only its stages' scales)
   if (dw && nb <= kResidentNb && g.k_splits <= 1)
-    return launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_RESIDENT>(g, mt, N, stream);
-  return dw ? launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
-            : launch_gemm<CfgDecDn, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
+    return launch_gemm<CfgDecDn128, MODE_LINEAR, AFP4, SCM_RESIDENT>(g, mt, N, stream);
+  return dw ? launch_gemm<CfgDecDn128, MODE_LINEAR, AFP4, SCM_STAGE>(g, mt, N, stream)
+            : launch_gemm<CfgDecDn128, MODE_LINEAR, AFP4, SCM_BYTE>(g, mt, N, stream);
 }
 
 bool use_prefill_tiles(int T, int k, int E) { return (int64_t)T * k >= 64LL * E; }

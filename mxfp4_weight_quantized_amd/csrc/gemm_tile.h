@@ -1026,7 +1026,12 @@ GemmKArgs down_args(const MoeGemmArgs& m) {
 struct CfgPreGU { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 2, ST = 2, GM = 4, OCC = 4, SCM = SCM_STAGE, MF = 32; };
 struct CfgPreDn { static constexpr int BM = 64, BN = 256, WM = 1, WN = 4, KT = 2, ST = 2, GM = 4, OCC = 4, SCM = SCM_STAGE, MF = 32; };
 struct CfgDecGU { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT, MF = 16; };
-struct CfgDecDn { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT, MF = 16; };
+struct CfgDecDn { static constexpr int BM = 16, BN = 192, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 2, SCM = SCM_RESIDENT, MF = 16; };
+// The single launch's down tiles and the dense linear at decode sizes (its K splits are sized
+// for 128-column tiles) keep the 128-column form; the per-step MoE down GEMM takes 192 columns (2880 = 15 x 192: 600 tiles of the
+// 20B-shaped T = 64 layer in one round of two workgroups per CU, against 920 128-column tiles in
+// 1.2 rounds of three per CU: 27.9 -> 27.0 us; with two stages at three per CU 33.1 us).
+struct CfgDecDn128 { static constexpr int BM = 16, BN = 128, WM = 1, WN = 4, KT = 4, ST = 3, GM = 1, OCC = 3, SCM = SCM_RESIDENT, MF = 16; };
 // Activation variant, prefill-shaped: FP4 activations take a quarter of the LDS and need no
 // decode instructions, so wide wave tiles with fewer bytes per MFMA pay: 128 x 256 workgroup
 // tiles of four waves of 64 x 128, 3 stages, two workgroups per CU (the eight waves a CU holds

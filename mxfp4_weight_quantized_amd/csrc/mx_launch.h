@@ -47,9 +47,24 @@ int route_partial_splits(int T, int H, int E);
 // *n_part workgroups are stored there without the bias (else *n_part = 0 and the logits with the
 // bias go to logits).
 bool route_logits_defers_select(int T, int E, int k);
+// zero_word (may be null): an int the launch sets to 0 (the counter of the next launch).
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
                                int H, int E, float* logits, float* partials, int* n_part,
-                               hipStream_t stream);
+                               hipStream_t stream, int32_t* zero_word = nullptr);
+// Decode-sized batches inside the MoE call whose router is the spread launch (more than one
+// expert group, selection not deferred to the permutation, T * k <= kSelectPermuteMaxPairs):
+// launch_route_logits (with zero_word = counter) then this one launch, which makes the top-k
+// selection of every token (as the selection kernel) and the permutation (as launch_permute).
+// (up to 512 pairs: the 20B-shaped T = 64 layer, 8.8 + 4.9 -> 4.7 + 7.3 us; with 1024 pairs, the
+// 120B-shaped T = 256 layer, the one workgroup's sort on four waves costs what the launch saves:
+// 13.0 + 5.1 -> 6.9 + 11.8 us)
+constexpr int kSelectPermuteMaxPairs = 512;
+bool route_select_permute_fits(int T, int H, int E, int k);
+hipError_t launch_route_select_permute(float* logits, const float* partials, int n_part,
+                                       const float* br, int T, int E, int k, int32_t* idx,
+                                       float* w, int32_t* counter, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
+                                       int32_t* num_tiles, hipStream_t stream);
 
 // Device error word, one per device, owned by the library: kernels OR error codes into it, and
 // mx_get_device_error reads and clears it. device_error_word() is its device address on the

@@ -47,7 +47,8 @@ template <bool SELECT, int BATCH>
 __global__ __launch_bounds__(1024) void route_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ br,
     int T, int H, int E, int n_groups, int n_splits, float* __restrict__ logits, int k,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out, float* __restrict__ partials) {
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, float* __restrict__ partials,
+    int32_t* __restrict__ zero_word) {
   __shared__ float part[16][kTokPerWG][16];  // per wave: its partial 16 x 16 tile
   __shared__ float tile[SELECT ? kTokPerWG : 1][SELECT ? 257 : 1];  // the workgroup's logits
   const int lane = threadIdx.x & 63;
@@ -56,6 +57,8 @@ __global__ __launch_bounds__(1024) void route_logits_kernel(
   const int m = lane & 15, g = lane >> 4;
   const int gl = wave % n_groups, split = wave / n_groups;
   const int grp = blockIdx.y * n_groups + gl;
+  // (a counter of the next launch, which starts from zero)
+  if (zero_word != nullptr && blockIdx.x + blockIdx.y + blockIdx.z == 0 && threadIdx.x == 0) *zero_word = 0;
 
   // ---- partial logits: experts [16*grp, 16*grp + 16), 32-element steps [s0, s1) of H ----
   const int nsteps = H >> 5;
@@ -105,17 +108,11 @@ __global__ __launch_bounds__(1024) void route_logits_kernel(
 // One 16-lane row per token (16 tokens per workgroup), logits read back from memory; with
 // NP > 0 partial tiles, the row first sums partials[0..NP)[t][e] in that order, adds the bias and
 // writes the logits (a compile-time NP lets all of a lane's loads go out together). NQ: experts
-// per lane (E <= 16 NQ).
+// per lane (E <= 16 NQ). Returns the row's logits (-inf past E).
 template <int NQ, int NP>
-__global__ __launch_bounds__(256) void route_select_kernel(float* __restrict__ logits, int T, int E,
-                                                           int k, int32_t* __restrict__ idx_out,
-                                                           float* __restrict__ w_out,
-                                                           const float* __restrict__ partials,
-                                                           const float* __restrict__ br) {
-  const int j16 = threadIdx.x & 15;
-  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
-  if (t >= T) return;
-  float cv[NQ];
+__device__ __forceinline__ void select_row_logits(float* __restrict__ logits, int T, int E, int t,
+                                                  int j16, const float* __restrict__ partials,
+                                                  const float* __restrict__ br, float (&cv)[NQ]) {
   if constexpr (NP == 0) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -142,7 +139,56 @@ __global__ __launch_bounds__(256) void route_select_kernel(float* __restrict__ l
       cv[q] = (e < E) ? s : -INFINITY;
     }
   }
+}
+
+template <int NQ, int NP>
+__global__ __launch_bounds__(256) void route_select_kernel(float* __restrict__ logits, int T, int E,
+                                                           int k, int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ w_out,
+                                                           const float* __restrict__ partials,
+                                                           const float* __restrict__ br) {
+  const int j16 = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (t >= T) return;
+  float cv[NQ];
+  select_row_logits<NQ, NP>(logits, T, E, t, j16, partials, br, cv);
   select_topk_row16<NQ>(cv, j16, t, E, k, idx_out, w_out);
+}
+
+// Decode-sized batches inside the MoE call: route_select_kernel's selection and then, by the
+// workgroup that finishes its tokens last, the permutation of all pairs (one launch instead of
+// two). Each workgroup stores its tokens' experts and weights device-coherent (written through
+// to the device's point of coherence), waits until those stores are done and counts itself in
+// on a counter the router launch set to zero; the one that counts last reads every pair's expert
+// device-coherent and runs the permutation kernel's counting sort with its four waves.
+template <int NQ, int NP>
+__global__ __launch_bounds__(256) void route_select_permute_kernel(
+    float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out, const float* __restrict__ partials, const float* __restrict__ br,
+    int32_t* __restrict__ counter, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv, int32_t* __restrict__ status, int32_t* __restrict__ dev_err,
+    int tile_rows, int2* __restrict__ tiles, int32_t* __restrict__ num_tiles) {
+  __shared__ int cnt[4][kPermuteMaxE];
+  __shared__ int tot[kPermuteMaxE + 1];
+  __shared__ int tbase[kPermuteMaxE + 1];
+  __shared__ int bad, last;
+  const int j16 = threadIdx.x & 15;
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 4);
+  if (t < T) {
+    float cv[NQ];
+    select_row_logits<NQ, NP>(logits, T, E, t, j16, partials, br, cv);
+    select_topk_row16<NQ, true>(cv, j16, t, E, k, idx_out, w_out);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are done
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  permute_pairs<4>([&](int p) { return __hip_atomic_load(idx_out + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
+                   T * k, E, offsets, perm, inv, status, dev_err, tile_rows, tiles, num_tiles,
+                   &cnt[0][0], tot, tbase, &bad);
 }
 
 template <int NP>
@@ -170,6 +216,25 @@ hipError_t launch_route_select(float* logits, int T, int E, int k, int32_t* idx,
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int NP>
+void launch_select_permute_np(int nq, dim3 grid, float* logits, int T, int E, int k, int32_t* idx,
+                              float* w, const float* partials, const float* br, int32_t* counter,
+                              int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* status,
+                              int32_t* dev_err, int tile_rows, int2* tiles, int32_t* num_tiles,
+                              hipStream_t stream) {
+  const dim3 block(256);
+#define MX_SP_LAUNCH(Q)                                                                           \
+  hipLaunchKernelGGL((route_select_permute_kernel<Q, NP>), grid, block, 0, stream, logits, T, E, k, \
+                     idx, w, partials, br, counter, offsets, perm, inv, status, dev_err,           \
+                     tile_rows, tiles, num_tiles)
+  if (nq <= 1) MX_SP_LAUNCH(1);
+  else if (nq <= 2) MX_SP_LAUNCH(2);
+  else if (nq <= 4) MX_SP_LAUNCH(4);
+  else if (nq <= 8) MX_SP_LAUNCH(8);
+  else MX_SP_LAUNCH(16);
+#undef MX_SP_LAUNCH
 }
 
 // ---- large batches: 64-token tiles over all experts, staged through LDS ----
@@ -335,7 +400,7 @@ int route_partial_splits(int T, int H, int E) {
 
 hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const float* br, int T,
                                int H, int E, float* logits, float* partials, int* n_part,
-                               hipStream_t stream) {
+                               hipStream_t stream, int32_t* zero_word) {
   *n_part = 0;
   if (T == 0) return hipSuccess;
   const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
@@ -345,7 +410,32 @@ hipError_t launch_route_logits(const uint16_t* x, const uint16_t* wr, const floa
   if (so > 1) *n_part = so;
   hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups, so), dim3(64 * (splits / so)), 0,
                      stream, x, wr, br, T, H, E, 1, splits / so, logits, 0, nullptr, nullptr,
-                     so > 1 ? partials : nullptr);
+                     so > 1 ? partials : nullptr, zero_word);
+  return hipGetLastError();
+}
+
+bool route_select_permute_fits(int T, int H, int E, int k) {
+  const int groups = (E + 15) / 16, tiles = (T + kTokPerWG - 1) / kTokPerWG;
+  return !route_logits_defers_select(T, E, k) && groups > 1 && tiles * groups <= kSpreadBelow &&
+         !route_tiled(T, H, E) && (int64_t)T * k <= kSelectPermuteMaxPairs && E <= kPermuteMaxE;
+}
+
+hipError_t launch_route_select_permute(float* logits, const float* partials, int n_part,
+                                       const float* br, int T, int E, int k, int32_t* idx,
+                                       float* w, int32_t* counter, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv, int32_t* status, int tile_rows, int2* tiles,
+                                       int32_t* num_tiles, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((T + 15) / 16);
+  const int nq = (E + 15) / 16;
+  int32_t* dev_err = device_error_word();
+  switch (n_part) {
+    case 0: launch_select_permute_np<0>(nq, grid, logits, T, E, k, idx, w, partials, br, counter, offsets, perm, inv, status, dev_err, tile_rows, tiles, num_tiles, stream); break;
+    case 2: launch_select_permute_np<2>(nq, grid, logits, T, E, k, idx, w, partials, br, counter, offsets, perm, inv, status, dev_err, tile_rows, tiles, num_tiles, stream); break;
+    case 4: launch_select_permute_np<4>(nq, grid, logits, T, E, k, idx, w, partials, br, counter, offsets, perm, inv, status, dev_err, tile_rows, tiles, num_tiles, stream); break;
+    case 8: launch_select_permute_np<8>(nq, grid, logits, T, E, k, idx, w, partials, br, counter, offsets, perm, inv, status, dev_err, tile_rows, tiles, num_tiles, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -369,16 +459,16 @@ hipError_t launch_route_topk(const uint16_t* x, const uint16_t* wr, const float*
   if (G == groups) {  // one workgroup covers all experts of its tokens: select in the same kernel
     if (splits >= 16)
       hipLaunchKernelGGL((route_logits_kernel<true, 8>), dim3(tiles, 1), dim3(64 * G * splits), 0, stream,
-                         x, wr, br, T, H, E, G, splits, logits, k, idx, w, nullptr);
+                         x, wr, br, T, H, E, G, splits, logits, k, idx, w, nullptr, nullptr);
     else
       hipLaunchKernelGGL((route_logits_kernel<true, 12>), dim3(tiles, 1), dim3(64 * G * splits), 0, stream,
-                         x, wr, br, T, H, E, G, splits, logits, k, idx, w, nullptr);
+                         x, wr, br, T, H, E, G, splits, logits, k, idx, w, nullptr, nullptr);
     return hipGetLastError();
   }
   // (G is 1 here: one expert group per workgroup; splits is 16 wherever so > 1)
   const int so = partials != nullptr ? route_spread_splits(T, H, E) : 1;
   hipLaunchKernelGGL((route_logits_kernel<false, 8>), dim3(tiles, groups, so), dim3(64 * (splits / so)), 0,
-                     stream, x, wr, br, T, H, E, 1, splits / so, logits, k, idx, w, partials);
+                     stream, x, wr, br, T, H, E, 1, splits / so, logits, k, idx, w, partials, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_route_select(logits, T, E, k, idx, w, partials, so > 1 ? so : 0, br, stream);

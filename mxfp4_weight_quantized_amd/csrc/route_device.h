@@ -143,9 +143,10 @@ __device__ __forceinline__ int select_topk_wave(LogitOf logit_of, int lane, int 
 // The same selection on one 16-lane row of a wave per token: lane j of the row holds the logits
 // of experts j, j + 16, ..., j + 16 (NQ - 1) in cv (entries past E are ignored). The four DPP
 // exchanges inside the row leave the row's best in every lane of it, so no step crosses rows.
-// Every lane of the row calls it; row lane j < k writes entry j. The softmax is the same
-// arithmetic as select_topk_wave's.
-template <int NQ>
+// Every lane of the row calls it; row lane j < k writes entry j (COH: device-coherent, for a
+// reader in another workgroup of the same launch). The softmax is the same arithmetic as
+// select_topk_wave's.
+template <int NQ, bool COH = false>
 __device__ __forceinline__ void select_topk_row16(const float (&cv)[NQ], int j16, int t, int E,
                                                   int k, int32_t* __restrict__ idx_out,
                                                   float* __restrict__ w_out) {
@@ -195,8 +196,8 @@ __device__ __forceinline__ void select_topk_row16(const float (&cv)[NQ], int j16
     }
   }
   if (j16 < k) {
-    idx_out[(int64_t)t * k + j16] = mine_i;
-    w_out[(int64_t)t * k + j16] = mine / sum;
+    st_out<COH>(idx_out + (int64_t)t * k + j16, mine_i);
+    st_out<COH>(w_out + (int64_t)t * k + j16, mine / sum);
   }
 }
 

@@ -419,7 +419,7 @@ hipError_t launch_moe_single(const MoeGemmArgs& m, const SingleRouting& r, hipSt
     a.bn_dn = CfgTinyDn::BN;
   } else {
     a.nt_gu = (m.F + CfgDecGU::BN / 2 - 1) / (CfgDecGU::BN / 2);
-    a.bn_dn = CfgDecDn::BN;
+    a.bn_dn = CfgDecDn128::BN;
   }
   a.nt_dn = (m.H + a.bn_dn - 1) / a.bn_dn;
   a.gu.n_tiles = a.nt_gu;
@@ -427,8 +427,8 @@ hipError_t launch_moe_single(const MoeGemmArgs& m, const SingleRouting& r, hipSt
   if (tiny)
     return m.tiled ? launch_single<CfgTinyGU, CfgTinyDn, true>(a, m.out_bf16, stream)
                    : launch_single<CfgTinyGU, CfgTinyDn, false>(a, m.out_bf16, stream);
-  return m.tiled ? launch_single<CfgDecGU, CfgDecDn, true>(a, m.out_bf16, stream)
-                 : launch_single<CfgDecGU, CfgDecDn, false>(a, m.out_bf16, stream);
+  return m.tiled ? launch_single<CfgDecGU, CfgDecDn128, true>(a, m.out_bf16, stream)
+                 : launch_single<CfgDecGU, CfgDecDn128, false>(a, m.out_bf16, stream);
 }
 
 }  // namespace mx

@@ -89,6 +89,28 @@ def test_moe_mxact_small_pinned_routing(T, H, F, E, k):
     check_tolerance(to_f64(out), ref, "moe mx-act T=%d" % T, slack=slack)
 
 
+# Routing indices outside [0, E) leave their pairs out (their inv is -1) and set the device error
+# word. Decode-shaped (16-row tiles: x's codes in token order, gathered) and prefill-shaped
+# (128-row tiles: x's and h's codes copied into pair order, tiled by 16 rows; P = 1026 leaves a
+# partial last group of 16): the reference is the oracle with those pairs' weights at zero.
+@pytest.mark.parametrize("T,H,F,E,k", [(40, 128, 96, 8, 2), (513, 64, 128, 4, 2)])
+def test_moe_mxact_skips_out_of_range_indices(T, H, F, E, k):
+    seed = 180 + T
+    x = inputs.activations(seed, T, H)
+    wts = moe_weights(seed, E, H, F)
+    idx, w = _routing(T, E, k, seed)
+    idx[3, 1], idx[7, 0], idx[T - 1, 1] = -1, E, E + 5
+    ref_idx, ref_w = idx.copy(), w.copy()
+    bad = (idx < 0) | (idx >= E)
+    ref_idx[bad], ref_w[bad] = 0, 0.0
+    mx.get_device_error()  # clear
+    note("moe mx-act out-of-range indices T=%d E=%d" % (T, E))
+    out, _ = _run(x, moe_weights_dev(seed, E, H, F), k, torch.float32, idx=idx, w=w)
+    assert mx.get_device_error() == mx.MX_DEVERR_ROUTING
+    ref, _, slack = oracle.moe_mlp(x, ref_idx, ref_w, *wts, E=E, mx_act=True, fragile_c=FRAGILE_C)
+    check_tolerance(to_f64(out), ref, "moe mx-act skipped pairs T=%d" % T, slack=slack)
+
+
 def test_moe_mxact_is_deterministic():
     T, H, F, E, k, seed = 300, 128, 128, 8, 4, 171
     x = inputs.activations(seed, T, H)
