@@ -238,8 +238,8 @@ mx_status mxfp4_moe_mlp(const mx_moe_desc* desc, void* ws, size_t ws_bytes, void
  * (MX_NOALLOC_SCRATCH_BYTES per device, kept until the process ends). The call allocates
  * nothing; the caller still owns desc's inputs and outputs.
  *   Problems whose workspace (mxfp4_moe_mlp_workspace(desc)) exceeds MX_NOALLOC_SCRATCH_BYTES
- *   return MX_ERR_WORKSPACE before anything is launched (32 MiB covers decode batches of up to
- *   about 1300 token-expert pairs at H = F = 2880).
+ *   return MX_ERR_WORKSPACE before anything is launched (32 MiB covers batches of up to about
+ *   1900 token-expert pairs at H = F = 2880 with bf16 activations: 484 tokens at top-4).
  *   Every call on a device shares that device's array, which keeps the last call's contents
  *   (no call needs it cleared): calls that overlap on one device -- on different streams, or from
  *   different threads -- race and must be serialized by the caller. Other errors as for
